@@ -1,0 +1,283 @@
+"""Benchmark of the gated delta-rule core on one MI355X.
+
+Headline (`value`): chunked-prefill throughput in tokens/s on the GDN prefill workload —
+one sequence, T=8192, H=16, d_k=d_v=128, chunk 64, bf16 q/k/v, fp32 gates and state. One
+step = one gdn_prefill_chunked call over that batch (chunk table + prep + sequential scan).
+Inputs are resident in HBM before timing; three input sets rotate so the 256 MB MALL does
+not serve them from one step to the next.
+
+Also reported on the same JSON line (secondary workloads of the same metric):
+  decode:   dense decode step, B=128, H=32, d=128, 256-slot fp32 pool, random slot map;
+            four layer pools rotate per step so the state stream comes from HBM
+  deltalog: DeltaLog vs dense decode, B=512, H=32, d=128 (1 GiB fp32 state), M=8, cycle
+            average over whole merge cycles
+  kda:      KDA-style varlen prefill, 8 sequences of 1k-8k tokens, H=32, d=128, conv1d+SiLU
+            pre-pass, in-kernel L2 norm, per-key gates
+  roofline: the prefill pass against HBM bandwidth (algorithmic bytes / event-timed
+            duration of the call); counters-based traffic when a matching profile exists
+  cpu_baseline: the fp64 oracle on the host cores over the same prefill workload
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-extras] [--no-cpu]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+from gated_delta_rule_prefill_amd import gdn, inputs, traffic  # noqa: E402
+
+METRIC = "decode state-update GB/s + tokens/s (B=128/512); prefill tokens/s, %roofline"
+DEV = "cuda:0"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def ev_time(fn, steps, warmup):
+    """Run fn() warmup times, then time `steps` calls with HIP events on the current stream
+    (bracketed by device synchronisation). Returns (ms per call, wall seconds)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_prefill_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(name, digest):
+    """HBM bytes per call from committed rocprofv3 counter runs, if they were taken on the
+    current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", f"{name}_counters.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("source_digest") != digest:
+        return None
+    return d.get("hbm_bytes_per_call")
+
+
+# ------------------------------------------------------------------------------ prefill
+def bench_prefill(steps, warmup):
+    sets = []
+    for seed in range(3):
+        x = inputs.prefill_config(seed)
+        sets.append([t.to(DEV) for t in (x.q, x.k, x.v, x.g, x.beta)])
+    cu = x.cu_seqlens.to(DEV)
+    T, H, d = x.q.shape
+    pool = torch.zeros((1, H, d, d), device=DEV)
+    slots = torch.zeros(1, dtype=torch.int32, device=DEV)
+    need = gdn.gdn_prefill_workspace_bytes(H, d, d, torch.bfloat16, False, 1, T, x.chunk)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    o = torch.empty((T, H, d), dtype=torch.bfloat16, device=DEV)
+    it = [0]
+
+    def step():
+        q, k, v, g, b = sets[it[0] % 3]
+        it[0] += 1
+        gdn.gdn_prefill_chunked(q, k, v, g, b, cu, x.chunk, pool, slots, scale=x.scale, o=o,
+                                workspace=ws)
+
+    ms, wall = ev_time(step, steps, warmup)
+    byts = traffic.prefill_bytes(T, H, d, d, 2, False, 1, False)
+    flops = traffic.prefill_flops([T], H, d, d, x.chunk)
+    return dict(ms=ms, wall=wall, tokens=T, bytes=byts, flops=flops, H=H, d=d, ws_bytes=need)
+
+
+# ------------------------------------------------------------------------------- decode
+def bench_decode(steps, warmup, layers=4):
+    B, H, d, n_slots = 128, 32, 128, 256
+    pools = [inputs.decode_pool(1 + l, n_slots, H, d, d).to(DEV) for l in range(layers)]
+    slots = inputs.decode_slots(0, n_slots, B).to(DEV)
+    stream = inputs.DecodeStream(0, B, H, d, d)
+    toks = [[t.to(DEV) for t in stream.next()] for _ in range(layers)]
+    o = torch.empty((B, H, d), dtype=torch.bfloat16, device=DEV)
+    it = [0]
+
+    def step():
+        l = it[0] % layers
+        it[0] += 1
+        q, k, v, g, b = toks[l]
+        gdn.gdn_decode_step(q, k, v, g, b, pools[l], slots, scale=d ** -0.5, o=o)
+
+    ms, _ = ev_time(step, steps * layers, warmup * layers)
+    state = 4 * B * H * d * d
+    byts = traffic.decode_bytes(B, H, d, d, 2, False)
+    return dict(ms_per_layer_step=ms, state_update_GBps=2 * state / (ms * 1e-3) / 1e9,
+                total_GBps=byts / (ms * 1e-3) / 1e9, tokens_per_s=B / (ms * 1e-3),
+                hbm_frac=byts / (ms * 1e-3) / traffic.HBM_PEAK_BPS,
+                workload="dense decode B=128 H=32 d=128, 256-slot fp32 pool, 4 rotating layers")
+
+
+def bench_deltalog(cycles=4, warm_cycles=1, M=8):
+    B, H, d = 512, 32, 128
+    base = inputs.decode_pool(1, B, H, d, d).to(DEV)
+    slots = inputs.decode_slots(0, B, B).to(DEV)
+    stream = inputs.DecodeStream(0, B, H, d, d)
+    toks = [[t.to(DEV) for t in stream.next()] for _ in range(M)]
+    o = torch.empty((B, H, d), dtype=torch.bfloat16, device=DEV)
+    dense = base.clone()
+    pool = gdn.DeltaLogPool(base, M)
+    it = [0]
+
+    def dl_step():
+        q, k, v, g, b = toks[it[0] % M]
+        it[0] += 1
+        gdn.gdn_decode_deltalog(q, k, v, g, b, pool, slots, scale=d ** -0.5, o=o)
+
+    def dense_step():
+        q, k, v, g, b = toks[it[0] % M]
+        it[0] += 1
+        gdn.gdn_decode_step(q, k, v, g, b, dense, slots, scale=d ** -0.5, o=o)
+
+    ms_dl, _ = ev_time(dl_step, cycles * M, warm_cycles * M)   # whole merge cycles
+    it[0] = 0
+    ms_dn, _ = ev_time(dense_step, cycles * M, warm_cycles * M)
+    m = traffic.DeltaLogModel(B, H, d, d, M)
+    common = traffic.decode_bytes(B, H, d, d, 2, False) - 2 * m.c_state
+    return dict(ms_dense=ms_dn, ms_deltalog_cycle_avg=ms_dl, speedup=ms_dn / ms_dl,
+                dense_GBps=m.t_dense(common) / (ms_dn * 1e-3) / 1e9,
+                deltalog_model_GBps=m.t_delta(common) / (ms_dl * 1e-3) / 1e9,
+                modelled_speedup=m.t_dense(common) / m.t_delta(common),
+                tokens_per_s_dense=B / (ms_dn * 1e-3), tokens_per_s_deltalog=B / (ms_dl * 1e-3),
+                workload="B=512 H=32 d=128 fp32 state (1 GiB), M=8, cycle average")
+
+
+def bench_kda(steps=3, warmup=1):
+    x = inputs.kda_varlen_config(0)
+    T = x.x.shape[0]
+    xd, wd, cud, g, b = (t.to(DEV) for t in (x.x, x.conv_w, x.cu_seqlens, x.g, x.beta))
+    H, d = x.H, x.d
+    pool = torch.zeros((8, H, d, d), device=DEV)
+    slots = torch.arange(8, dtype=torch.int32, device=DEV)
+    qkv = torch.empty((3, T, H * d), dtype=torch.bfloat16, device=DEV)
+    need = gdn.gdn_prefill_workspace_bytes(H, d, d, torch.bfloat16, True, 8, T, x.chunk)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    o = torch.empty((T, H, d), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        gdn.gdn_conv1d_silu(xd, wd, cud, planes=3, y=qkv)
+        q, k, v = (qkv[i].view(T, H, d) for i in range(3))
+        gdn.gdn_prefill_chunked(q, k, v, g, b, cud, x.chunk, pool, slots, scale=x.scale,
+                                qk_l2norm=True, o=o, workspace=ws)
+
+    ms, _ = ev_time(step, steps, warmup)
+    lengths = (x.cu_seqlens[1:] - x.cu_seqlens[:-1]).tolist()
+    byts = traffic.prefill_bytes(T, H, d, d, 2, True, 8, False) + 2 * T * 3 * H * d * 2
+    return dict(ms=ms, tokens=T, tokens_per_s=T / (ms * 1e-3),
+                GBps=byts / (ms * 1e-3) / 1e9, hbm_frac=byts / (ms * 1e-3) / traffic.HBM_PEAK_BPS,
+                flops=traffic.prefill_flops(lengths, H, d, d, x.chunk),
+                workload=f"KDA varlen prefill, 8 seqs (T_total={T}), H=32, d=128, conv+SiLU, "
+                         "per-key gates, in-kernel L2 norm")
+
+
+# ------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(budget_s=20.0):
+    """The fp64 oracle (unmodified) on the host over the prefill workload: all 16 heads of
+    the first n tokens, n doubling from 512 until a run takes a few seconds or the whole
+    8192 tokens are done."""
+    import oracle
+    x = inputs.prefill_config(0)
+    threads = oracle.default_threads()
+    n = 512
+    while True:
+        sl = slice(0, n)
+        t0 = time.perf_counter()
+        oracle.recurrence(x.q[sl], x.k[sl], x.v[sl], x.g[sl], x.beta[sl],
+                          torch.tensor([0, n], dtype=torch.int32), scale=x.scale,
+                          n_threads=threads)
+        dt = time.perf_counter() - t0
+        if n >= x.q.shape[0] or dt * 2 > budget_s / 2:
+            break
+        n *= 2
+    return dict(value=n / dt, unit="tokens/s", cores=min(threads, x.q.shape[1]), kind="oracle",
+                sample=f"fp64 sequential recurrence, first {n} of 8192 tokens x 16 heads "
+                       f"({dt:.1f} s, one thread per (sequence, head) unit)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the core shards by requests and heads with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    gdn.load()
+    digest = source_digest()
+    log("prefill ...")
+    p = bench_prefill(args.steps, args.warmup)
+    secs = p["ms"] * 1e-3
+    achieved = p["bytes"] / secs
+    hbm_traffic = counter_traffic("prefill", digest)
+    line = {
+        "metric": METRIC,
+        "value": p["tokens"] / secs,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": p["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "GDN chunked prefill, 1 sequence, T=8192, H=16, d_k=d_v=128, "
+                               "chunk 64, bf16 q/k/v, fp32 gates/state",
+                   "global_batch": 1, "seq_len": p["tokens"], "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": traffic.HBM_PEAK_BPS / 1e9,
+                     "unit": "GB/s", "frac": achieved / traffic.HBM_PEAK_BPS,
+                     "traffic": hbm_traffic,
+                     "kernel": "gdn_prefill_chunked pass (seq_first + prep + scan kernels)",
+                     "algorithmic_bytes": p["bytes"],
+                     "mfma_TFLOPs": p["flops"] / secs / 1e12,
+                     "mfma_frac_bf16": p["flops"] / secs / traffic.BF16_MFMA_PEAK},
+    }
+    if not args.no_extras:
+        log("decode ...")
+        line["decode"] = bench_decode(args.steps, args.warmup)
+        log("deltalog ...")
+        line["deltalog"] = bench_deltalog()
+        log("kda ...")
+        line["kda_prefill"] = bench_kda()
+    if not args.no_cpu:
+        log("cpu baseline ...")
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,110 @@
+// Causal depthwise short convolution (width <= 4) followed by SiLU, over packed varlen
+// sequences, writing q|k|v planes.
+//
+// Page: [LA-Infra] "深度解析线性注意力机制演进与 AI Infra 实现", section "去掉分母引入卷积"
+// (per channel, fixed weights over the current and previous tokens, weight column
+// width-1 on the current token, then SiLU; zero history at a sequence start) and
+// "vLLM中Decode的实现" (one convolution over the concatenated q|k|v channels equals three).
+//
+// HBM-bound elementwise pass: each thread produces 8 adjacent channels of one token
+// (16-byte loads/stores for bf16), reading the current and previous width-1 tokens of the
+// same 8 channels (those rows are shared with the neighbouring tokens' threads through L2).
+#include "gdn_common.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+constexpr int CONV_THREADS = 256;
+
+// Each thread produces 8 adjacent channels of CONV_TT consecutive tokens: the weights are
+// read once (float4 per channel), each x row once, and the window slides in registers.
+constexpr int CONV_TT = 8;
+
+template <typename T, int W>
+__global__ __launch_bounds__(CONV_THREADS) void conv1d_silu_kernel(ConvArgs a) {
+    const int groups = a.channels / 8;
+    const int tgroups = (a.total_tokens + CONV_TT - 1) / CONV_TT;
+    const int64_t idx = (int64_t)blockIdx.x * CONV_THREADS + threadIdx.x;
+    if (idx >= (int64_t)tgroups * groups) return;
+    const int tg = (int)(idx / groups);
+    const int c0 = (int)(idx - (int64_t)tg * groups) * 8;
+    const int t0 = tg * CONV_TT;
+    // sequence of token t0: last n with cu_seqlens[n] <= t0 (binary search)
+    int lo = 0, hi = a.n_seqs;
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (a.cu_seqlens[mid] <= t0) lo = mid; else hi = mid;
+    }
+    int start = a.cu_seqlens[lo];
+    int next = a.cu_seqlens[lo + 1];
+    float wv[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        if constexpr (W == 4) {
+            f32x4 w4 = *reinterpret_cast<const f32x4*>(a.w + (size_t)(c0 + i) * 4);
+            wv[i][0] = w4[0]; wv[i][1] = w4[1]; wv[i][2] = w4[2]; wv[i][3] = w4[3];
+        } else {
+#pragma unroll
+            for (int j = 0; j < W; j++) wv[i][j] = a.w[(size_t)(c0 + i) * W + j];
+        }
+    }
+    const T* x = reinterpret_cast<const T*>(a.x);
+    // rows t0-(W-1) .. t0+CONV_TT-1, zero outside [0, total_tokens)
+    constexpr int NR = CONV_TT + W - 1;
+    float xr[NR][8];
+#pragma unroll
+    for (int r = 0; r < NR; r++) {
+        const int src = t0 - (W - 1) + r;
+        if (src >= 0 && src < a.total_tokens) {
+            load8<T>(x + (size_t)src * a.channels + c0, xr[r]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; i++) xr[r][i] = 0.f;
+        }
+    }
+    const int pc = a.channels / a.planes;
+    const int plane = c0 / pc;
+    T* ybase = reinterpret_cast<T*>(a.y) + (size_t)plane * a.total_tokens * pc + (c0 - plane * pc);
+#pragma unroll
+    for (int tt = 0; tt < CONV_TT; tt++) {
+        const int t = t0 + tt;
+        if (t >= a.total_tokens) break;
+        while (t >= next && lo + 1 < a.n_seqs) {  // crossed into the next sequence
+            lo++;
+            start = a.cu_seqlens[lo];
+            next = a.cu_seqlens[lo + 1];
+        }
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < W; j++) {
+            const int src = t - (W - 1) + j;
+            const bool keep = src >= start;  // zero history before the sequence start
+#pragma unroll
+            for (int i = 0; i < 8; i++) acc[i] += keep ? wv[i][j] * xr[tt + j][i] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i++) acc[i] = acc[i] / (1.f + __expf(-acc[i]));
+        store8<T>(ybase + (size_t)t * pc, acc);
+    }
+}
+
+template <typename T>
+static hipError_t conv_launch(const ConvArgs& a, hipStream_t s) {
+    const int64_t work = (int64_t)((a.total_tokens + CONV_TT - 1) / CONV_TT) * (a.channels / 8);
+    dim3 grid((unsigned)((work + CONV_THREADS - 1) / CONV_THREADS)), block(CONV_THREADS);
+    switch (a.width) {
+        case 2: hipLaunchKernelGGL((conv1d_silu_kernel<T, 2>), grid, block, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((conv1d_silu_kernel<T, 3>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((conv1d_silu_kernel<T, 4>), grid, block, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_conv1d(const ConvArgs& a, hipStream_t s) {
+    if (a.total_tokens == 0 || a.n_seqs == 0) return hipSuccess;
+    (void)hipGetLastError();  // report only errors raised by this call's launches
+    return a.dtype == 1 ? conv_launch<bf16>(a, s) : conv_launch<float>(a, s);
+}
+
+}  // namespace gdn

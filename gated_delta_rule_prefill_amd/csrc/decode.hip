@@ -1,0 +1,494 @@
+// One-token recurrent decode over a slot-indexed fp32 state pool (dense), and the DeltaLog
+// variant (dense base + append log, merged every M steps).
+//
+// Pages: [LA-Infra] "深度解析线性注意力机制演进与 AI Infra 实现", sections "GDN：增加遗忘门",
+// "KDA实现逻辑概述" (per-token step list), App. 2 (L2 norm); [Handbook] "线性注意力与混合架构的推理",
+// "投机解码与 PD 分离" (fixed slots, batched kernel addresses states by slot index);
+// [DeltaLog] "DeltaLog：延迟物化递归状态以加速线性注意力解码" reading notes, §1.2 (the step is
+// bound by the state stream, about 0.5 flop/byte), §2.1-2.4 (base + log, Algorithm 1,
+// Eqs. 4-7), §2.6 (one writer for the shared log metadata).
+//
+// Design (MI355X): one 256-thread workgroup owns one (request, head) state, d_k x d_v fp32
+// (64 KiB at d = 128). Each thread holds 4 adjacent value columns of d_k / (256 / (d_v/4))
+// rows in registers, so the state is read from HBM once, both column reductions
+// (vhat = Sbar^T k and Sbar^T q) come from the same registers, and the update is written
+// back once with 16-byte coalesced accesses along d_v. Reductions: xor-shuffles inside a
+// wave, one LDS exchange across the 4 waves. With B*H workgroups (4096 at B = 128, H = 32)
+// every CU keeps several 64 KiB streams in flight. Because one workgroup covers the whole
+// value range, the DeltaLog key-side replay coefficients are computed once per
+// (request, head) in-workgroup and a single thread is the one writer of K_log, Lambda_log,
+// lbar and L — no separate replay-prep launch and no scratch buffer.
+#include "gdn_common.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+constexpr float L2_EPS = 1e-6f;
+constexpr int DEC_THREADS = 256;
+constexpr int DL_MAXLOG = 16;  // M - 1 <= 16
+
+template <int DK, int DV>
+struct DecGeom {
+    static constexpr int TPR = DV / 4;                 // threads per state row
+    static constexpr int RPP = DEC_THREADS / TPR;      // rows per pass
+    static constexpr int NP = (DK + RPP - 1) / RPP;    // passes
+    static constexpr int NWAVE = DEC_THREADS / WAVE;
+    // lanes of a wave that hold the same column group
+    static constexpr int ROWS_PER_WAVE = WAVE / TPR;
+};
+
+// Shared prologue: stage k, q (fp32, optionally L2-normalised), v, and per-key decay in
+// LDS; every wave computes the norms itself to avoid an extra barrier.
+template <typename T, int DK, int DV>
+struct DecSmem {
+    float k[DK];
+    float q[DK];
+    float v[DV];
+    float gk[DK];
+    float red_v[DecGeom<DK, DV>::NWAVE][DV];
+    float red_q[DecGeom<DK, DV>::NWAVE][DV];
+    float r[DV];
+};
+
+template <int DK>
+__device__ __forceinline__ void kq_norms(const float* ks, const float* qs, float& ik, float& iq,
+                                         float& kq, bool l2norm) {
+    // each wave reduces the full d_k vectors (DK <= 128: at most two values per lane)
+    const int l = lane_id();
+    float sk = 0.f, sq = 0.f, skq = 0.f;
+    for (int i = l; i < DK; i += WAVE) {
+        float a = ks[i], b = qs[i];
+        sk += a * a;
+        sq += b * b;
+        skq += a * b;
+    }
+    sk = group_sum<WAVE>(sk);
+    sq = group_sum<WAVE>(sq);
+    skq = group_sum<WAVE>(skq);
+    if (l2norm) {
+        ik = rsqrtf(sk + L2_EPS);
+        iq = rsqrtf(sq + L2_EPS);
+    } else {
+        ik = 1.f;
+        iq = 1.f;
+    }
+    kq = skq * ik * iq;
+}
+
+template <typename T, int DK, int DV, bool PERKEY>
+__global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecodeArgs a) {
+    using G = DecGeom<DK, DV>;
+    __shared__ DecSmem<T, DK, DV> sm;
+    const int tid = threadIdx.x;
+    const int H = a.H;
+    const int bh = blockIdx.x;
+    const int b = bh / H, h = bh - (bh / H) * H;
+    const int slot = a.slots[b];
+    T* o = reinterpret_cast<T*>(a.o) + (size_t)bh * DV;
+    if (slot < 0 || slot >= a.n_slots) {
+        if (tid < DV / 4) {
+            float z[4] = {0.f, 0.f, 0.f, 0.f};
+            store4<T>(o + tid * 4, z);
+        }
+        return;
+    }
+    const int cg = tid % G::TPR;
+    const int r0 = tid / G::TPR;
+    float* S = a.pool + ((size_t)slot * H + h) * DK * DV;
+
+    // issue the state stream first
+    f32x4 st[G::NP];
+#pragma unroll
+    for (int p = 0; p < G::NP; p++) {
+        const int r = r0 + p * G::RPP;
+        if (r < DK) st[p] = *reinterpret_cast<const f32x4*>(S + (size_t)r * DV + cg * 4);
+    }
+    const T* qp = reinterpret_cast<const T*>(a.q) + (size_t)bh * DK;
+    const T* kp = reinterpret_cast<const T*>(a.k) + (size_t)bh * DK;
+    const T* vp = reinterpret_cast<const T*>(a.v) + (size_t)bh * DV;
+    if (tid < DK) {
+        sm.k[tid] = to_f32(kp[tid]);
+        sm.q[tid] = to_f32(qp[tid]);
+        if (PERKEY) sm.gk[tid] = __expf(a.g[(size_t)bh * DK + tid]);
+    }
+    if (tid < DV) sm.v[tid] = to_f32(vp[tid]);
+    const float beta = a.beta[bh];
+    const float alpha = PERKEY ? 1.f : __expf(a.g[bh]);
+    lds_barrier();
+
+    float ik, iq, kq;
+    kq_norms<DK>(sm.k, sm.q, ik, iq, kq, a.l2norm != 0);
+
+    // decay and the two column reductions from the same registers
+    float pv[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
+    float kr[G::NP];
+#pragma unroll
+    for (int p = 0; p < G::NP; p++) {
+        const int r = r0 + p * G::RPP;
+        if (r < DK) {
+            const float dec = PERKEY ? sm.gk[r] : alpha;
+            const float kk = sm.k[r] * ik, qq = sm.q[r] * iq;
+            kr[p] = kk;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                float s = st[p][i] * dec;
+                st[p][i] = s;
+                pv[i] += s * kk;
+                pq[i] += s * qq;
+            }
+        }
+    }
+    // reduce across the lanes of this wave that share the column group
+#pragma unroll
+    for (int off = G::TPR; off < WAVE; off <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            pv[i] += __shfl_xor(pv[i], off, WAVE);
+            pq[i] += __shfl_xor(pq[i], off, WAVE);
+        }
+    }
+    const int w = wave_id();
+    if (lane_id() < G::TPR) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            sm.red_v[w][cg * 4 + i] = pv[i];
+            sm.red_q[w][cg * 4 + i] = pq[i];
+        }
+    }
+    lds_barrier();
+    if (tid < DV) {
+        float vh = 0.f, sh = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < G::NWAVE; ww++) {
+            vh += sm.red_v[ww][tid];
+            sh += sm.red_q[ww][tid];
+        }
+        const float r = beta * (sm.v[tid] - vh);
+        sm.r[tid] = r;
+        o[tid] = from_f32<T>(a.scale * (sh + kq * r));
+    }
+    lds_barrier();
+    float rr[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) rr[i] = sm.r[cg * 4 + i];
+#pragma unroll
+    for (int p = 0; p < G::NP; p++) {
+        const int r = r0 + p * G::RPP;
+        if (r < DK) {
+            f32x4 s = st[p];
+#pragma unroll
+            for (int i = 0; i < 4; i++) s[i] += kr[p] * rr[i];
+            *reinterpret_cast<f32x4*>(S + (size_t)r * DV + cg * 4) = s;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------ DeltaLog
+template <int DK, int DV>
+struct DlSmem {
+    float k[DK];
+    float q[DK];
+    float v[DV];
+    float klog[DL_MAXLOG][DK];
+    float ulog[DL_MAXLOG][DV];
+    float lam[DL_MAXLOG];
+    float ck[DL_MAXLOG];  // e^{lp - Lambda_i} (k . K_i)
+    float cq[DL_MAXLOG];  // e^{lp - Lambda_i} (q . K_i)
+    float wl[DL_MAXLOG];  // e^{lp - Lambda_i}
+    float red_v[DecGeom<DK, DV>::NWAVE][DV];
+    float red_q[DecGeom<DK, DV>::NWAVE][DV];
+    float b[DV];
+};
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(DEC_THREADS) void deltalog_kernel(DeltaLogArgs a) {
+    using G = DecGeom<DK, DV>;
+    __shared__ DlSmem<DK, DV> sm;
+    const int tid = threadIdx.x;
+    const int H = a.H;
+    const int bh = blockIdx.x;
+    const int b = bh / H, h = bh - (bh / H) * H;
+    const int slot = a.slots[b];
+    T* o = reinterpret_cast<T*>(a.o) + (size_t)bh * DV;
+    if (slot < 0 || slot >= a.n_slots) {
+        if (tid < DV / 4) {
+            float z[4] = {0.f, 0.f, 0.f, 0.f};
+            store4<T>(o + tid * 4, z);
+        }
+        return;
+    }
+    const int C = a.M - 1;
+    const size_t sh = (size_t)slot * H + h;
+    const int cg = tid % G::TPR;
+    const int r0 = tid / G::TPR;
+    float* S = a.base + sh * DK * DV;
+    f32x4 st[G::NP];
+#pragma unroll
+    for (int p = 0; p < G::NP; p++) {
+        const int r = r0 + p * G::RPP;
+        if (r < DK) st[p] = *reinterpret_cast<const f32x4*>(S + (size_t)r * DV + cg * 4);
+    }
+    // clamp so that corrupted metadata can never index past the log buffers
+    const int L = min(max(a.len[sh], 0), C);
+    const float lp = a.lbar[sh] + a.g[bh];  // Algorithm 1: accumulate the decay first
+    const T* qp = reinterpret_cast<const T*>(a.q) + (size_t)bh * DK;
+    const T* kp = reinterpret_cast<const T*>(a.k) + (size_t)bh * DK;
+    const T* vp = reinterpret_cast<const T*>(a.v) + (size_t)bh * DV;
+    if (tid < DK) {
+        sm.k[tid] = to_f32(kp[tid]);
+        sm.q[tid] = to_f32(qp[tid]);
+    }
+    if (tid < DV) sm.v[tid] = to_f32(vp[tid]);
+    const uint16_t* kl = a.klog + sh * C * DK;
+    const float* ul = a.ulog + sh * C * DV;
+    for (int i = tid; i < L * DK; i += DEC_THREADS) {
+        uint32_t bits = (uint32_t)kl[i] << 16;
+        sm.klog[i / DK][i % DK] = __builtin_bit_cast(float, bits);
+    }
+    for (int i = tid; i < L * DV; i += DEC_THREADS) sm.ulog[i / DV][i % DV] = ul[i];
+    if (tid < L) {
+        float lam = a.lamlog[sh * C + tid];
+        sm.lam[tid] = lam;
+        sm.wl[tid] = __expf(lp - lam);
+    }
+    const float beta = a.beta[bh];
+    lds_barrier();
+
+    float ik, iq, kq;
+    kq_norms<DK>(sm.k, sm.q, ik, iq, kq, a.l2norm != 0);
+    // key-side replay coefficients, one wave per log entry (strided)
+    {
+        const int w = wave_id(), l = lane_id();
+        for (int e = w; e < L; e += G::NWAVE) {
+            float sk = 0.f, sq = 0.f;
+            for (int i = l; i < DK; i += WAVE) {
+                sk += sm.k[i] * sm.klog[e][i];
+                sq += sm.q[i] * sm.klog[e][i];
+            }
+            sk = group_sum<WAVE>(sk);
+            sq = group_sum<WAVE>(sq);
+            if (l == 0) {
+                sm.ck[e] = sm.wl[e] * sk * ik;
+                sm.cq[e] = sm.wl[e] * sq * iq;
+            }
+        }
+    }
+    // base reads (undecayed base; the scalar factor e^{lp} is applied after the reduction)
+    float pv[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < G::NP; p++) {
+        const int r = r0 + p * G::RPP;
+        if (r < DK) {
+            const float kk = sm.k[r] * ik, qq = sm.q[r] * iq;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                pv[i] += st[p][i] * kk;
+                pq[i] += st[p][i] * qq;
+            }
+        }
+    }
+#pragma unroll
+    for (int off = G::TPR; off < WAVE; off <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            pv[i] += __shfl_xor(pv[i], off, WAVE);
+            pq[i] += __shfl_xor(pq[i], off, WAVE);
+        }
+    }
+    {
+        const int w = wave_id();
+        if (lane_id() < G::TPR) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                sm.red_v[w][cg * 4 + i] = pv[i];
+                sm.red_q[w][cg * 4 + i] = pq[i];
+            }
+        }
+    }
+    lds_barrier();
+    const float dec = __expf(lp);
+    if (tid < DV) {
+        float vh = 0.f, shq = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < G::NWAVE; ww++) {
+            vh += sm.red_v[ww][tid];
+            shq += sm.red_q[ww][tid];
+        }
+        vh *= dec;
+        shq *= dec;
+        for (int e = 0; e < L; e++) {
+            vh += sm.ck[e] * sm.ulog[e][tid];
+            shq += sm.cq[e] * sm.ulog[e][tid];
+        }
+        const float bb = beta * (sm.v[tid] - vh);
+        sm.b[tid] = bb;
+        o[tid] = from_f32<T>(a.scale * (shq + kq * bb));
+    }
+    if (L < C) {
+        // append: the base is not written; one value entry, and a single writer for the
+        // shared key entry and metadata of this (slot, head)
+        lds_barrier();
+        if (tid < DV) a.ulog[(sh * C + L) * DV + tid] = sm.b[tid];
+        if (tid < DK) {
+            bf16 kb = (bf16)(sm.k[tid] * ik);
+            a.klog[(sh * C + L) * DK + tid] = __builtin_bit_cast(uint16_t, kb);
+        }
+        if (tid == 0) {
+            a.lamlog[sh * C + L] = lp;
+            a.lbar[sh] = lp;
+            a.len[sh] = L + 1;
+        }
+        return;
+    }
+    // merge (Eq. 6): fold the log and the current update into the base, clear the log
+    lds_barrier();
+    float bb[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) bb[i] = sm.b[cg * 4 + i];
+#pragma unroll
+    for (int p = 0; p < G::NP; p++) {
+        const int r = r0 + p * G::RPP;
+        if (r < DK) {
+            f32x4 s = st[p];
+            const float kk = sm.k[r] * ik;
+#pragma unroll
+            for (int i = 0; i < 4; i++) s[i] = s[i] * dec + kk * bb[i];
+            for (int e = 0; e < L; e++) {
+                const float we = sm.wl[e] * sm.klog[e][r];
+#pragma unroll
+                for (int i = 0; i < 4; i++) s[i] += we * sm.ulog[e][cg * 4 + i];
+            }
+            *reinterpret_cast<f32x4*>(S + (size_t)r * DV + cg * 4) = s;
+        }
+    }
+    if (tid == 0) {
+        a.lbar[sh] = 0.f;
+        a.len[sh] = 0;
+    }
+}
+
+// reset (mode 0) or materialize (mode 1) the listed slots; grid = n * H
+template <int DK, int DV>
+__global__ __launch_bounds__(DEC_THREADS) void deltalog_maint_kernel(DeltaLogArgs a, int mode) {
+    using G = DecGeom<DK, DV>;
+    __shared__ float klog[DL_MAXLOG][DK];
+    __shared__ float ulog[DL_MAXLOG][DV];
+    __shared__ float wl[DL_MAXLOG];
+    const int tid = threadIdx.x;
+    const int H = a.H;
+    const int n = blockIdx.x / H, h = blockIdx.x % H;
+    const int slot = a.slots[n];
+    if (slot < 0 || slot >= a.n_slots) return;
+    const size_t sh = (size_t)slot * H + h;
+    if (mode == 1) {
+        const int C = a.M - 1;
+        const int L = min(max(a.len[sh], 0), C);
+        const float lb = a.lbar[sh];
+        const uint16_t* kl = a.klog + sh * C * DK;
+        const float* ul = a.ulog + sh * C * DV;
+        for (int i = tid; i < L * DK; i += DEC_THREADS) {
+            uint32_t bits = (uint32_t)kl[i] << 16;
+            klog[i / DK][i % DK] = __builtin_bit_cast(float, bits);
+        }
+        for (int i = tid; i < L * DV; i += DEC_THREADS) ulog[i / DV][i % DV] = ul[i];
+        if (tid < L) wl[tid] = __expf(lb - a.lamlog[sh * C + tid]);
+        lds_barrier();
+        const float dec = __expf(lb);
+        const int cg = tid % G::TPR;
+        const int r0 = tid / G::TPR;
+        float* S = a.base + sh * DK * DV;
+#pragma unroll
+        for (int p = 0; p < G::NP; p++) {
+            const int r = r0 + p * G::RPP;
+            if (r < DK) {
+                f32x4 s = *reinterpret_cast<const f32x4*>(S + (size_t)r * DV + cg * 4);
+#pragma unroll
+                for (int i = 0; i < 4; i++) s[i] *= dec;
+                for (int e = 0; e < L; e++) {
+                    const float we = wl[e] * klog[e][r];
+#pragma unroll
+                    for (int i = 0; i < 4; i++) s[i] += we * ulog[e][cg * 4 + i];
+                }
+                *reinterpret_cast<f32x4*>(S + (size_t)r * DV + cg * 4) = s;
+            }
+        }
+        lds_barrier();
+    }
+    if (tid == 0) {
+        a.lbar[sh] = 0.f;
+        a.len[sh] = 0;
+    }
+}
+
+// ------------------------------------------------------------------------------- launch
+template <typename T, int D>
+static hipError_t dec_dispatch_gate(const DecodeArgs& a, hipStream_t s) {
+    dim3 grid((unsigned)(a.batch * a.H)), block(DEC_THREADS);
+    if (a.gate == 1)
+        hipLaunchKernelGGL((decode_kernel<T, D, D, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((decode_kernel<T, D, D, false>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t dec_dispatch_dim(const DecodeArgs& a, hipStream_t s) {
+    switch (a.dk) {
+        case 16: return dec_dispatch_gate<T, 16>(a, s);
+        case 32: return dec_dispatch_gate<T, 32>(a, s);
+        case 64: return dec_dispatch_gate<T, 64>(a, s);
+        case 128: return dec_dispatch_gate<T, 128>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+    if (a.batch == 0) return hipSuccess;
+    (void)hipGetLastError();  // report only errors raised by this call's launches
+    return a.dtype == 1 ? dec_dispatch_dim<bf16>(a, s) : dec_dispatch_dim<float>(a, s);
+}
+
+template <typename T, int D>
+static hipError_t dl_launch(const DeltaLogArgs& a, hipStream_t s) {
+    dim3 grid((unsigned)(a.batch * a.H)), block(DEC_THREADS);
+    hipLaunchKernelGGL((deltalog_kernel<T, D, D>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t dl_dispatch_dim(const DeltaLogArgs& a, hipStream_t s) {
+    switch (a.dk) {
+        case 16: return dl_launch<T, 16>(a, s);
+        case 32: return dl_launch<T, 32>(a, s);
+        case 64: return dl_launch<T, 64>(a, s);
+        case 128: return dl_launch<T, 128>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_deltalog(const DeltaLogArgs& a, hipStream_t s) {
+    if (a.batch == 0) return hipSuccess;
+    (void)hipGetLastError();  // report only errors raised by this call's launches
+    return a.dtype == 1 ? dl_dispatch_dim<bf16>(a, s) : dl_dispatch_dim<float>(a, s);
+}
+
+template <int D>
+static hipError_t dlm_launch(const DeltaLogArgs& a, int mode, hipStream_t s) {
+    dim3 grid((unsigned)(a.batch * a.H)), block(DEC_THREADS);
+    hipLaunchKernelGGL((deltalog_maint_kernel<D, D>), grid, block, 0, s, a, mode);
+    return hipGetLastError();
+}
+
+hipError_t launch_deltalog_maint(const DeltaLogArgs& a, int mode, hipStream_t s) {
+    if (a.batch == 0) return hipSuccess;
+    (void)hipGetLastError();  // report only errors raised by this call's launches
+    switch (a.dk) {
+        case 16: return dlm_launch<16>(a, mode, s);
+        case 32: return dlm_launch<32>(a, mode, s);
+        case 64: return dlm_launch<64>(a, mode, s);
+        case 128: return dlm_launch<128>(a, mode, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

@@ -1,0 +1,104 @@
+// Host-side launch interface between the C ABI layer (gdn_api.cpp) and the kernel files.
+// Arguments arrive here already validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Prefill workspace sections (all device pointers into the caller's workspace).
+// Per (chunk, head) unit, with C the chunk size, CP the contraction-padded chunk length
+// (C rounded up to the MFMA K step of the element type), e the element size:
+//   wneg  [C][DKP]   e   -W (correction directions, negated)      row-major
+//   qin   [C][DKP]   e   Q_in = s * Q * e^{G}                      row-major
+// (DKP = d_k rounded up to the MFMA contraction step, zero-padded)
+//   kgt   [d_k][CP]  e   K_g^T, K_g = K * e^{G_C - G}              (key-channel major)
+//   mmat  [C][CP]    e   M (lower triangular incl. diagonal)        row-major
+//   ut    [d_v][C]   f32 U^T (local residuals)                     (value-channel major)
+//   decay [d_k]      f32 e^{G_C} per key channel
+struct PrefillWs {
+    int32_t* chunk_info;   // [max_chunks][4]: seq, token start, length, 0
+    int32_t* seq_first;    // [n_seqs + 1] first chunk index of each sequence
+    void* wneg;
+    void* qin;
+    void* kgt;
+    void* mmat;
+    float* ut;
+    float* decay;
+    void* dump;            // scratch words that absorb stores of lanes past a sequence end
+    int64_t max_chunks;
+};
+
+struct PrefillArgs {
+    int dtype, gate, H, dk, dv, chunk, cp, l2norm;
+    float scale;
+    const void *q, *k, *v;
+    const float *g, *beta;
+    const int32_t* cu_seqlens;
+    int n_seqs, total_tokens;
+    float* state_pool;
+    int n_slots;
+    const int32_t* slots;
+    const int32_t* has_init;
+    void* o;
+    PrefillWs ws;
+};
+
+// Chunk length / key dim rounded up to the MFMA contraction step of the element type
+// (bf16: 32, fp32: 4); the padding is zero-filled.
+inline int prefill_cp(int dtype, int chunk) {
+    int kb = dtype == 1 ? 32 : 4;
+    return ((chunk + kb - 1) / kb) * kb;
+}
+inline int prefill_dkp(int dtype, int dk) { return prefill_cp(dtype, dk); }
+
+// Byte size of the prefill workspace and, if base != nullptr, its carving.
+size_t prefill_ws_layout(int dtype, int H, int dk, int dv, int chunk, int n_seqs,
+                         int total_tokens, void* base, PrefillWs* out);
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+    int dtype, gate, H, dk, dv, l2norm;
+    float scale;
+    const void *q, *k, *v;
+    const float *g, *beta;
+    float* pool;
+    int n_slots;
+    const int32_t* slots;
+    int batch;
+    void* o;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+struct DeltaLogArgs {
+    int dtype, H, dk, dv, l2norm, M;
+    float scale;
+    const void *q, *k, *v;
+    const float *g, *beta;
+    float* base;
+    float* lbar;
+    uint16_t* klog;
+    float* ulog;
+    float* lamlog;
+    int32_t* len;
+    int n_slots;
+    const int32_t* slots;
+    int batch;
+    void* o;
+};
+hipError_t launch_deltalog(const DeltaLogArgs& a, hipStream_t stream);
+// mode 0: reset (L = 0, lbar = 0); mode 1: materialize (fold the log into the base)
+hipError_t launch_deltalog_maint(const DeltaLogArgs& a, int mode, hipStream_t stream);
+
+struct ConvArgs {
+    int dtype, channels, width, planes, n_seqs, total_tokens;
+    const void* x;
+    const float* w;
+    const int32_t* cu_seqlens;
+    void* y;
+};
+hipError_t launch_conv1d(const ConvArgs& a, hipStream_t stream);
+
+}  // namespace gdn

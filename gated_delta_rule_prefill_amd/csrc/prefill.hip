@@ -1,0 +1,86 @@
+// Prefill front end: per-sequence chunk table (device-side, no host synchronisation),
+// workspace carving and dispatch to the element-type instantiations.
+#include "gdn_common.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+
+// seq_first[n] = sum_{s < n} ceil(len_s / C), n = 0..n_seqs (one workgroup, tiled scan).
+__global__ __launch_bounds__(256) void seq_first_kernel(const int32_t* cu, int n_seqs, int C,
+                                                        int32_t* seq_first) {
+    __shared__ int32_t part[256];
+    __shared__ int32_t carry;
+    if (threadIdx.x == 0) carry = 0;
+    __syncthreads();
+    for (int base = 0; base < n_seqs; base += 256) {
+        const int n = base + (int)threadIdx.x;
+        int cnt = 0;
+        if (n < n_seqs) {
+            const int len = max(0, cu[n + 1] - cu[n]);
+            cnt = (len + C - 1) / C;
+        }
+        part[threadIdx.x] = cnt;
+        __syncthreads();
+        // inclusive Hillis-Steele scan over 256 entries
+        for (int off = 1; off < 256; off <<= 1) {
+            int v = threadIdx.x >= (unsigned)off ? part[threadIdx.x - off] : 0;
+            __syncthreads();
+            part[threadIdx.x] += v;
+            __syncthreads();
+        }
+        if (n < n_seqs) seq_first[n] = carry + part[threadIdx.x] - cnt;
+        __syncthreads();
+        if (threadIdx.x == 255) carry += part[255];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) seq_first[n_seqs] = carry;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t prefill_ws_layout(int dtype, int H, int dk, int dv, int chunk, int n_seqs,
+                         int total_tokens, void* base, PrefillWs* out) {
+    const size_t e = dtype == 1 ? 2 : 4;
+    const int cp = prefill_cp(dtype, chunk);
+    const int dkp = prefill_dkp(dtype, dk);
+    // upper bound on the chunk count: sum_s ceil(len_s / C) <= (T + n (C - 1)) / C
+    const int64_t max_chunks =
+        ((int64_t)total_tokens + (int64_t)n_seqs * (chunk - 1)) / chunk;
+    const size_t units = (size_t)max_chunks * H;
+    size_t off = 0;
+    const size_t o_seq = off; off = align256(off + sizeof(int32_t) * (size_t)(n_seqs + 1));
+    const size_t o_w = off;   off = align256(off + units * chunk * dkp * e);
+    const size_t o_q = off;   off = align256(off + units * chunk * dkp * e);
+    const size_t o_k = off;   off = align256(off + units * dk * cp * e);
+    const size_t o_m = off;   off = align256(off + units * chunk * cp * e);
+    const size_t o_u = off;   off = align256(off + units * dv * chunk * 4);
+    const size_t o_d = off;   off = align256(off + units * dk * 4);
+    const size_t o_x = off;   off = align256(off + 256 * 4);
+    if (out != nullptr) {
+        char* b = static_cast<char*>(base);
+        out->chunk_info = nullptr;
+        out->seq_first = reinterpret_cast<int32_t*>(b + o_seq);
+        out->wneg = b + o_w;
+        out->qin = b + o_q;
+        out->kgt = b + o_k;
+        out->mmat = b + o_m;
+        out->ut = reinterpret_cast<float*>(b + o_u);
+        out->decay = reinterpret_cast<float*>(b + o_d);
+        out->dump = b + o_x;
+        out->max_chunks = max_chunks;
+    }
+    return off;
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
+    // zero tokens still defines the final states (initial state, or zero), so only an
+    // empty sequence list is a no-op
+    if (a.n_seqs == 0) return hipSuccess;
+    (void)hipGetLastError();  // report only errors raised by this call's launches
+    return a.dtype == 1 ? launch_prefill_bf16(a, s) : launch_prefill_f32(a, s);
+}
+
+}  // namespace gdn

@@ -1,0 +1,820 @@
+// Chunk-parallel prefill kernels (templates; instantiated per element type in
+// prefill_bf16.hip / prefill_f32.hip).
+//
+// Page: [LA-Infra] "深度解析线性注意力机制演进与 AI Infra 实现", section "Prefill中的Chunk微观并行":
+//   "计算 Δchunk"        local residuals U from the unit lower-triangular system (I + A) U = B V,
+//   "计算 Transitionchunk" correction directions W from (I + A) W = B K_in with the same R,
+//   "块内输出"            O = Q_in S_0 + M E without materialising per-token states,
+//   "完整计算顺序"         the six-step order (G, K_in/K_g/e^{G_C}, A and R, U and W, E and S_C,
+//                        Q_in/M/O); the blocked inverse of L = I + A through 2x2 blocks
+//                        ((L^{-1})_{21} = -L_22^{-1} L_21 L_11^{-1}) with 16x16 leaves;
+// appendix "附1. chunk内 A和M 的计算" (per-key gates: 16x16 sub-blocks, reference point = the
+// first token of the row block, A and M from one pass sharing the key-side operand).
+// Orientation: S is d_k x d_v here (the page's S^T); the page's E^T K_g is K_g^T E.
+//
+// Work split on MI355X:
+//   prep  (grid: chunks x heads, fully parallel): everything that depends only on the chunk
+//         — G, A and M on MFMA, R by blocked substitution in fp32, U and W on MFMA — written
+//         once to a workspace in MFMA-operand-ready layouts (-W and Q_in row-major, K_g^T
+//         key-major, M row-major, U^T value-major, e^{G_C}).
+//   scan  (grid: sequences x heads x d_v/16 value tiles, serial over a sequence's chunks):
+//         the only sequential part. A 16-column slice of the fp32 state lives in MFMA
+//         accumulators across the whole sequence; per chunk
+//           E = U - W S,  O = Q_in S + M E,  S <- Diag(e^{G_C}) S + K_g^T E
+//         with the next chunk's operands prefetched into registers during the current one.
+//         The value tiles of one (sequence, head) are placed on the same XCD so the shared
+//         per-chunk operands are served from that XCD's L2.
+#pragma once
+#include "gdn_common.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+constexpr int PF_THREADS = 256;
+constexpr int PF_WAVES = PF_THREADS / WAVE;
+constexpr int SCAN_BV = 16;
+
+template <typename T, int DK, int DV, int C>
+struct PfCfg {
+    using MM = Mma<T>;
+    static constexpr int KB = MM::KB;
+    static constexpr int KPL = MM::KPL;
+    static constexpr int CP = ((C + KB - 1) / KB) * KB;     // padded token contraction
+    static constexpr int DKP = ((DK + KB - 1) / KB) * KB;   // padded key-channel contraction
+    static constexpr int PADE = 16 / (int)sizeof(T);          // 16-byte row padding
+    static constexpr int LDK = DKP + PADE;                    // LDS row stride, d_k rows
+    static constexpr int LDC = CP + PADE;                     // LDS row stride, token rows
+    static constexpr int NB = C / 16;                         // 16-token blocks
+};
+
+// chunk -> (sequence, first token, length) from the per-sequence first-chunk table
+struct ChunkLoc {
+    int seq, tok0, len;
+};
+__device__ __forceinline__ ChunkLoc locate_chunk(int c, const int32_t* seq_first,
+                                                 const int32_t* cu, int n_seqs, int C,
+                                                 int total_tokens) {
+    ChunkLoc r;
+    r.seq = -1;
+    r.tok0 = 0;
+    r.len = 0;
+    if (c >= seq_first[n_seqs]) return r;
+    int lo = 0, hi = n_seqs;  // find last n with seq_first[n] <= c
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (seq_first[mid] <= c) lo = mid; else hi = mid;
+    }
+    r.tok0 = cu[lo] + (c - seq_first[lo]) * C;
+    r.len = min(C, min(cu[lo + 1], total_tokens) - r.tok0);
+    if (r.tok0 < 0 || r.len <= 0) {  // inconsistent cu_seqlens: never index outside q/k/v
+        r.len = 0;
+        return r;
+    }
+    r.seq = lo;
+    return r;
+}
+
+// Fragment-major layout of an R x K MFMA A-operand matrix (R a multiple of 16, K of KB):
+// the 16 x KB fragment (row block rb, k block kb) is stored as 64 lane slots of KPL elements,
+// slot `lane` holding X[16 rb + (lane & 15)][kb KB + (lane >> 4) KPL + e]. A wave then loads a
+// fragment as one contiguous run (1 KiB for bf16, 8 full cache lines) instead of 16 rows that
+// are each touched for 64 bytes; the vector-memory pipe of a CU processes the former at
+// twice the rate.
+template <typename T>
+struct Frag {
+    static constexpr int KB = Mma<T>::KB, KPL = Mma<T>::KPL;
+    __device__ __forceinline__ static int off(int row, int col, int K) {
+        const int kb = col / KB, kk = col - kb * KB;
+        const int ln = (row & 15) + 16 * (kk / KPL);
+        return (((row >> 4) * (K / KB) + kb) * 64 + ln) * KPL + (kk % KPL);
+    }
+    // N consecutive columns starting at col (col a multiple of N)
+    template <int N>
+    __device__ __forceinline__ static void store_run(T* base, int row, int col, int K,
+                                                     const float* v) {
+        if constexpr (KPL >= N) {
+            if constexpr (N == 8) store8<T>(base + off(row, col, K), v);
+            else store4<T>(base + off(row, col, K), v);
+        } else {
+#pragma unroll
+            for (int i = 0; i < N; i++) base[off(row, col + i, K)] = from_f32<T>(v[i]);
+        }
+    }
+    __device__ __forceinline__ static const T* ptr(const T* base, int rb, int kb, int K, int ln) {
+        return base + ((rb * (K / KB) + kb) * 64 + ln) * KPL;
+    }
+};
+
+// =====================================================================================
+// prep kernel
+// =====================================================================================
+template <typename T, int DK, int DV, int C, bool PERKEY>
+struct PrepSmem {
+    using F = PfCfg<T, DK, DV, C>;
+    // live for the whole kernel
+    alignas(16) float af[C][C + 1];   // A (strictly lower); upper part reused as scratch
+    alignas(16) float bs[C];          // beta
+    alignas(16) T kint[DK][F::LDC];   // (diag(beta) K_in)^T, made in phase A, used in phase B
+    union {
+        struct {                      // phase A: inputs, gates, A and M
+            alignas(16) T ks[C][F::LDK];   // keys (normalised if requested)
+            alignas(16) T qs[C][F::LDK];   // queries
+            alignas(16) float gs[PERKEY ? C : 1][PERKEY ? DK + 4 : C];  // cumulative log gate
+            float gseg[PERKEY ? PF_THREADS / DK : 1][PERKEY ? DK : 1];    // segment totals
+        } a;
+        struct {                      // phase B: triangular solve, U and W
+            alignas(16) float rf[C][C + 1];  // R = (I + A)^{-1} (lower, unit diagonal)
+            alignas(16) T rs[C][F::LDC];     // R as an MFMA operand
+            alignas(16) T vt[DV][F::LDC];    // (diag(beta) V)^T
+        } b;
+    } u;
+};
+
+template <bool PERKEY, int DK, int C>
+__device__ __forceinline__ float gval(const float (*gs)[PERKEY ? DK + 4 : C], int i, int c) {
+    if constexpr (PERKEY) return gs[i][c];
+    else return gs[0][i];
+}
+
+template <typename T, int DK, int DV, int C, bool PERKEY>
+__global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a) {
+    using F = PfCfg<T, DK, DV, C>;
+    using MM = typename F::MM;
+    constexpr int KB = F::KB, KPL = F::KPL, CP = F::CP, NB = F::NB, DKP = F::DKP;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    auto& sm = *reinterpret_cast<PrepSmem<T, DK, DV, C, PERKEY>*>(smem_raw);
+
+    const int H = a.H;
+    const int c = blockIdx.x / H;
+    const int h = blockIdx.x - c * H;
+    const ChunkLoc loc = locate_chunk(c, a.ws.seq_first, a.cu_seqlens, a.n_seqs, C, a.total_tokens);
+    if (loc.seq < 0) return;
+    const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+    const size_t u = (size_t)c * H + h;  // (chunk, head) workspace unit
+
+    // V rows are only needed in phase B; fetch them into registers now so the load latency
+    // overlaps phase A (tokens past the chunk end and the padding up to CP read as zero)
+    constexpr int TPRV = DV / 8;
+    constexpr int NVR = (CP * TPRV + PF_THREADS - 1) / PF_THREADS;
+    float vreg[NVR][8];
+    {
+        const T* vg = reinterpret_cast<const T*>(a.v);
+#pragma unroll
+        for (int r = 0; r < NVR; r++) {
+            const int idx = tid + r * PF_THREADS;
+            const int i = idx / TPRV, c0 = (idx % TPRV) * 8;
+            if (idx < CP * TPRV && i < loc.len) {
+                const size_t off = ((size_t)(loc.tok0 + i) * H + h) * DV + c0;
+                load4<T>(vg + off, vreg[r]);
+                load4<T>(vg + off + 4, vreg[r] + 4);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; j++) vreg[r][j] = 0.f;
+            }
+        }
+    }
+    // ---------------- step 0: load K, Q (optionally L2-normalised), beta, G
+    // Every global load of this step is issued before the first one is consumed.
+    {
+        constexpr int TPR = DK / 8;  // threads per key row, 8 elements each
+        constexpr int NKR = (C * TPR + PF_THREADS - 1) / PF_THREADS;
+        const T* kg = reinterpret_cast<const T*>(a.k);
+        const T* qg = reinterpret_cast<const T*>(a.q);
+        float kv[NKR][8], qv[NKR][8];
+#pragma unroll
+        for (int r = 0; r < NKR; r++) {
+            const int idx = tid + r * PF_THREADS;
+            const int i = idx / TPR, c0 = (idx % TPR) * 8;
+            if (idx < C * TPR && i < loc.len) {
+                const size_t off = ((size_t)(loc.tok0 + i) * H + h) * DK + c0;
+                load8<T>(kg + off, kv[r]);
+                load8<T>(qg + off, qv[r]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; j++) kv[r][j] = qv[r][j] = 0.f;
+            }
+        }
+        // per-key gate: thread (channel, row segment) loads its GR rows of g
+        constexpr int GP = PERKEY ? PF_THREADS / DK : 1;  // row segments per channel
+        constexpr int GR = PERKEY ? C / GP : 1;           // rows per segment
+        float gv[GR];
+        const int gch = tid % DK, gseg = tid / DK;
+        if constexpr (PERKEY) {
+#pragma unroll
+            for (int r = 0; r < GR; r++) {
+                const int i = gseg * GR + r;
+                gv[r] = i < loc.len ? a.g[((size_t)(loc.tok0 + i) * H + h) * DK + gch] : 0.f;
+            }
+        }
+        float gs_scalar = 0.f, bval = 0.f;
+        if (!PERKEY && w == 0)
+            gs_scalar = (lane < loc.len && lane < C) ? a.g[(size_t)(loc.tok0 + lane) * H + h] : 0.f;
+        if (tid < C && tid < loc.len) bval = a.beta[(size_t)(loc.tok0 + tid) * H + h];
+        // consume
+#pragma unroll
+        for (int r = 0; r < NKR; r++) {
+            const int idx = tid + r * PF_THREADS;
+            const int i = idx / TPR, c0 = (idx % TPR) * 8;
+            if (a.l2norm) {
+                float sk = 0.f, sq = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    sk += kv[r][j] * kv[r][j];
+                    sq += qv[r][j] * qv[r][j];
+                }
+                sk = group_sum<TPR>(sk);
+                sq = group_sum<TPR>(sq);
+                const float ik = rsqrtf(sk + 1e-6f), iq = rsqrtf(sq + 1e-6f);
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    kv[r][j] *= ik;
+                    qv[r][j] *= iq;
+                }
+            }
+            if (idx < C * TPR) {
+                store8<T>(&sm.u.a.ks[i][c0], kv[r]);
+                store8<T>(&sm.u.a.qs[i][c0], qv[r]);
+            }
+        }
+        if constexpr (DKP > DK) {  // zero the padded contraction columns
+            for (int idx = tid; idx < C * (DKP - DK); idx += PF_THREADS) {
+                const int i = idx / (DKP - DK), c0 = DK + idx % (DKP - DK);
+                sm.u.a.ks[i][c0] = from_f32<T>(0.f);
+                sm.u.a.qs[i][c0] = from_f32<T>(0.f);
+            }
+        }
+        if (tid < C) sm.bs[tid] = bval;
+        if constexpr (PERKEY) {
+            // in-register running sum of the segment, segment totals through LDS, then the
+            // prefix of the preceding segments is added
+            float run = 0.f;
+#pragma unroll
+            for (int r = 0; r < GR; r++) {
+                run += gv[r];
+                gv[r] = run;
+            }
+            sm.u.a.gseg[gseg][gch] = run;
+            lds_barrier();
+            float base = 0.f;
+            for (int p2 = 0; p2 < gseg; p2++) base += sm.u.a.gseg[p2][gch];
+#pragma unroll
+            for (int r = 0; r < GR; r++) sm.u.a.gs[gseg * GR + r][gch] = gv[r] + base;
+        } else {
+            if (w == 0) {
+                float x = gs_scalar;
+#pragma unroll
+                for (int off = 1; off < WAVE; off <<= 1) {
+                    float y = __shfl_up(x, off, WAVE);
+                    if (lane >= off) x += y;
+                }
+                if (lane < C) sm.u.a.gs[0][lane] = x;
+            }
+        }
+    }
+    lds_barrier();
+    // ---------------- step 1-2: gated key copies, Q_in, whole-chunk decay
+    {
+        // Q_in = s Q e^{G} -> workspace, fragment-major [C][DKP]
+        constexpr int TPR = DK / 8;
+        T* qin = reinterpret_cast<T*>(a.ws.qin) + u * C * DKP;
+        for (int idx = tid; idx < C * TPR; idx += PF_THREADS) {
+            const int i = idx / TPR, c0 = (idx % TPR) * 8;
+            float out[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                out[j] = a.scale * to_f32(sm.u.a.qs[i][c0 + j]) *
+                         __expf(gval<PERKEY, DK, C>(sm.u.a.gs, i, c0 + j));
+            Frag<T>::template store_run<8>(qin, i, c0, DKP, out);
+        }
+        if constexpr (DKP > DK) {
+            for (int idx = tid; idx < C * ((DKP - DK) / 4); idx += PF_THREADS) {
+                const int i = idx / ((DKP - DK) / 4), c0 = DK + (idx % ((DKP - DK) / 4)) * 4;
+                float z[4] = {0.f, 0.f, 0.f, 0.f};
+                Frag<T>::template store_run<4>(qin, i, c0, DKP, z);
+            }
+        }
+        // K_in^T * beta (LDS) and K_g^T (workspace, fragment-major [DK][CP]), 8 tokens each
+        constexpr int TG = CP / 8;
+        T* kgt = reinterpret_cast<T*>(a.ws.kgt) + u * DK * CP;
+        for (int idx = tid; idx < DK * TG; idx += PF_THREADS) {
+            const int ch = idx / TG, i0 = (idx % TG) * 8;
+            const float gC = gval<PERKEY, DK, C>(sm.u.a.gs, C - 1, ch);
+            float kin[8], kgv[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const int i = i0 + j;
+                if (i < C) {
+                    const float kk = to_f32(sm.u.a.ks[i][ch]);
+                    const float gi = gval<PERKEY, DK, C>(sm.u.a.gs, i, ch);
+                    kin[j] = sm.bs[i] * kk * __expf(gi);
+                    kgv[j] = kk * __expf(gC - gi);
+                } else {
+                    kin[j] = 0.f;
+                    kgv[j] = 0.f;
+                }
+            }
+            store8<T>(&sm.kint[ch][i0], kin);
+            Frag<T>::template store_run<8>(kgt, ch, i0, CP, kgv);
+        }
+        if (tid < DK) a.ws.decay[u * DK + tid] = __expf(gval<PERKEY, DK, C>(sm.u.a.gs, C - 1, tid));
+    }
+    // ---------------- step 3a: A and M (transposed tiles: row = j, column = i), one pass
+    {
+        constexpr int NT = NB * (NB + 1) / 2;
+        T* mmat = reinterpret_cast<T*>(a.ws.mmat) + u * C * CP;
+        const int r16 = lane & 15, kq = (lane >> 4) * KPL;
+        for (int t = w; t < NT; t += PF_WAVES) {
+            // t -> (jb <= ib)
+            int ib = 0, rem = t;
+            while (rem > ib) {
+                rem -= ib + 1;
+                ib++;
+            }
+            const int jb = rem;
+            const int ref = ib * 16;  // reference token: first of the i block
+            f32x4 accK = zero4(), accQ = zero4();
+            const int jrow = jb * 16 + r16, irow = ib * 16 + r16;
+#pragma unroll
+            for (int kb = 0; kb < DKP / KB; kb++) {
+                const int c0 = kb * KB + kq;
+                typename MM::frag fa, fbk, fbq;
+                if constexpr (PERKEY) {
+#pragma unroll
+                    for (int e = 0; e < KPL; e++) {
+                        const int ch = c0 + e;
+                        float aj = 0.f, bk = 0.f, bq = 0.f;
+                        if (ch < DK) {  // padded channels contribute zero
+                            const float gr = sm.u.a.gs[ref][ch];
+                            const float fj = __expf(gr - sm.u.a.gs[jrow][ch]);
+                            const float fi = __expf(sm.u.a.gs[irow][ch] - gr);
+                            aj = to_f32(sm.u.a.ks[jrow][ch]) * fj;
+                            bk = to_f32(sm.u.a.ks[irow][ch]) * fi;
+                            bq = to_f32(sm.u.a.qs[irow][ch]) * fi;
+                        }
+                        if constexpr (KPL == 1) {
+                            fa = from_f32<T>(aj);
+                            fbk = from_f32<T>(bk);
+                            fbq = from_f32<T>(bq);
+                        } else {
+                            fa[e] = from_f32<T>(aj);
+                            fbk[e] = from_f32<T>(bk);
+                            fbq[e] = from_f32<T>(bq);
+                        }
+                    }
+                } else {
+                    fa = MM::load(&sm.u.a.ks[jrow][c0]);
+                    fbk = MM::load(&sm.u.a.ks[irow][c0]);
+                    fbq = MM::load(&sm.u.a.qs[irow][c0]);
+                }
+                accK = MM::mma(fa, fbk, accK);
+                accQ = MM::mma(fa, fbq, accQ);
+            }
+            // lane holds D[j = jb*16 + 4*(lane>>4) + e][i = ib*16 + (lane & 15)]
+            const int i = ib * 16 + r16;
+            const float gi = PERKEY ? 0.f : sm.u.a.gs[0][i];
+            float mrow[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int j = jb * 16 + (lane >> 4) * 4 + e;
+                float dec = 1.f;
+                if constexpr (!PERKEY) dec = (j <= i) ? __expf(gi - sm.u.a.gs[0][j]) : 0.f;
+                if (j < i) sm.af[i][j] = sm.bs[i] * accK[e] * dec;
+                mrow[e] = (j <= i) ? a.scale * accQ[e] * dec : 0.f;
+            }
+            // M fragment-major [C][CP]: 4 consecutive j of row i
+            Frag<T>::template store_run<4>(mmat, i, jb * 16 + (lane >> 4) * 4, CP, mrow);
+        }
+        // zero the upper tiles and the padding columns of M
+        for (int idx = tid; idx < C * (CP / 4); idx += PF_THREADS) {
+            const int i = idx / (CP / 4), j0 = (idx % (CP / 4)) * 4;
+            if (j0 / 16 > i / 16 || j0 >= C) {
+                float z[4] = {0.f, 0.f, 0.f, 0.f};
+                Frag<T>::template store_run<4>(mmat, i, j0, CP, z);
+            }
+        }
+    }
+    lds_barrier();  // phase A storage (keys, queries, gates) is dead from here on
+    // (diag(beta) V)^T into phase-B storage, zero-padded to CP tokens
+#pragma unroll
+    for (int r = 0; r < NVR; r++) {
+        const int idx = tid + r * PF_THREADS;
+        if (idx < CP * TPRV) {
+            const int i = idx / TPRV, c0 = (idx % TPRV) * 8;
+            const float b = i < C ? sm.bs[i] : 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; j++) sm.u.b.vt[c0 + j][i] = from_f32<T>(b * vreg[r][j]);
+        }
+    }
+    // ---------------- step 3b: R = (I + A)^{-1}, blocked (16x16 leaves, 2x2 merges)
+    if (w == 0) {
+        const int blk = lane >> 4, col = lane & 15;
+        if (blk < NB) {
+            const int b0 = blk * 16;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; r++) x[r] = (r == col) ? 1.f : 0.f;
+#pragma unroll
+            for (int r = 1; r < 16; r++) {
+                float acc = 0.f;
+#pragma unroll
+                for (int kk = 0; kk < r; kk++) acc += sm.af[b0 + r][b0 + kk] * x[kk];
+                x[r] -= acc;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; r++) sm.u.b.rf[b0 + r][b0 + col] = x[r];
+        }
+    }
+    lds_barrier();
+    if constexpr (NB >= 2) {
+        // level 1: blocks (2p, 2p+1): R21 = -X_{2p+1} A_{2p+1,2p} X_{2p}
+        constexpr int NP = NB / 2;
+        for (int idx = tid; idx < NP * 256; idx += PF_THREADS) {
+            const int p = idx / 256, r = (idx % 256) / 16, cc = idx % 16;
+            const int lo = 2 * p * 16, hi = lo + 16;
+            float acc = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < 16; kk++) acc += sm.af[hi + r][lo + kk] * sm.u.b.rf[lo + kk][lo + cc];
+            sm.af[lo + r][hi + cc] = acc;  // T1 kept in the (unused) upper part of A
+        }
+        lds_barrier();
+        for (int idx = tid; idx < NP * 256; idx += PF_THREADS) {
+            const int p = idx / 256, r = (idx % 256) / 16, cc = idx % 16;
+            const int lo = 2 * p * 16, hi = lo + 16;
+            float acc = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < 16; kk++) acc += sm.u.b.rf[hi + r][hi + kk] * sm.af[lo + kk][hi + cc];
+            sm.u.b.rf[hi + r][lo + cc] = -acc;
+            sm.u.b.rf[lo + r][hi + cc] = 0.f;
+        }
+        lds_barrier();
+    }
+    if constexpr (NB >= 4) {
+        // level 2: R[32:64, 0:32] = -R_B A[32:64, 0:32] R_A
+        for (int idx = tid; idx < 1024; idx += PF_THREADS) {
+            const int r = idx / 32, cc = idx % 32;
+            float acc = 0.f;
+#pragma unroll 8
+            for (int kk = 0; kk < 32; kk++) acc += sm.af[32 + r][kk] * sm.u.b.rf[kk][cc];
+            sm.af[r][32 + cc] = acc;  // T2 in the upper-right quarter of A
+        }
+        lds_barrier();
+        for (int idx = tid; idx < 1024; idx += PF_THREADS) {
+            const int r = idx / 32, cc = idx % 32;
+            float acc = 0.f;
+#pragma unroll 8
+            for (int kk = 0; kk < 32; kk++) acc += sm.u.b.rf[32 + r][32 + kk] * sm.af[kk][32 + cc];
+            sm.u.b.rf[32 + r][cc] = -acc;
+        }
+        lds_barrier();
+    }
+    // R -> MFMA operand (lower triangle only, zero elsewhere and in the padding)
+    for (int idx = tid; idx < C * CP; idx += PF_THREADS) {
+        const int i = idx / CP, j = idx % CP;
+        sm.u.b.rs[i][j] = from_f32<T>((j <= i && j < C) ? sm.u.b.rf[i][j] : 0.f);
+    }
+    lds_barrier();
+    // ---------------- step 4: W^T = K_in^T R^T (stored as -W, row-major) and U = R (beta V)
+    {
+        const int r16 = lane & 15, kq = (lane >> 4) * KPL;
+        T* wneg = reinterpret_cast<T*>(a.ws.wneg) + u * C * DKP;
+        if constexpr (DKP > DK) {
+            for (int idx = tid; idx < C * ((DKP - DK) / 4); idx += PF_THREADS) {
+                const int i = idx / ((DKP - DK) / 4), c0 = DK + (idx % ((DKP - DK) / 4)) * 4;
+                float z[4] = {0.f, 0.f, 0.f, 0.f};
+                Frag<T>::template store_run<4>(wneg, i, c0, DKP, z);
+            }
+        }
+        float* ut = a.ws.ut + u * DV * C;
+        constexpr int NW = (DK / 16) * NB;  // W^T tiles: (channel block, token block)
+        constexpr int NU = NB * (DV / 16);  // U tiles: (token block, value block)
+        for (int t = w; t < NW + NU; t += PF_WAVES) {
+            f32x4 acc = zero4();
+            if (t < NW) {
+                const int mb = t / NB, nb = t % NB;  // mb: channel block, nb: token block
+#pragma unroll
+                for (int kb = 0; kb < CP / KB; kb++) {
+                    auto fa = MM::load(&sm.kint[mb * 16 + r16][kb * KB + kq]);
+                    auto fb = MM::load(&sm.u.b.rs[nb * 16 + r16][kb * KB + kq]);
+                    acc = MM::mma(fa, fb, acc);
+                }
+                // lane: W^T[ch = mb*16 + 4*(lane>>4) + e][i = nb*16 + r16]
+                float nw[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) nw[e] = -acc[e];
+                Frag<T>::template store_run<4>(wneg, nb * 16 + r16, mb * 16 + (lane >> 4) * 4, DKP, nw);
+            } else {
+                const int tt = t - NW;
+                const int mb = tt / (DV / 16), nb = tt % (DV / 16);  // token block, value block
+#pragma unroll
+                for (int kb = 0; kb < CP / KB; kb++) {
+                    auto fa = MM::load(&sm.u.b.rs[mb * 16 + r16][kb * KB + kq]);
+                    auto fb = MM::load(&sm.u.b.vt[nb * 16 + r16][kb * KB + kq]);
+                    acc = MM::mma(fa, fb, acc);
+                }
+                // lane: U[i = mb*16 + 4*(lane>>4) + e][v = nb*16 + r16], stored in the scan's
+                // accumulator order: slot (value block nb, token block mb, lane)
+                float uu[4] = {acc[0], acc[1], acc[2], acc[3]};
+                store4<float>(ut + ((size_t)(nb * NB + mb) * 64 + lane) * 4, uu);
+            }
+        }
+    }
+}
+
+// =====================================================================================
+// scan kernel: the sequential state pass over chunks
+// =====================================================================================
+template <typename T, int DK, int DV, int C, bool PERKEY>
+struct ScanOps {
+    using F = PfCfg<T, DK, DV, C>;
+    using frag = typename F::MM::frag;
+    static constexpr int NK = F::DKP / F::KB;    // k-steps over (padded) d_k
+    static constexpr int NK2 = F::CP / F::KB;    // k-steps over the chunk
+    static constexpr int MBW = (F::NB + PF_WAVES - 1) / PF_WAVES;         // token blocks / wave
+    static constexpr int RBW = (DK / 16 + PF_WAVES - 1) / PF_WAVES;       // state row blocks / wave
+    // every wave owns a full set of blocks: no runtime guard (keeps the loop branch-free,
+    // which lets the compiler wait only for the operands it needs, not for the prefetch)
+    static constexpr bool MB_FULL = F::NB % PF_WAVES == 0;
+    static constexpr bool RB_FULL = (DK / 16) % PF_WAVES == 0;
+    frag aw[MBW][NK];   // -W rows
+    frag aq[MBW][NK];   // Q_in rows
+    frag am[MBW][NK2];  // M rows
+    frag ak[RBW][NK2];  // K_g^T rows
+    f32x4 u[MBW];       // U^T slice in accumulator layout
+    f32x4 dec[PERKEY ? RBW : 1];  // per key: e^{G_C} for the lane's 4 state rows
+    float dec0;                   // scalar gate: e^{G_C}
+};
+
+template <typename T, int DK, int DV, int C, bool PERKEY>
+__device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY>& op,
+                                              const PrefillArgs& a, size_t u, int vcol0) {
+    using O = ScanOps<T, DK, DV, C, PERKEY>;
+    using F = PfCfg<T, DK, DV, C>;
+    using MM = typename F::MM;
+    constexpr int CP = F::CP;
+    const int lane = lane_id(), w = wave_id();
+    const T* wneg = reinterpret_cast<const T*>(a.ws.wneg) + u * C * F::DKP;
+    const T* qin = reinterpret_cast<const T*>(a.ws.qin) + u * C * F::DKP;
+    const T* mm = reinterpret_cast<const T*>(a.ws.mmat) + u * C * CP;
+    const T* kgt = reinterpret_cast<const T*>(a.ws.kgt) + u * DK * CP;
+    const float* ut = a.ws.ut + u * DV * C;
+    const float* dec = a.ws.decay + u * DK;
+    if constexpr (!PERKEY) op.dec0 = dec[0];  // one value per chunk (uniform address)
+#pragma unroll
+    for (int r = 0; r < O::MBW; r++) {
+        const int mb = w + r * PF_WAVES;
+        if (O::MB_FULL || mb < F::NB) {
+#pragma unroll
+            for (int kb = 0; kb < O::NK; kb++) {
+                op.aw[r][kb] = MM::load(Frag<T>::ptr(wneg, mb, kb, F::DKP, lane));
+                op.aq[r][kb] = MM::load(Frag<T>::ptr(qin, mb, kb, F::DKP, lane));
+            }
+#pragma unroll
+            for (int kb = 0; kb < O::NK2; kb++)
+                op.am[r][kb] = MM::load(Frag<T>::ptr(mm, mb, kb, CP, lane));
+            op.u[r] = *reinterpret_cast<const f32x4*>(
+                ut + ((size_t)((vcol0 / 16) * F::NB + mb) * 64 + lane) * 4);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < O::RBW; r++) {
+        const int rb = w + r * PF_WAVES;
+        if (O::RB_FULL || rb < DK / 16) {
+#pragma unroll
+            for (int kb = 0; kb < O::NK2; kb++)
+                op.ak[r][kb] = MM::load(Frag<T>::ptr(kgt, rb, kb, CP, lane));
+            if constexpr (PERKEY)  // 4 distinct 16-byte words per wave: one cache line
+                op.dec[r] = *reinterpret_cast<const f32x4*>(dec + rb * 16 + (lane >> 4) * 4);
+        }
+    }
+}
+
+#ifndef GDN_SCAN_PFD
+#define GDN_SCAN_PFD 1
+#endif
+
+template <typename T, int DK, int DV, int C, bool PERKEY, int PFD = GDN_SCAN_PFD>
+__global__ __launch_bounds__(PF_THREADS) void prefill_scan_kernel(PrefillArgs a) {
+    using F = PfCfg<T, DK, DV, C>;
+    using MM = typename F::MM;
+    using O = ScanOps<T, DK, DV, C, PERKEY>;
+    constexpr int KB = F::KB, KPL = F::KPL, CP = F::CP;
+    constexpr int NVT = DV / SCAN_BV;
+    __shared__ __align__(16) T st[SCAN_BV][F::LDK];   // S^T slice (MFMA B operand)
+    __shared__ __align__(16) T et[SCAN_BV][F::LDC];   // E^T slice
+
+    // XCD-aware unit mapping: all value tiles of a (sequence, head) on one XCD
+    const int id = blockIdx.x;
+    const int xcd = id & 7, jj = id >> 3;
+    const int unit = (jj / NVT) * 8 + xcd;
+    const int vt = jj % NVT;
+    const int H = a.H;
+    if (unit >= a.n_seqs * H) return;
+    const int n = unit / H, h = unit - (unit / H) * H;
+    const int lane = lane_id(), w = wave_id(), r16 = lane & 15, kq = (lane >> 4) * KPL;
+    const int vcol0 = vt * SCAN_BV;
+    // clamps keep inconsistent cu_seqlens inside the workspace and the token range
+    const int c_begin = a.ws.seq_first[n];
+    const int c_end = (int)min((int64_t)a.ws.seq_first[n + 1], a.ws.max_chunks);
+    const int t_begin = a.cu_seqlens[n], t_end = min(a.cu_seqlens[n + 1], a.total_tokens);
+    const int slot = a.slots[n];
+    const bool valid = slot >= 0 && slot < a.n_slots;
+    const bool init = valid && a.has_init != nullptr && a.has_init[n] != 0;
+    float* S = valid ? a.state_pool + ((size_t)slot * H + h) * DK * DV : nullptr;
+
+    // state slice in accumulators: acc_s[r][e] = S[rb*16 + 4*(lane>>4) + e][vcol0 + r16]
+    f32x4 acc_s[O::RBW];
+#pragma unroll
+    for (int r = 0; r < O::RBW; r++) {
+        acc_s[r] = zero4();
+        const int rb = w + r * PF_WAVES;
+        if (rb < DK / 16) {
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int row = rb * 16 + (lane >> 4) * 4 + e;
+                acc_s[r][e] = init ? S[(size_t)row * DV + vcol0 + r16] : 0.f;
+                st[r16][row] = from_f32<T>(acc_s[r][e]);
+            }
+        }
+    }
+    if constexpr (CP > C) {
+        for (int idx = threadIdx.x; idx < SCAN_BV * (CP - C); idx += PF_THREADS)
+            et[idx / (CP - C)][C + idx % (CP - C)] = from_f32<T>(0.f);
+    }
+    if constexpr (F::DKP > DK) {  // padded state rows stay zero
+        for (int idx = threadIdx.x; idx < SCAN_BV * (F::DKP - DK); idx += PF_THREADS)
+            st[idx / (F::DKP - DK)][DK + idx % (F::DKP - DK)] = from_f32<T>(0.f);
+    }
+
+    T* out = reinterpret_cast<T*>(a.o);
+    T* dump = reinterpret_cast<T*>(a.ws.dump) + threadIdx.x;
+    // one chunk of the sequential pass, operands already in registers
+    auto chunk_step = [&](const O& cur, int c) {
+        const int tok0 = t_begin + (c - c_begin) * C;
+        const int len = min(C, t_end - tok0);
+        lds_barrier();  // st holds S_0 of this chunk
+        f32x4 acc_o[O::MBW];
+#pragma unroll
+        for (int r = 0; r < O::MBW; r++) {
+            const int mb = w + r * PF_WAVES;
+            acc_o[r] = zero4();
+            if (O::MB_FULL || mb < F::NB) {
+                f32x4 acc_e = cur.u[r];
+#pragma unroll
+                for (int kb = 0; kb < O::NK; kb++) {
+                    auto fb = MM::load(&st[r16][kb * KB + kq]);
+                    acc_e = MM::mma(cur.aw[r][kb], fb, acc_e);        // U - W S
+                    acc_o[r] = MM::mma(cur.aq[r][kb], fb, acc_o[r]);  // Q_in S
+                }
+#pragma unroll
+                for (int e = 0; e < 4; e++) et[r16][mb * 16 + (lane >> 4) * 4 + e] = from_f32<T>(acc_e[e]);
+            }
+        }
+        lds_barrier();  // et holds E
+#pragma unroll
+        for (int r = 0; r < O::MBW; r++) {
+            const int mb = w + r * PF_WAVES;
+            if (O::MB_FULL || mb < F::NB) {
+#pragma unroll
+                for (int kb = 0; kb < O::NK2; kb++) {
+                    auto fb = MM::load(&et[r16][kb * KB + kq]);
+                    acc_o[r] = MM::mma(cur.am[r][kb], fb, acc_o[r]);  // + M E
+                }
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    // tokens past the sequence end go to a scratch word instead of a branch
+                    const int i = mb * 16 + (lane >> 4) * 4 + e;
+                    T* dst = i < len ? out + ((size_t)(tok0 + i) * H + h) * DV + vcol0 + r16 : dump;
+                    *dst = from_f32<T>(acc_o[r][e]);
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < O::RBW; r++) {
+            const int rb = w + r * PF_WAVES;
+            if (O::RB_FULL || rb < DK / 16) {
+#pragma unroll
+                for (int e = 0; e < 4; e++) acc_s[r][e] *= PERKEY ? cur.dec[PERKEY ? r : 0][e] : cur.dec0;
+#pragma unroll
+                for (int kb = 0; kb < O::NK2; kb++) {
+                    auto fb = MM::load(&et[r16][kb * KB + kq]);
+                    acc_s[r] = MM::mma(cur.ak[r][kb], fb, acc_s[r]);  // + K_g^T E
+                }
+#pragma unroll
+                for (int e = 0; e < 4; e++) st[r16][rb * 16 + (lane >> 4) * 4 + e] = from_f32<T>(acc_s[r][e]);
+            }
+        }
+    };
+    // Operand prefetch over the chunk sequence. PFD = prefetch distance in chunks: 0 loads a
+    // chunk's operands right before it is computed (fewest registers, latency hidden by other
+    // resident workgroups), 1 and 2 keep 2 or 3 rotating operand sets so the loads for chunk
+    // c+PFD are in flight while chunk c is computed. Prefetch indices are clamped to the last
+    // chunk so every load is unconditional.
+    if (c_begin < c_end) {
+        const int clast = c_end - 1;
+        auto ld = [&](O& op, int c) {
+            scan_load_ops<T, DK, DV, C, PERKEY>(op, a, (size_t)min(c, clast) * H + h, vcol0);
+        };
+        if constexpr (PFD == 0) {
+            O op0;
+            for (int c = c_begin; c < c_end; c++) {
+                ld(op0, c);
+                chunk_step(op0, c);
+            }
+        } else if constexpr (PFD == 1) {
+            O op0, op1;
+            ld(op0, c_begin);
+            for (int c = c_begin; c < c_end; c += 2) {
+                ld(op1, c + 1);
+                chunk_step(op0, c);
+                if (c + 1 >= c_end) break;
+                ld(op0, c + 2);
+                chunk_step(op1, c + 1);
+            }
+        } else {
+            O op0, op1, op2;
+            ld(op0, c_begin);
+            ld(op1, c_begin + 1);
+            for (int c = c_begin; c < c_end; c += 3) {
+                ld(op2, c + 2);
+                chunk_step(op0, c);
+                if (c + 1 >= c_end) break;
+                ld(op0, c + 3);
+                chunk_step(op1, c + 1);
+                if (c + 2 >= c_end) break;
+                ld(op1, c + 4);
+                chunk_step(op2, c + 2);
+            }
+        }
+    }
+    if (valid) {
+#pragma unroll
+        for (int r = 0; r < O::RBW; r++) {
+            const int rb = w + r * PF_WAVES;
+            if (rb < DK / 16) {
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    S[(size_t)(rb * 16 + (lane >> 4) * 4 + e) * DV + vcol0 + r16] = acc_s[r][e];
+            }
+        }
+    }
+}
+
+// =====================================================================================
+// dispatch for one element type
+// =====================================================================================
+__global__ void seq_first_kernel(const int32_t* cu, int n_seqs, int C, int32_t* seq_first);
+
+template <typename T, int D, int C, bool PERKEY>
+hipError_t prefill_launch_cfg(const PrefillArgs& a, hipStream_t s) {
+    const size_t smem = sizeof(PrepSmem<T, D, D, C, PERKEY>);
+    static_assert(sizeof(PrepSmem<T, D, D, C, PERKEY>) <= 160 * 1024, "prep LDS over 160 KiB");
+    auto prep = prefill_prep_kernel<T, D, D, C, PERKEY>;
+    // dynamic LDS above 64 KiB must be allowed explicitly (idempotent, no library state);
+    // done before the first launch so a refusal launches nothing
+    hipError_t e = hipFuncSetAttribute((const void*)prep,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return e;
+    }
+    hipLaunchKernelGGL(seq_first_kernel, dim3(1), dim3(256), 0, s, a.cu_seqlens, a.n_seqs,
+                       C, a.ws.seq_first);
+    const int64_t nchunk = a.ws.max_chunks;
+    if (nchunk > 0)
+        hipLaunchKernelGGL(prep, dim3((unsigned)(nchunk * a.H)), dim3(PF_THREADS), smem, s, a);
+    const int units = a.n_seqs * a.H;
+    const int nvt = D / SCAN_BV;
+    const int grid = ((units + 7) / 8) * 8 * nvt;
+    hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY>), dim3((unsigned)grid),
+                       dim3(PF_THREADS), 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename T, int D, int C>
+hipError_t prefill_launch_gate(const PrefillArgs& a, hipStream_t s) {
+    return a.gate == 1 ? prefill_launch_cfg<T, D, C, true>(a, s)
+                       : prefill_launch_cfg<T, D, C, false>(a, s);
+}
+
+template <typename T, int D>
+hipError_t prefill_launch_chunk(const PrefillArgs& a, hipStream_t s) {
+    switch (a.chunk) {
+        case 16: return prefill_launch_gate<T, D, 16>(a, s);
+        case 32: return prefill_launch_gate<T, D, 32>(a, s);
+        case 64: return prefill_launch_gate<T, D, 64>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t prefill_launch_typed(const PrefillArgs& a, hipStream_t s) {
+    switch (a.dk) {
+        case 16: return prefill_launch_chunk<T, 16>(a, s);
+        case 32: return prefill_launch_chunk<T, 32>(a, s);
+        case 64: return prefill_launch_chunk<T, 64>(a, s);
+        case 128: return prefill_launch_chunk<T, 128>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

@@ -1,0 +1,167 @@
+"""The C-ABI library loads on a host without a GPU, exports every symbol the header
+declares, and rejects bad arguments on the host before any HIP call (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_prefill_amd import gdn
+from gated_delta_rule_prefill_amd.gdn import gdn_dims_t, gdn_deltalog_pool_t
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    names = _declared()
+    for n in ("gdn_prefill_chunked", "gdn_prefill_workspace_bytes", "gdn_decode_step",
+              "gdn_decode_deltalog", "gdn_deltalog_workspace_bytes", "gdn_deltalog_reset",
+              "gdn_deltalog_materialize", "gdn_conv1d_silu", "gdn_status_string",
+              "gdn_last_error", "gdn_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = gdn.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert gdn.gdn_abi_version() == 1
+
+
+def test_binding_uses_the_c_names():
+    for name in _declared():
+        assert hasattr(gdn, name), name
+
+
+def test_status_strings():
+    assert gdn.gdn_status_string(0) == "ok"
+    assert gdn.gdn_status_string(5) == "workspace too small"
+    assert gdn.gdn_status_string(99) == "unknown status"
+
+
+def _dims(H=4, dk=128, dv=128, dtype=1, gate=0, l2=0):
+    return gdn_dims_t(H, dk, dv, dtype, gate, 0.1, l2)
+
+
+FAKE = 0x7f0000000000  # aligned, never dereferenced (validation fails before any launch)
+
+
+def _prefill(dims, ws_bytes=1 << 40, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, cu=FAKE, n=2, T=100, chunk=64,
+             pool=FAKE, n_slots=4, slots=FAKE, has_init=None, o=FAKE, ws=FAKE)
+    a.update(kw)
+    lib = gdn.load()
+    return lib.gdn_prefill_chunked(
+        ctypes.byref(dims), a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["n"], a["T"],
+        a["chunk"], a["pool"], a["n_slots"], a["slots"], a["has_init"], a["o"], a["ws"],
+        ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(cu=None), 1), (dict(ws=None), 1), (dict(slots=None), 1),
+    (dict(q=FAKE + 8), 4), (dict(o=FAKE + 2), 4), (dict(has_init=FAKE + 4), 4),
+    (dict(chunk=48), 3), (dict(chunk=128), 3), (dict(n=-1), 2), (dict(T=-5), 2),
+    (dict(n_slots=0), 2),
+])
+def test_prefill_rejects_bad_arguments(kw, status):
+    assert _prefill(_dims(), **kw) == status
+    assert gdn.gdn_last_error() != ""
+
+
+@pytest.mark.parametrize("dims,status", [
+    (_dims(dk=96, dv=96), 3), (_dims(dk=64, dv=128), 3), (_dims(dtype=2), 3),
+    (_dims(gate=2), 3), (_dims(H=0), 2), (_dims(l2=3), 3),
+])
+def test_prefill_rejects_bad_dims(dims, status):
+    assert _prefill(dims) == status
+
+
+def test_prefill_workspace_too_small_and_sizing():
+    lib = gdn.load()
+    dims = _dims(H=16, dk=128, dv=128)
+    need = ctypes.c_size_t(0)
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(dims), 1, 8192, 64, ctypes.byref(need)) == 0
+    # 128 chunks x 16 heads x (W, Q_in, K_g^T, M in bf16 + U^T, decay in fp32) + table
+    per = 64 * 128 * 2 * 3 + 64 * 64 * 2 + 128 * 64 * 4 + 128 * 4
+    assert need.value >= 128 * 16 * per
+    assert need.value < 128 * 16 * per + 64 * 1024
+    assert _prefill(dims, ws_bytes=need.value - 1, n=1, T=8192) == 5
+    # more sequences -> a larger chunk bound
+    more = ctypes.c_size_t(0)
+    lib.gdn_prefill_workspace_bytes(ctypes.byref(dims), 8, 8192, 64, ctypes.byref(more))
+    assert more.value > need.value
+
+
+def test_zero_sized_calls_are_noops_without_gpu():
+    lib = gdn.load()
+    d = _dims()
+    assert _prefill(d, n=0, q=None, ws=None) == 0
+    assert lib.gdn_decode_step(ctypes.byref(d), None, None, None, None, None, None, 1, None, 0,
+                               None, None) == 0
+    assert lib.gdn_conv1d_silu(None, None, None, 0, 0, 8, 4, 1, 1, None, None) == 0
+
+
+def test_decode_rejects_bad_arguments():
+    lib = gdn.load()
+    d = _dims()
+    args = [FAKE] * 6
+    assert lib.gdn_decode_step(ctypes.byref(d), *args, 4, FAKE, -1, FAKE, None) == 2
+    assert lib.gdn_decode_step(ctypes.byref(d), None, *args[1:], 4, FAKE, 8, FAKE, None) == 1
+    assert lib.gdn_decode_step(ctypes.byref(d), *args, 0, FAKE, 8, FAKE, None) == 2
+    assert lib.gdn_decode_step(None, *args, 4, FAKE, 8, FAKE, None) == 1
+
+
+def test_deltalog_rejects_bad_arguments():
+    lib = gdn.load()
+    d = _dims()
+    pool = gdn_deltalog_pool_t(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8)
+    bad_m = gdn_deltalog_pool_t(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1)
+    big_m = gdn_deltalog_pool_t(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 18)
+    null_base = gdn_deltalog_pool_t(None, FAKE, FAKE, FAKE, FAKE, FAKE, 8)
+    args = [FAKE] * 5
+
+    def call(dims, p, batch=8):
+        return lib.gdn_decode_deltalog(ctypes.byref(dims), *args, ctypes.byref(p), 4, FAKE,
+                                       batch, FAKE, None, 0, None)
+    assert call(d, bad_m) == 3
+    assert call(d, big_m) == 3
+    assert call(d, null_base) == 1
+    assert call(_dims(gate=1), pool) == 3
+    ws = ctypes.c_size_t(123)
+    assert lib.gdn_deltalog_workspace_bytes(ctypes.byref(d), 512, 8, ctypes.byref(ws)) == 0
+    assert ws.value == 0
+    assert lib.gdn_deltalog_reset(ctypes.byref(d), ctypes.byref(bad_m), 4, FAKE, 2, None) == 3
+
+
+def test_conv_rejects_bad_arguments():
+    lib = gdn.load()
+    assert lib.gdn_conv1d_silu(FAKE, FAKE, FAKE, 1, 10, 12, 4, 1, 1, FAKE, None) == 2   # 12 % 8
+    assert lib.gdn_conv1d_silu(FAKE, FAKE, FAKE, 1, 10, 40, 4, 3, 1, FAKE, None) == 2   # 40 % 24
+    assert lib.gdn_conv1d_silu(FAKE, FAKE, FAKE, 1, 10, 48, 5, 1, 1, FAKE, None) == 3
+    assert lib.gdn_conv1d_silu(FAKE, FAKE, FAKE, 1, 10, 48, 4, 1, 7, FAKE, None) == 3
+    assert lib.gdn_conv1d_silu(FAKE + 2, FAKE, FAKE, 1, 10, 48, 4, 1, 1, FAKE, None) == 4
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(2, 1, 16)
+    with pytest.raises(ValueError):
+        gdn._dev(q)
+
+
+def test_product_path_does_not_import_the_oracle():
+    """The oracle is test infrastructure: the package and the library sources never name it."""
+    pkg = os.path.join(ROOT, "gated_delta_rule_prefill_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "liboracle" not in text and "gdn_oracle" not in text, f

@@ -1,0 +1,150 @@
+"""DeltaLog decode (dense base + append log, merge every M steps) on the GPU, against the
+oracle's DeltaLog bookkeeping, the oracle's dense recurrence and the GPU dense decode."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_prefill_amd import gdn, inputs
+from gpu_util import DEV, say, to_dev
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_scalar_worked_example_embedded():
+    """DeltaLog notes §2.3 teaching example embedded at d = 16: k = e1, beta = 1,
+    alpha = 1/2, S0[0,0] = 10 and v chosen so the corrected updates are 2, 3, 4
+    (v_t = S_{t-1}[0,0]/2 + increment); M = 3 -> logical 7, 6.5, 7.25; base 10, 10, 7.25."""
+    say("case deltalog worked example")
+    ex = json.load(open(os.path.join(GOLDEN, "deltalog_scalar_example.json")))
+    d = 16
+    base = torch.zeros((1, 1, d, d), device=DEV)
+    base[0, 0, 0, 0] = ex["S0"]
+    pool = gdn.DeltaLogPool(base, M=ex["M"])
+    slots = torch.zeros(1, dtype=torch.int32, device=DEV)
+    e1 = torch.zeros((1, 1, d), device=DEV)
+    e1[0, 0, 0] = 1.0
+    logical = ex["S0"]
+    for t, inc in enumerate(ex["increments"]):
+        v = torch.zeros((1, 1, d), device=DEV)
+        v[0, 0, 0] = logical * ex["decay"] + inc       # residual after decay = increment
+        g = torch.full((1, 1), math.log(ex["decay"]), device=DEV)
+        o = gdn.gdn_decode_deltalog(e1, e1, v, g, torch.ones((1, 1), device=DEV), pool, slots)
+        torch.cuda.synchronize()
+        logical = ex["logical_state"][t]
+        assert abs(o[0, 0, 0].item() - logical) < 1e-5
+        assert abs(pool.base[0, 0, 0, 0].item() - ex["base"][t]) < 1e-5
+    assert pool.len[0, 0].item() == 0
+    assert abs(pool.ulog[0, 0, 0, 0].item() - 2.0) < 1e-5
+    assert abs(pool.ulog[0, 0, 1, 0].item() - 3.0) < 1e-5
+
+
+@pytest.mark.parametrize("dtype,d,M,l2", [
+    (torch.float32, 16, 2, False), (torch.float32, 64, 3, False),
+    (torch.bfloat16, 128, 8, False), (torch.bfloat16, 32, 17, True),
+])
+def test_deltalog_vs_oracle_bookkeeping(dtype, d, M, l2):
+    """Step by step against the oracle's DeltaLog (same bf16 key log), and against the
+    oracle's dense recurrence; includes a batch where slots sit at different log lengths."""
+    say(f"case deltalog {dtype} d={d} M={M} l2={l2}")
+    B, H, n_slots, steps = 6, 2, 9, 2 * M + 3
+    base0 = inputs.decode_pool(6, n_slots, H, d, d)
+    slots = inputs.decode_slots(7, n_slots, B)
+    stream = inputs.DecodeStream(8, B, H, d, d, dtype=dtype, prenorm=not l2)
+    pool = gdn.DeltaLogPool(base0.to(DEV), M)
+    # stagger the log lengths: advance half the requests by some steps first
+    sl = slots.long()
+    ref = oracle.DeltaLogState(base0[sl].reshape(B * H, d, d).double().numpy(), M)
+    dense = base0[sl].double().numpy()
+    sd = slots.to(DEV)
+    worst_o = worst_dense = 0.0
+    for step in range(steps):
+        q, k, v, g, b = stream.next()
+        active = torch.arange(B) if step % 3 else torch.arange(B // 2)
+        sub = slots.clone()
+        sub[[i for i in range(B) if i not in active.tolist()]] = -1   # inactive rows
+        o = gdn.gdn_decode_deltalog(*to_dev(q, k, v, g, b), pool, sub.to(DEV), scale=0.2,
+                                    qk_l2norm=l2).cpu()
+        # oracle on the active rows only
+        idx = torch.tensor([i * H + h for i in active.tolist() for h in range(H)])
+        full_o = np.zeros((B * H, d))
+        sub_state = oracle.DeltaLogState(np.zeros((len(idx), d, d)), M)
+        for name in ("base", "lbar", "klog", "ulog", "lamlog", "len"):
+            getattr(sub_state, name)[:] = getattr(ref, name)[idx.numpy()]
+        f = lambda t: t.reshape(B * H, -1)[idx]
+        o_ref = sub_state.step(f(q), f(k), f(v), f(g), f(b).reshape(-1), scale=0.2, l2norm=l2)
+        for name in ("base", "lbar", "klog", "ulog", "lamlog", "len"):
+            getattr(ref, name)[idx.numpy()] = getattr(sub_state, name)
+        full_o[idx.numpy()] = o_ref
+        od, sd_new = oracle.decode_step(q[active], k[active], v[active], g[active], b[active],
+                                        dense[active.numpy()], scale=0.2, l2norm=l2)
+        dense[active.numpy()] = sd_new
+        got = o.reshape(B * H, d)[idx]
+        worst_o = max(worst_o, oracle.rel_err(got, o_ref))
+        worst_dense = max(worst_dense, oracle.rel_err(got, od.reshape(-1, d)))
+        assert torch.all(o[[i for i in range(B) if i not in active.tolist()]] == 0)
+    torch.cuda.synchronize()
+    say(f"   worst o vs oracle-DeltaLog {worst_o:.2e}, vs oracle-dense {worst_dense:.2e}")
+    bar = 1e-4 if dtype == torch.float32 else 1e-2
+    assert worst_o <= bar
+    assert worst_dense <= 5e-3
+    assert np.array_equal(pool.len.cpu()[sl].reshape(-1).numpy(), ref.len)
+    # materialize: base then equals the dense state
+    gdn.gdn_deltalog_materialize(pool, sd)
+    torch.cuda.synchronize()
+    assert torch.all(pool.len.cpu()[sl] == 0)
+    assert oracle.rel_err(pool.base.cpu()[sl], dense) <= 5e-3
+    assert oracle.rel_err(pool.base.cpu()[sl].reshape(B * H, d, d), ref.materialize()) <= bar
+
+
+def test_reset_clears_log_keeps_base():
+    say("case deltalog reset")
+    d, H = 32, 2
+    base0 = inputs.decode_pool(9, 4, H, d, d).to(DEV)
+    pool = gdn.DeltaLogPool(base0.clone(), 4)
+    slots = torch.tensor([1, 3], dtype=torch.int32, device=DEV)
+    q, k, v, g, b = inputs.DecodeStream(10, 2, H, d, d).next()
+    gdn.gdn_decode_deltalog(*to_dev(q, k, v, g, b), pool, slots)
+    gdn.gdn_deltalog_reset(pool, slots)
+    torch.cuda.synchronize()
+    assert torch.all(pool.len == 0) and torch.all(pool.lbar == 0)
+    assert torch.equal(pool.base, base0)
+
+
+def test_deltalog_config_vs_dense_full_size():
+    """DeltaLog decode vs dense decode at full size: B=512, H=32, d=128, fp32 state (1 GiB
+    per layer), M=8 (log capacity 7), 128-step rollout (16 merge cycles), identical inputs.
+    5e-3 bar: DeltaLog outputs against the exact dense recurrence (oracle, sampled units,
+    every step) and the materialised fp32 DeltaLog state against the GPU dense fp32 state.
+    DeltaLog and dense GPU outputs are both rounded to bf16, so they are compared at the bf16
+    bar (they can differ by one bf16 ulp, up to 2^-7 of an element)."""
+    say("case deltalog B=512 vs dense, 128 steps")
+    B, H, d, M, steps = 512, 32, 128, 8, 128
+    base0 = inputs.decode_pool(1, B, H, d, d)
+    slots = inputs.decode_slots(0, B, B)
+    dense = base0.to(DEV)
+    pool = gdn.DeltaLogPool(base0.to(DEV), M)
+    sd = slots.to(DEV)
+    stream = inputs.DecodeStream(0, B, H, d, d)
+    rng = np.random.default_rng(1)
+    bs, hs = rng.choice(B, 48), rng.choice(H, 48)
+    S = base0[slots.long()[bs], hs].double().numpy()[:, None]
+    worst = worst_or = 0.0
+    for step in range(steps):
+        q, k, v, g, b = to_dev(*stream.next())
+        od = gdn.gdn_decode_step(q, k, v, g, b, dense, sd, scale=d ** -0.5)
+        ol = gdn.gdn_decode_deltalog(q, k, v, g, b, pool, sd, scale=d ** -0.5)
+        worst = max(worst, oracle.rel_err(ol.float().cpu(), od.float().cpu()))
+        sel = lambda t: t.cpu()[bs, hs][:, None]
+        o_ref, S = oracle.decode_step(sel(q), sel(k), sel(v), sel(g), sel(b), S, scale=d ** -0.5)
+        worst_or = max(worst_or, oracle.rel_err(ol.cpu()[bs, hs], o_ref[:, 0]))
+    gdn.gdn_deltalog_materialize(pool, sd)
+    torch.cuda.synchronize()
+    e_s = oracle.rel_err(pool.base.cpu(), dense.cpu())
+    say(f"   worst o DeltaLog vs dense {worst:.2e}; state {e_s:.2e}; vs oracle {worst_or:.2e}")
+    assert worst <= 1e-2 and e_s <= 5e-3 and worst_or <= 5e-3

@@ -1,0 +1,190 @@
+"""Chunked prefill on the GPU vs the fp64 oracle, element by element, through the C ABI.
+
+Bars (per tensor, max|x - ref| / max|ref|): 1e-4 for fp32 inputs, 1e-2 for bf16 inputs, on
+outputs and final states.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_prefill_amd import gdn, inputs
+from gpu_util import BAR, DEV, oracle_prefill, run_prefill, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(x, o, pool, o_ref, s_ref, bar=None, slots=None):
+    bar = bar or BAR[x.dtype]
+    e_o = oracle.rel_err(o, o_ref)
+    sl = slots if slots is not None else torch.arange(x.n_seqs)
+    e_s = oracle.rel_err(pool[sl.long()], s_ref)
+    say(f"   rel err o={e_o:.2e} S={e_s:.2e} (bar {bar:g})")
+    assert np.isfinite(o.float().numpy()).all()
+    assert e_o <= bar and e_s <= bar
+
+
+def test_tiny_gdn_fp32():
+    """Tiny GDN: T=64, H=1, d=16, chunk 16, fp32, zero initial state."""
+    say("case tiny fp32 T=64 d=16 C=16")
+    x = inputs.tiny_config(0)
+    o, pool = run_prefill(x)
+    o_ref, s_ref = oracle_prefill(x)
+    _check(x, o, pool, o_ref, s_ref)
+
+
+CASES = [
+    # (dtype, d, chunk, perkey, lengths, init, l2norm)
+    (torch.float32, 16, 16, False, [64], False, False),
+    (torch.float32, 32, 32, True, [1, 31, 70], True, False),
+    (torch.float32, 64, 64, False, [129, 5], True, True),
+    (torch.float32, 128, 64, True, [100], True, False),
+    (torch.bfloat16, 16, 16, True, [17, 64, 3], True, True),
+    (torch.bfloat16, 16, 32, False, [50, 33], True, False),
+    (torch.bfloat16, 32, 32, False, [65, 96], False, False),
+    (torch.bfloat16, 64, 16, True, [200], True, False),
+    (torch.bfloat16, 64, 64, False, [1, 2, 63, 64, 65], True, True),
+    (torch.bfloat16, 128, 64, False, [300, 1, 77], True, False),
+    (torch.bfloat16, 128, 64, True, [191, 64], True, True),
+    (torch.bfloat16, 128, 32, True, [150], False, False),
+    (torch.bfloat16, 128, 16, False, [90, 40], True, False),
+]
+
+
+@pytest.mark.parametrize("dtype,d,chunk,perkey,lengths,init,l2", CASES)
+def test_prefill_vs_oracle(dtype, d, chunk, perkey, lengths, init, l2):
+    say(f"case prefill {dtype} d={d} C={chunk} perkey={perkey} lens={lengths} init={init} l2={l2}")
+    x = inputs.random_prefill(11, lengths, H=3, dk=d, dv=d, dtype=dtype, perkey=perkey,
+                              chunk=chunk, prenorm=not l2, with_init=init)
+    o, pool = run_prefill(x)
+    o_ref, s_ref = oracle_prefill(x)
+    _check(x, o, pool, o_ref, s_ref)
+
+
+@pytest.mark.parametrize("perkey", [False, True])
+def test_chunk_size_invariance(perkey):
+    """The chunk size is an execution choice: C = 16, 32, 64 give the same result."""
+    say(f"case chunk invariance perkey={perkey}")
+    x = inputs.random_prefill(12, [333, 45], H=2, dk=128, dv=128, perkey=perkey, with_init=True)
+    outs = [run_prefill(x, chunk=c) for c in (16, 32, 64)]
+    o_ref, s_ref = oracle_prefill(x)
+    for o, pool in outs:
+        _check(x, o, pool, o_ref, s_ref)
+
+
+def test_split_prefill_handoff_and_decode_continuation():
+    """Handbook split-prefill: 20 | 25 | 19 tokens with the state handed over through the pool,
+    then decode steps, equals one-shot prefill of all 64 + 8 tokens."""
+    say("case split handoff")
+    T = 72
+    x = inputs.random_prefill(13, [T], H=4, dk=128, dv=128)
+    o_ref, s_ref = oracle_prefill(x)
+    pool = torch.zeros((2, 4, 128, 128), device=DEV)
+    slots = torch.tensor([1], dtype=torch.int32, device=DEV)
+    outs = []
+    for i, (a, b) in enumerate(((0, 20), (20, 45), (45, 64))):
+        q, k, v, g, be = to_dev(x.q[a:b], x.k[a:b], x.v[a:b], x.g[a:b], x.beta[a:b])
+        cu = torch.tensor([0, b - a], dtype=torch.int32, device=DEV)
+        hi = torch.tensor([1 if i else 0], dtype=torch.int32, device=DEV)
+        outs.append(gdn.gdn_prefill_chunked(q, k, v, g, be, cu, 64, pool, slots, has_init=hi,
+                                            scale=x.scale).cpu())
+    for t in range(64, T):
+        q, k, v, g, be = to_dev(*(z[t:t + 1] for z in (x.q, x.k, x.v, x.g, x.beta)))
+        outs.append(gdn.gdn_decode_step(q, k, v, g, be, pool, slots, scale=x.scale).cpu())
+    torch.cuda.synchronize()
+    o = torch.cat(outs)
+    assert oracle.rel_err(o, o_ref) <= 1e-2
+    assert oracle.rel_err(pool.cpu()[1], s_ref[0]) <= 1e-2
+    assert torch.all(pool.cpu()[0] == 0)
+
+
+def test_per_key_equal_channels_matches_scalar_gate():
+    say("case per-key equal channels")
+    x = inputs.random_prefill(14, [200, 37], H=2, dk=64, dv=64, with_init=True)
+    o1, p1 = run_prefill(x)
+    x.g = x.g[:, :, None].expand(-1, -1, 64).contiguous()
+    o2, p2 = run_prefill(x)
+    assert oracle.rel_err(o2, o1) <= 1e-2 and oracle.rel_err(p2, p1) <= 1e-2
+
+
+def test_per_key_strong_decay_no_overflow():
+    """Appendix 1 stress: per-key log gate -5 on every channel and step (the pages' lower
+    bound): the in-chunk cumulative gate reaches -320; results stay finite and match."""
+    say("case per-key g=-5 stress")
+    x = inputs.random_prefill(15, [256], H=2, dk=128, dv=128, perkey=True, with_init=True)
+    x.g = torch.full_like(x.g, -5.0)
+    o, pool = run_prefill(x)
+    o_ref, s_ref = oracle_prefill(x)
+    _check(x, o, pool, o_ref, s_ref)
+
+
+def test_slots_untouched_noslot_and_empty_sequences():
+    """Pool slots not named stay bit-identical; a sequence with slot -1 starts from zero and
+    stores nothing; empty sequences store their initial (or zero) state."""
+    say("case slots / no-slot / empty")
+    x = inputs.random_prefill(16, [40, 0, 70, 0], H=2, dk=64, dv=64, with_init=True)
+    pool = torch.randn(6, 2, 64, 64)
+    slots = torch.tensor([4, 1, -1, 2], dtype=torch.int32)
+    has_init = torch.tensor([1, 1, 1, 0], dtype=torch.int32)
+    init = torch.stack([pool[4], pool[1], torch.zeros(2, 64, 64), torch.zeros(2, 64, 64)])
+    o, after = run_prefill(x, pool=pool.clone(), slots=slots, has_init=has_init)
+    o_ref, s_ref = oracle_prefill(x, init=init)
+    assert oracle.rel_err(o, o_ref) <= 1e-2
+    assert oracle.rel_err(after[4], s_ref[0]) <= 1e-2
+    assert torch.equal(after[1], pool[1])               # empty sequence, has_init
+    assert torch.all(after[2] == 0)                     # empty sequence, zero init
+    for untouched in (0, 3, 5):
+        assert torch.equal(after[untouched], pool[untouched])
+
+
+def test_deterministic():
+    say("case determinism")
+    x = inputs.random_prefill(17, [500, 300], H=4, dk=128, dv=128, perkey=True)
+    o1, p1 = run_prefill(x)
+    o2, p2 = run_prefill(x)
+    assert torch.equal(o1, o2) and torch.equal(p1, p2)
+
+
+def test_prefill_config_full_size():
+    """GDN chunked prefill at its full size: B=1, H=16, T=8192, d=128, chunk 64, bf16."""
+    say("case prefill full size T=8192 H=16")
+    x = inputs.prefill_config(0)
+    o, pool = run_prefill(x)
+    o_ref, s_ref = oracle_prefill(x)
+    _check(x, o, pool, o_ref, s_ref)
+
+
+def test_kda_varlen_with_conv_sampled_heads():
+    """KDA-style varlen prefill at full size (8 sequences, 1k-8k tokens, H=32, d=128):
+    conv1d + SiLU pre-pass, in-kernel L2 norm, per-key gate. Checked element by element on a
+    sample of heads (every output of those heads and their final states)."""
+    say("case KDA varlen full size, sampled heads")
+    x = inputs.kda_varlen_config(0)
+    H, d = x.H, x.d
+    xd, wd, cud = to_dev(x.x, x.conv_w, x.cu_seqlens)
+    qkv = gdn.gdn_conv1d_silu(xd, wd, cud, planes=3)
+    T = x.x.shape[0]
+    q, k, v = (qkv[i].view(T, H, d) for i in range(3))
+    pool = torch.zeros((8, H, d, d), device=DEV)
+    g, b = to_dev(x.g, x.beta)
+    o = gdn.gdn_prefill_chunked(q, k, v, g, b, cud, x.chunk, pool,
+                                torch.arange(8, dtype=torch.int32, device=DEV),
+                                scale=x.scale, qk_l2norm=True)
+    torch.cuda.synchronize()
+    heads = [0, 13, 31]
+    ch = torch.tensor([p * H * d + h * d + j for p in range(3) for h in heads for j in range(d)])
+    y = oracle.conv1d_silu(x.x[:, ch], x.conv_w[ch], x.cu_seqlens)
+    # the oracle's conv output is rounded to the same bf16 tensor the GPU hands to prefill
+    y = torch.tensor(y).to(torch.bfloat16)
+    nh = len(heads)
+    qs, ks, vs = (y[:, i * nh * d:(i + 1) * nh * d].view(T, nh, d) for i in range(3))
+    gpu_qkv = qkv.cpu()
+    for i, t in enumerate((qs, ks, vs)):
+        got = gpu_qkv[i].view(T, H, d)[:, heads]
+        assert oracle.rel_err(got, t) <= 1e-2
+    o_ref, s_ref = oracle.recurrence(qs, ks, vs, x.g[:, heads], x.beta[:, heads], x.cu_seqlens,
+                                     scale=x.scale, l2norm=True)
+    e_o = oracle.rel_err(o.cpu()[:, heads], o_ref)
+    e_s = oracle.rel_err(pool.cpu()[:, heads], s_ref)
+    say(f"   rel err o={e_o:.2e} S={e_s:.2e}")
+    assert e_o <= 1e-2 and e_s <= 1e-2
