@@ -108,22 +108,31 @@ struct Frag {
 // =====================================================================================
 // prep kernel
 // =====================================================================================
+// One workgroup per (chunk, head); wave w owns token block w (16 tokens) for the row-wise
+// work. Phases (LDS barriers between them):
+//   P0  loads (K, Q, V straight into MFMA row fragments), L2 norm, gate prefix sums
+//   P1  Q_in, K_g^T, (beta K_in)^T via identity-MFMA transposes; A and M tiles
+//   P2  16x16 leaf inverses of I + A (forward substitution, one lane per column), V^T
+//   P3  2x2 block merges on fp32 MFMA (16 -> 32 -> 64), in place over A
+//   P4  -W and U on MFMA, written to the workspace
 template <typename T, int DK, int DV, int C, bool PERKEY>
 struct PrepSmem {
     using F = PfCfg<T, DK, DV, C>;
     // live for the whole kernel
-    alignas(16) float af[C][C + 1];   // A (strictly lower); upper part reused as scratch
+    alignas(16) float ar[C][C + 1];   // A (strictly lower), then R = (I + A)^{-1} in place;
+                                      // the strictly upper part is merge scratch
     alignas(16) float bs[C];          // beta
-    alignas(16) T kint[DK][F::LDC];   // (diag(beta) K_in)^T, made in phase A, used in phase B
+    alignas(16) float eg[C];          // scalar gate: e^{G_i}
+    alignas(16) float egc[C];         // scalar gate: e^{G_C - G_i}
+    alignas(16) T kint[DK][F::LDC];   // (diag(beta) K_in)^T
     union {
-        struct {                      // phase A: inputs, gates, A and M
-            alignas(16) T ks[C][F::LDK];   // keys (normalised if requested)
-            alignas(16) T qs[C][F::LDK];   // queries
+        struct {                      // P0-P1: keys and queries in fragment-major order
+            alignas(16) T ks[C * F::DKP];
+            alignas(16) T qs[C * F::DKP];
             alignas(16) float gs[PERKEY ? C : 1][PERKEY ? DK + 4 : C];  // cumulative log gate
             float gseg[PERKEY ? PF_THREADS / DK : 1][PERKEY ? DK : 1];    // segment totals
         } a;
-        struct {                      // phase B: triangular solve, U and W
-            alignas(16) float rf[C][C + 1];  // R = (I + A)^{-1} (lower, unit diagonal)
+        struct {                      // P2-P4
             alignas(16) T rs[C][F::LDC];     // R as an MFMA operand
             alignas(16) T vt[DV][F::LDC];    // (diag(beta) V)^T
         } b;
@@ -136,196 +145,250 @@ __device__ __forceinline__ float gval(const float (*gs)[PERKEY ? DK + 4 : C], in
     else return gs[0][i];
 }
 
+// Identity B fragments: MFMA(A_rows, I_h) returns, in accumulator layout, the 16 x 16 block
+// of the row fragment A_rows whose columns are selected by h, i.e. lane (g, n) receives
+// A[4g + e][16 cb + n] — four consecutive rows of one column, the transposed orientation.
+template <typename T> struct Ident;
+template <> struct Ident<bf16> {
+    static constexpr int N = 2;  // 32 columns per fragment: two 16-column halves
+    __device__ __forceinline__ static void make(bf16x8 (&id)[2]) {
+        const int g = lane_id() >> 4, n = lane_id() & 15;
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+            for (int e = 0; e < 8; e++) id[h][e] = (bf16)((8 * g + e == 16 * h + n) ? 1.f : 0.f);
+    }
+    template <int NK>
+    __device__ __forceinline__ static f32x4 transpose(const bf16x8 (&rows)[NK], int cb,
+                                                      const bf16x8 (&id)[2]) {
+        return Mma<bf16>::mma(rows[cb >> 1], id[cb & 1], zero4());
+    }
+};
+template <> struct Ident<float> {
+    static constexpr int N = 4;  // 4 columns per fragment
+    __device__ __forceinline__ static void make(float (&id)[4]) {
+        const int g = lane_id() >> 4, n = lane_id() & 15;
+#pragma unroll
+        for (int s4 = 0; s4 < 4; s4++) id[s4] = (4 * s4 + g == n) ? 1.f : 0.f;
+    }
+    template <int NK>
+    __device__ __forceinline__ static f32x4 transpose(const float (&rows)[NK], int cb,
+                                                      const float (&id)[4]) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int s4 = 0; s4 < 4; s4++) acc = Mma<float>::mma(rows[4 * cb + s4], id[s4], acc);
+        return acc;
+    }
+};
+
 template <typename T, int DK, int DV, int C, bool PERKEY>
 __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a) {
     using F = PfCfg<T, DK, DV, C>;
     using MM = typename F::MM;
+    using frag = typename MM::frag;
     constexpr int KB = F::KB, KPL = F::KPL, CP = F::CP, NB = F::NB, DKP = F::DKP;
+    constexpr int NK = DKP / KB;                       // row fragments over d_k
+    constexpr int NV = ((DV + KB - 1) / KB);           // row fragments over d_v
     extern __shared__ __align__(16) unsigned char smem_raw[];
     auto& sm = *reinterpret_cast<PrepSmem<T, DK, DV, C, PERKEY>*>(smem_raw);
 
     const int H = a.H;
     const int c = blockIdx.x / H;
     const int h = blockIdx.x - c * H;
-    const ChunkLoc loc = locate_chunk(c, a.ws.seq_first, a.cu_seqlens, a.n_seqs, C, a.total_tokens);
+    const ChunkLoc loc = locate_chunk(c, a.ws.seq_first, a.cu_seqlens, a.n_seqs, C,
+                                      a.total_tokens);
     if (loc.seq < 0) return;
     const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+    const int g4 = lane >> 4, r16 = lane & 15;
     const size_t u = (size_t)c * H + h;  // (chunk, head) workspace unit
+    const bool own = w < NB;             // this wave owns token block w
+    const int row = w * 16 + r16;        // token row of this lane's row fragments
+    const bool rvalid = own && row < loc.len;
 
-    // V rows are only needed in phase B; fetch them into registers now so the load latency
-    // overlaps phase A (tokens past the chunk end and the padding up to CP read as zero)
-    constexpr int TPRV = DV / 8;
-    constexpr int NVR = (CP * TPRV + PF_THREADS - 1) / PF_THREADS;
-    float vreg[NVR][8];
+    // ------------------------------------------------------------------------ P0 loads
+    frag kf[NK], qf[NK], vf[NV];
     {
-        const T* vg = reinterpret_cast<const T*>(a.v);
+        const size_t tk = ((size_t)(loc.tok0 + row) * H + h);
+        const T* kg = reinterpret_cast<const T*>(a.k) + tk * DK;
+        const T* qg = reinterpret_cast<const T*>(a.q) + tk * DK;
+        const T* vg = reinterpret_cast<const T*>(a.v) + tk * DV;
 #pragma unroll
-        for (int r = 0; r < NVR; r++) {
-            const int idx = tid + r * PF_THREADS;
-            const int i = idx / TPRV, c0 = (idx % TPRV) * 8;
-            if (idx < CP * TPRV && i < loc.len) {
-                const size_t off = ((size_t)(loc.tok0 + i) * H + h) * DV + c0;
-                load4<T>(vg + off, vreg[r]);
-                load4<T>(vg + off + 4, vreg[r] + 4);
+        for (int kb = 0; kb < NK; kb++) {
+            const int c0 = kb * KB + g4 * KPL;
+            kf[kb] = MM::zero();
+            qf[kb] = MM::zero();
+            if (rvalid && c0 < DK) {
+                kf[kb] = MM::load(kg + c0);
+                qf[kb] = MM::load(qg + c0);
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < NV; kb++) {
+            const int c0 = kb * KB + g4 * KPL;
+            vf[kb] = MM::zero();
+            if (rvalid && c0 < DV) vf[kb] = MM::load(vg + c0);
+        }
+    }
+    constexpr int GP = PERKEY ? PF_THREADS / DK : 1;  // per-key gate: row segments per channel
+    constexpr int GR = PERKEY ? C / GP : 1;           // rows per segment
+    float gv[GR];
+    const int gch = tid % DK, gseg = tid / DK;
+    if constexpr (PERKEY) {
+#pragma unroll
+        for (int r = 0; r < GR; r++) {
+            const int i = gseg * GR + r;
+            gv[r] = i < loc.len ? a.g[((size_t)(loc.tok0 + i) * H + h) * DK + gch] : 0.f;
+        }
+    }
+    float gsc = 0.f, bval = 0.f;
+    if (!PERKEY && w == 0)
+        gsc = (lane < loc.len && lane < C) ? a.g[(size_t)(loc.tok0 + lane) * H + h] : 0.f;
+    if (tid < C && tid < loc.len) bval = a.beta[(size_t)(loc.tok0 + tid) * H + h];
+
+    // L2 norm of q and k rows: a row lives in the 4 lane groups sharing r16
+    if (a.l2norm) {
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < NK; kb++) {
+#pragma unroll
+            for (int e = 0; e < KPL; e++) {
+                float x, y;
+                if constexpr (KPL == 1) { x = to_f32(kf[kb]); y = to_f32(qf[kb]); }
+                else { x = to_f32(kf[kb][e]); y = to_f32(qf[kb][e]); }
+                sk += x * x;
+                sq += y * y;
+            }
+        }
+        sk += __shfl_xor(sk, 16, WAVE);
+        sk += __shfl_xor(sk, 32, WAVE);
+        sq += __shfl_xor(sq, 16, WAVE);
+        sq += __shfl_xor(sq, 32, WAVE);
+        const float ik = rsqrtf(sk + 1e-6f), iq = rsqrtf(sq + 1e-6f);
+#pragma unroll
+        for (int kb = 0; kb < NK; kb++) {
+            if constexpr (KPL == 1) {
+                kf[kb] = from_f32<T>(to_f32(kf[kb]) * ik);
+                qf[kb] = from_f32<T>(to_f32(qf[kb]) * iq);
             } else {
 #pragma unroll
-                for (int j = 0; j < 8; j++) vreg[r][j] = 0.f;
+                for (int e = 0; e < KPL; e++) {
+                    kf[kb][e] = from_f32<T>(to_f32(kf[kb][e]) * ik);
+                    qf[kb][e] = from_f32<T>(to_f32(qf[kb][e]) * iq);
+                }
             }
         }
     }
-    // ---------------- step 0: load K, Q (optionally L2-normalised), beta, G
-    // Every global load of this step is issued before the first one is consumed.
-    {
-        constexpr int TPR = DK / 8;  // threads per key row, 8 elements each
-        constexpr int NKR = (C * TPR + PF_THREADS - 1) / PF_THREADS;
-        const T* kg = reinterpret_cast<const T*>(a.k);
-        const T* qg = reinterpret_cast<const T*>(a.q);
-        float kv[NKR][8], qv[NKR][8];
+    // keys / queries to LDS in fragment-major order (conflict-free 16-byte accesses)
+    if (own) {
 #pragma unroll
-        for (int r = 0; r < NKR; r++) {
-            const int idx = tid + r * PF_THREADS;
-            const int i = idx / TPR, c0 = (idx % TPR) * 8;
-            if (idx < C * TPR && i < loc.len) {
-                const size_t off = ((size_t)(loc.tok0 + i) * H + h) * DK + c0;
-                load8<T>(kg + off, kv[r]);
-                load8<T>(qg + off, qv[r]);
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; j++) kv[r][j] = qv[r][j] = 0.f;
-            }
-        }
-        // per-key gate: thread (channel, row segment) loads its GR rows of g
-        constexpr int GP = PERKEY ? PF_THREADS / DK : 1;  // row segments per channel
-        constexpr int GR = PERKEY ? C / GP : 1;           // rows per segment
-        float gv[GR];
-        const int gch = tid % DK, gseg = tid / DK;
-        if constexpr (PERKEY) {
-#pragma unroll
-            for (int r = 0; r < GR; r++) {
-                const int i = gseg * GR + r;
-                gv[r] = i < loc.len ? a.g[((size_t)(loc.tok0 + i) * H + h) * DK + gch] : 0.f;
-            }
-        }
-        float gs_scalar = 0.f, bval = 0.f;
-        if (!PERKEY && w == 0)
-            gs_scalar = (lane < loc.len && lane < C) ? a.g[(size_t)(loc.tok0 + lane) * H + h] : 0.f;
-        if (tid < C && tid < loc.len) bval = a.beta[(size_t)(loc.tok0 + tid) * H + h];
-        // consume
-#pragma unroll
-        for (int r = 0; r < NKR; r++) {
-            const int idx = tid + r * PF_THREADS;
-            const int i = idx / TPR, c0 = (idx % TPR) * 8;
-            if (a.l2norm) {
-                float sk = 0.f, sq = 0.f;
-#pragma unroll
-                for (int j = 0; j < 8; j++) {
-                    sk += kv[r][j] * kv[r][j];
-                    sq += qv[r][j] * qv[r][j];
-                }
-                sk = group_sum<TPR>(sk);
-                sq = group_sum<TPR>(sq);
-                const float ik = rsqrtf(sk + 1e-6f), iq = rsqrtf(sq + 1e-6f);
-#pragma unroll
-                for (int j = 0; j < 8; j++) {
-                    kv[r][j] *= ik;
-                    qv[r][j] *= iq;
-                }
-            }
-            if (idx < C * TPR) {
-                store8<T>(&sm.u.a.ks[i][c0], kv[r]);
-                store8<T>(&sm.u.a.qs[i][c0], qv[r]);
-            }
-        }
-        if constexpr (DKP > DK) {  // zero the padded contraction columns
-            for (int idx = tid; idx < C * (DKP - DK); idx += PF_THREADS) {
-                const int i = idx / (DKP - DK), c0 = DK + idx % (DKP - DK);
-                sm.u.a.ks[i][c0] = from_f32<T>(0.f);
-                sm.u.a.qs[i][c0] = from_f32<T>(0.f);
-            }
-        }
-        if (tid < C) sm.bs[tid] = bval;
-        if constexpr (PERKEY) {
-            // in-register running sum of the segment, segment totals through LDS, then the
-            // prefix of the preceding segments is added
-            float run = 0.f;
-#pragma unroll
-            for (int r = 0; r < GR; r++) {
-                run += gv[r];
-                gv[r] = run;
-            }
-            sm.u.a.gseg[gseg][gch] = run;
-            lds_barrier();
-            float base = 0.f;
-            for (int p2 = 0; p2 < gseg; p2++) base += sm.u.a.gseg[p2][gch];
-#pragma unroll
-            for (int r = 0; r < GR; r++) sm.u.a.gs[gseg * GR + r][gch] = gv[r] + base;
-        } else {
-            if (w == 0) {
-                float x = gs_scalar;
-#pragma unroll
-                for (int off = 1; off < WAVE; off <<= 1) {
-                    float y = __shfl_up(x, off, WAVE);
-                    if (lane >= off) x += y;
-                }
-                if (lane < C) sm.u.a.gs[0][lane] = x;
-            }
+        for (int kb = 0; kb < NK; kb++) {
+            const int off = ((w * NK + kb) * 64 + lane) * KPL;
+            *reinterpret_cast<frag*>(&sm.u.a.ks[off]) = kf[kb];
+            *reinterpret_cast<frag*>(&sm.u.a.qs[off]) = qf[kb];
         }
     }
-    lds_barrier();
-    // ---------------- step 1-2: gated key copies, Q_in, whole-chunk decay
-    {
-        // Q_in = s Q e^{G} -> workspace, fragment-major [C][DKP]
-        constexpr int TPR = DK / 8;
+    if (tid < C) sm.bs[tid] = bval;
+    if constexpr (PERKEY) {
+        float run = 0.f;
+#pragma unroll
+        for (int r = 0; r < GR; r++) {
+            run += gv[r];
+            gv[r] = run;
+        }
+        sm.u.a.gseg[gseg][gch] = run;
+        lds_barrier();
+        float base = 0.f;
+        for (int p2 = 0; p2 < gseg; p2++) base += sm.u.a.gseg[p2][gch];
+#pragma unroll
+        for (int r = 0; r < GR; r++) sm.u.a.gs[gseg * GR + r][gch] = gv[r] + base;
+    } else if (w == 0) {
+        float x = gsc;
+#pragma unroll
+        for (int off = 1; off < WAVE; off <<= 1) {
+            const float y = __shfl_up(x, off, WAVE);
+            if (lane >= off) x += y;
+        }
+        const float gC = __shfl(x, C - 1, WAVE);
+        if (lane < C) {
+            sm.u.a.gs[0][lane] = x;
+            sm.eg[lane] = __expf(x);
+            sm.egc[lane] = __expf(gC - x);
+        }
+    }
+    lds_barrier();  // #1: gates, beta, keys, queries in LDS
+
+    // --------------------------------------------------- P1a: own token block, row-wise
+    frag idf[Ident<T>::N];
+    Ident<T>::make(idf);
+    if (own) {
+        // Q_in = s * Q * e^{G} -> workspace (fragment-major slot of this lane)
         T* qin = reinterpret_cast<T*>(a.ws.qin) + u * C * DKP;
-        for (int idx = tid; idx < C * TPR; idx += PF_THREADS) {
-            const int i = idx / TPR, c0 = (idx % TPR) * 8;
-            float out[8];
+        const float erow = PERKEY ? 1.f : sm.eg[row];
 #pragma unroll
-            for (int j = 0; j < 8; j++)
-                out[j] = a.scale * to_f32(sm.u.a.qs[i][c0 + j]) *
-                         __expf(gval<PERKEY, DK, C>(sm.u.a.gs, i, c0 + j));
-            Frag<T>::template store_run<8>(qin, i, c0, DKP, out);
-        }
-        if constexpr (DKP > DK) {
-            for (int idx = tid; idx < C * ((DKP - DK) / 4); idx += PF_THREADS) {
-                const int i = idx / ((DKP - DK) / 4), c0 = DK + (idx % ((DKP - DK) / 4)) * 4;
-                float z[4] = {0.f, 0.f, 0.f, 0.f};
-                Frag<T>::template store_run<4>(qin, i, c0, DKP, z);
+        for (int kb = 0; kb < NK; kb++) {
+            float vals[KPL];
+#pragma unroll
+            for (int e = 0; e < KPL; e++) {
+                const int ch = kb * KB + g4 * KPL + e;
+                float qv;
+                if constexpr (KPL == 1) qv = to_f32(qf[kb]);
+                else qv = to_f32(qf[kb][e]);
+                float f = erow;
+                if constexpr (PERKEY) f = ch < DK ? __expf(sm.u.a.gs[row][ch]) : 0.f;
+                vals[e] = a.scale * qv * f;
             }
+            T* dst = qin + ((w * NK + kb) * 64 + lane) * KPL;
+            if constexpr (KPL == 8) store8<T>(dst, vals);
+            else *dst = from_f32<T>(vals[0]);
         }
-        // K_in^T * beta (LDS) and K_g^T (workspace, fragment-major [DK][CP]), 8 tokens each
-        constexpr int TG = CP / 8;
+        // K transposes: lane (g4, n) gets K[16w + 4 g4 + e][16 cb + n]; scaled twice into
+        // (beta K_in)^T (LDS) and K_g^T (workspace, fragment-major)
         T* kgt = reinterpret_cast<T*>(a.ws.kgt) + u * DK * CP;
-        for (int idx = tid; idx < DK * TG; idx += PF_THREADS) {
-            const int ch = idx / TG, i0 = (idx % TG) * 8;
-            const float gC = gval<PERKEY, DK, C>(sm.u.a.gs, C - 1, ch);
-            float kin[8], kgv[8];
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const int i = i0 + j;
-                if (i < C) {
-                    const float kk = to_f32(sm.u.a.ks[i][ch]);
-                    const float gi = gval<PERKEY, DK, C>(sm.u.a.gs, i, ch);
-                    kin[j] = sm.bs[i] * kk * __expf(gi);
-                    kgv[j] = kk * __expf(gC - gi);
+        for (int cb = 0; cb < DK / 16; cb++) {
+            const f32x4 kt = Ident<T>::template transpose<NK>(kf, cb, idf);
+            const int ch = cb * 16 + r16;
+            const int t0 = w * 16 + g4 * 4;
+            float kin[4], kgv[4];
+            const float gC = PERKEY ? sm.u.a.gs[C - 1][ch] : 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int t = t0 + e;
+                float fin, fg;
+                if constexpr (PERKEY) {
+                    const float gt = sm.u.a.gs[t][ch];
+                    fin = __expf(gt);
+                    fg = __expf(gC - gt);
                 } else {
-                    kin[j] = 0.f;
-                    kgv[j] = 0.f;
+                    fin = sm.eg[t];
+                    fg = sm.egc[t];
                 }
+                kin[e] = sm.bs[t] * kt[e] * fin;
+                kgv[e] = kt[e] * fg;
             }
-            store8<T>(&sm.kint[ch][i0], kin);
-            Frag<T>::template store_run<8>(kgt, ch, i0, CP, kgv);
+            store4<T>(&sm.kint[ch][t0], kin);
+            Frag<T>::template store_run<4>(kgt, ch, t0, CP, kgv);
         }
-        if (tid < DK) a.ws.decay[u * DK + tid] = __expf(gval<PERKEY, DK, C>(sm.u.a.gs, C - 1, tid));
     }
-    // ---------------- step 3a: A and M (transposed tiles: row = j, column = i), one pass
+    // zero the K_g^T / (beta K_in)^T token padding [C, CP)
+    if constexpr (CP > C) {
+        T* kgt = reinterpret_cast<T*>(a.ws.kgt) + u * DK * CP;
+        for (int idx = tid; idx < DK * ((CP - C) / 4); idx += PF_THREADS) {
+            const int ch = idx / ((CP - C) / 4), t0 = C + (idx % ((CP - C) / 4)) * 4;
+            float z[4] = {0.f, 0.f, 0.f, 0.f};
+            store4<T>(&sm.kint[ch][t0], z);
+            Frag<T>::template store_run<4>(kgt, ch, t0, CP, z);
+        }
+    }
+    // Q_in padding channels [DK, DKP) were loaded as zeros and stored above
+    if (tid < DK) a.ws.decay[u * DK + tid] = __expf(gval<PERKEY, DK, C>(sm.u.a.gs, C - 1, tid));
+
+    // ------------------------------------------------------- P1b: A and M tiles
     {
         constexpr int NT = NB * (NB + 1) / 2;
         T* mmat = reinterpret_cast<T*>(a.ws.mmat) + u * C * CP;
-        const int r16 = lane & 15, kq = (lane >> 4) * KPL;
         for (int t = w; t < NT; t += PF_WAVES) {
-            // t -> (jb <= ib)
-            int ib = 0, rem = t;
+            int ib = 0, rem = t;  // t -> (jb <= ib)
             while (rem > ib) {
                 rem -= ib + 1;
                 ib++;
@@ -335,21 +398,29 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
             f32x4 accK = zero4(), accQ = zero4();
             const int jrow = jb * 16 + r16, irow = ib * 16 + r16;
 #pragma unroll
-            for (int kb = 0; kb < DKP / KB; kb++) {
-                const int c0 = kb * KB + kq;
-                typename MM::frag fa, fbk, fbq;
+            for (int kb = 0; kb < NK; kb++) {
+                const frag ka = MM::load(&sm.u.a.ks[((jb * NK + kb) * 64 + lane) * KPL]);
+                const frag kbv = MM::load(&sm.u.a.ks[((ib * NK + kb) * 64 + lane) * KPL]);
+                const frag qbv = MM::load(&sm.u.a.qs[((ib * NK + kb) * 64 + lane) * KPL]);
+                frag fa, fbk, fbq;
                 if constexpr (PERKEY) {
 #pragma unroll
                     for (int e = 0; e < KPL; e++) {
-                        const int ch = c0 + e;
+                        const int ch = kb * KB + g4 * KPL + e;
                         float aj = 0.f, bk = 0.f, bq = 0.f;
                         if (ch < DK) {  // padded channels contribute zero
                             const float gr = sm.u.a.gs[ref][ch];
                             const float fj = __expf(gr - sm.u.a.gs[jrow][ch]);
                             const float fi = __expf(sm.u.a.gs[irow][ch] - gr);
-                            aj = to_f32(sm.u.a.ks[jrow][ch]) * fj;
-                            bk = to_f32(sm.u.a.ks[irow][ch]) * fi;
-                            bq = to_f32(sm.u.a.qs[irow][ch]) * fi;
+                            if constexpr (KPL == 1) {
+                                aj = to_f32(ka) * fj;
+                                bk = to_f32(kbv) * fi;
+                                bq = to_f32(qbv) * fi;
+                            } else {
+                                aj = to_f32(ka[e]) * fj;
+                                bk = to_f32(kbv[e]) * fi;
+                                bq = to_f32(qbv[e]) * fi;
+                            }
                         }
                         if constexpr (KPL == 1) {
                             fa = from_f32<T>(aj);
@@ -362,27 +433,26 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
                         }
                     }
                 } else {
-                    fa = MM::load(&sm.u.a.ks[jrow][c0]);
-                    fbk = MM::load(&sm.u.a.ks[irow][c0]);
-                    fbq = MM::load(&sm.u.a.qs[irow][c0]);
+                    fa = ka;
+                    fbk = kbv;
+                    fbq = qbv;
                 }
                 accK = MM::mma(fa, fbk, accK);
                 accQ = MM::mma(fa, fbq, accQ);
             }
-            // lane holds D[j = jb*16 + 4*(lane>>4) + e][i = ib*16 + (lane & 15)]
-            const int i = ib * 16 + r16;
+            // lane holds D[j = jb*16 + 4*g4 + e][i = ib*16 + r16]
+            const int i = irow;
             const float gi = PERKEY ? 0.f : sm.u.a.gs[0][i];
             float mrow[4];
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const int j = jb * 16 + (lane >> 4) * 4 + e;
+                const int j = jb * 16 + g4 * 4 + e;
                 float dec = 1.f;
                 if constexpr (!PERKEY) dec = (j <= i) ? __expf(gi - sm.u.a.gs[0][j]) : 0.f;
-                if (j < i) sm.af[i][j] = sm.bs[i] * accK[e] * dec;
+                if (j < i) sm.ar[i][j] = sm.bs[i] * accK[e] * dec;
                 mrow[e] = (j <= i) ? a.scale * accQ[e] * dec : 0.f;
             }
-            // M fragment-major [C][CP]: 4 consecutive j of row i
-            Frag<T>::template store_run<4>(mmat, i, jb * 16 + (lane >> 4) * 4, CP, mrow);
+            Frag<T>::template store_run<4>(mmat, i, jb * 16 + g4 * 4, CP, mrow);
         }
         // zero the upper tiles and the padding columns of M
         for (int idx = tid; idx < C * (CP / 4); idx += PF_THREADS) {
@@ -393,23 +463,20 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
             }
         }
     }
-    lds_barrier();  // phase A storage (keys, queries, gates) is dead from here on
-    // (diag(beta) V)^T into phase-B storage, zero-padded to CP tokens
-#pragma unroll
-    for (int r = 0; r < NVR; r++) {
-        const int idx = tid + r * PF_THREADS;
-        if (idx < CP * TPRV) {
-            const int i = idx / TPRV, c0 = (idx % TPRV) * 8;
-            const float b = i < C ? sm.bs[i] : 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; j++) sm.u.b.vt[c0 + j][i] = from_f32<T>(b * vreg[r][j]);
-        }
-    }
-    // ---------------- step 3b: R = (I + A)^{-1}, blocked (16x16 leaves, 2x2 merges)
+    lds_barrier();  // #2: A complete; keys, queries and gates are dead from here on
+
+    // ------------------------------------------- P2: leaf inverses, V^T, R zero padding
     if (w == 0) {
-        const int blk = lane >> 4, col = lane & 15;
+        // lane (blk, col): column col of (I + A_bb)^{-1} by forward substitution, with the
+        // block's strictly lower entries held in registers
+        const int blk = g4, col = r16;
         if (blk < NB) {
             const int b0 = blk * 16;
+            float av[16][16];
+#pragma unroll
+            for (int r = 1; r < 16; r++)
+#pragma unroll
+                for (int kk = 0; kk < r; kk++) av[r][kk] = sm.ar[b0 + r][b0 + kk];
             float x[16];
 #pragma unroll
             for (int r = 0; r < 16; r++) x[r] = (r == col) ? 1.f : 0.f;
@@ -417,65 +484,105 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
             for (int r = 1; r < 16; r++) {
                 float acc = 0.f;
 #pragma unroll
-                for (int kk = 0; kk < r; kk++) acc += sm.af[b0 + r][b0 + kk] * x[kk];
+                for (int kk = 0; kk < r; kk++) acc += av[r][kk] * x[kk];
                 x[r] -= acc;
             }
 #pragma unroll
-            for (int r = 0; r < 16; r++) sm.u.b.rf[b0 + r][b0 + col] = x[r];
+            for (int r = 0; r < 16; r++) {
+                sm.ar[b0 + r][b0 + col] = x[r];
+                sm.u.b.rs[b0 + r][b0 + col] = from_f32<T>(x[r]);
+            }
         }
     }
-    lds_barrier();
+    if (own) {
+        // (diag(beta) V)^T: lane (g4, n) gets V[16w + 4 g4 + e][16 vb + n]
+        const int t0 = w * 16 + g4 * 4;
+#pragma unroll
+        for (int vb = 0; vb < DV / 16; vb++) {
+            const f32x4 vt4 = Ident<T>::template transpose<NV>(vf, vb, idf);
+            float vv[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) vv[e] = sm.bs[t0 + e] * vt4[e];
+            store4<T>(&sm.u.b.vt[vb * 16 + r16][t0], vv);
+        }
+    }
+    // zeros: V^T padding tokens, R above the diagonal blocks and in the padding columns
+    if constexpr (CP > C) {
+        for (int idx = tid; idx < DV * ((CP - C) / 4); idx += PF_THREADS) {
+            const int ch = idx / ((CP - C) / 4), t0 = C + (idx % ((CP - C) / 4)) * 4;
+            float z[4] = {0.f, 0.f, 0.f, 0.f};
+            store4<T>(&sm.u.b.vt[ch][t0], z);
+        }
+    }
+    for (int idx = tid; idx < C * (CP / 4); idx += PF_THREADS) {
+        const int i = idx / (CP / 4), j0 = (idx % (CP / 4)) * 4;
+        if (j0 / 16 > i / 16 || j0 >= C) {
+            float z[4] = {0.f, 0.f, 0.f, 0.f};
+            store4<T>(&sm.u.b.rs[i][j0], z);
+        }
+    }
+    lds_barrier();  // #3: diagonal blocks of R
+
+    // ------------------------------------------------ P3: 2x2 block merges, fp32 MFMA
+    // (L^{-1})_{21} = -L_22^{-1} L_21 L_11^{-1}; the contraction index of each 16x16x4 step
+    // is taken as k = 4 g + s so that an accumulator is directly the next B operand.
     if constexpr (NB >= 2) {
-        // level 1: blocks (2p, 2p+1): R21 = -X_{2p+1} A_{2p+1,2p} X_{2p}
-        constexpr int NP = NB / 2;
-        for (int idx = tid; idx < NP * 256; idx += PF_THREADS) {
-            const int p = idx / 256, r = (idx % 256) / 16, cc = idx % 16;
-            const int lo = 2 * p * 16, hi = lo + 16;
-            float acc = 0.f;
+        if (w % 2 == 0 && w / 2 < NB / 2) {
+            const int lo = (w / 2) * 32, hi = lo + 16;
+            f32x4 t1 = zero4();
 #pragma unroll
-            for (int kk = 0; kk < 16; kk++) acc += sm.af[hi + r][lo + kk] * sm.u.b.rf[lo + kk][lo + cc];
-            sm.af[lo + r][hi + cc] = acc;  // T1 kept in the (unused) upper part of A
-        }
-        lds_barrier();
-        for (int idx = tid; idx < NP * 256; idx += PF_THREADS) {
-            const int p = idx / 256, r = (idx % 256) / 16, cc = idx % 16;
-            const int lo = 2 * p * 16, hi = lo + 16;
-            float acc = 0.f;
+            for (int s4 = 0; s4 < 4; s4++) {
+                const int k = 4 * g4 + s4;
+                t1 = Mma<float>::mma(sm.ar[hi + r16][lo + k], sm.ar[lo + k][lo + r16], t1);
+            }
+            f32x4 rr = zero4();
 #pragma unroll
-            for (int kk = 0; kk < 16; kk++) acc += sm.u.b.rf[hi + r][hi + kk] * sm.af[lo + kk][hi + cc];
-            sm.u.b.rf[hi + r][lo + cc] = -acc;
-            sm.u.b.rf[lo + r][hi + cc] = 0.f;
+            for (int s4 = 0; s4 < 4; s4++) {
+                const int k = 4 * g4 + s4;
+                rr = Mma<float>::mma(sm.ar[hi + r16][hi + k], t1[s4], rr);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                sm.ar[hi + 4 * g4 + e][lo + r16] = -rr[e];
+                sm.u.b.rs[hi + 4 * g4 + e][lo + r16] = from_f32<T>(-rr[e]);
+            }
         }
-        lds_barrier();
+        lds_barrier();  // #4
     }
     if constexpr (NB >= 4) {
-        // level 2: R[32:64, 0:32] = -R_B A[32:64, 0:32] R_A
-        for (int idx = tid; idx < 1024; idx += PF_THREADS) {
-            const int r = idx / 32, cc = idx % 32;
-            float acc = 0.f;
-#pragma unroll 8
-            for (int kk = 0; kk < 32; kk++) acc += sm.af[32 + r][kk] * sm.u.b.rf[kk][cc];
-            sm.af[r][32 + cc] = acc;  // T2 in the upper-right quarter of A
+        const int tr = w >> 1, tc = w & 1;
+        // T2 = A[32:64, 0:32] R[0:32, 0:32], tile (tr, tc), kept in the strictly upper
+        // quarter ar[0:32, 32:64]
+        f32x4 t2 = zero4();
+#pragma unroll
+        for (int kb = 0; kb < 8; kb++) {
+            const int k = 4 * kb + g4;
+            // R[k][col] is zero above the diagonal blocks (that part of ar was never written)
+            const float rb = (tc == 1 && k < 16) ? 0.f : sm.ar[k][16 * tc + r16];
+            t2 = Mma<float>::mma(sm.ar[32 + 16 * tr + r16][k], rb, t2);
         }
-        lds_barrier();
-        for (int idx = tid; idx < 1024; idx += PF_THREADS) {
-            const int r = idx / 32, cc = idx % 32;
-            float acc = 0.f;
-#pragma unroll 8
-            for (int kk = 0; kk < 32; kk++) acc += sm.u.b.rf[32 + r][32 + kk] * sm.af[kk][32 + cc];
-            sm.u.b.rf[32 + r][cc] = -acc;
+#pragma unroll
+        for (int e = 0; e < 4; e++) sm.ar[16 * tr + 4 * g4 + e][32 + 16 * tc + r16] = t2[e];
+        lds_barrier();  // #5
+        f32x4 rr = zero4();
+#pragma unroll
+        for (int kb = 0; kb < 8; kb++) {
+            const int k = 4 * kb + g4;
+            const float ra = (tr == 0 && k >= 16) ? 0.f : sm.ar[32 + 16 * tr + r16][32 + k];
+            rr = Mma<float>::mma(ra, sm.ar[k][32 + 16 * tc + r16], rr);
         }
-        lds_barrier();
+        // the A quarter ar[32:64, 0:32] was last read before barrier #5: overwrite with R_21
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            sm.ar[32 + 16 * tr + 4 * g4 + e][16 * tc + r16] = -rr[e];
+            sm.u.b.rs[32 + 16 * tr + 4 * g4 + e][16 * tc + r16] = from_f32<T>(-rr[e]);
+        }
     }
-    // R -> MFMA operand (lower triangle only, zero elsewhere and in the padding)
-    for (int idx = tid; idx < C * CP; idx += PF_THREADS) {
-        const int i = idx / CP, j = idx % CP;
-        sm.u.b.rs[i][j] = from_f32<T>((j <= i && j < C) ? sm.u.b.rf[i][j] : 0.f);
-    }
-    lds_barrier();
-    // ---------------- step 4: W^T = K_in^T R^T (stored as -W, row-major) and U = R (beta V)
+    lds_barrier();  // #6: R complete
+
+    // ---------------------------------------- P4: -W (fragment-major) and U (scan order)
     {
-        const int r16 = lane & 15, kq = (lane >> 4) * KPL;
+        const int kq = g4 * KPL;
         T* wneg = reinterpret_cast<T*>(a.ws.wneg) + u * C * DKP;
         if constexpr (DKP > DK) {
             for (int idx = tid; idx < C * ((DKP - DK) / 4); idx += PF_THREADS) {
@@ -487,32 +594,32 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
         float* ut = a.ws.ut + u * DV * C;
         constexpr int NW = (DK / 16) * NB;  // W^T tiles: (channel block, token block)
         constexpr int NU = NB * (DV / 16);  // U tiles: (token block, value block)
+        // tile order keeps the R fragments of one token block on one wave
         for (int t = w; t < NW + NU; t += PF_WAVES) {
             f32x4 acc = zero4();
             if (t < NW) {
-                const int mb = t / NB, nb = t % NB;  // mb: channel block, nb: token block
+                const int nb = t % NB, mb = t / NB;  // nb: token block, mb: channel block
 #pragma unroll
                 for (int kb = 0; kb < CP / KB; kb++) {
                     auto fa = MM::load(&sm.kint[mb * 16 + r16][kb * KB + kq]);
                     auto fb = MM::load(&sm.u.b.rs[nb * 16 + r16][kb * KB + kq]);
                     acc = MM::mma(fa, fb, acc);
                 }
-                // lane: W^T[ch = mb*16 + 4*(lane>>4) + e][i = nb*16 + r16]
+                // lane: W^T[ch = mb*16 + 4*g4 + e][i = nb*16 + r16]
                 float nw[4];
 #pragma unroll
                 for (int e = 0; e < 4; e++) nw[e] = -acc[e];
-                Frag<T>::template store_run<4>(wneg, nb * 16 + r16, mb * 16 + (lane >> 4) * 4, DKP, nw);
+                Frag<T>::template store_run<4>(wneg, nb * 16 + r16, mb * 16 + g4 * 4, DKP, nw);
             } else {
                 const int tt = t - NW;
-                const int mb = tt / (DV / 16), nb = tt % (DV / 16);  // token block, value block
+                const int mb = tt % NB, nb = tt / NB;  // mb: token block, nb: value block
 #pragma unroll
                 for (int kb = 0; kb < CP / KB; kb++) {
                     auto fa = MM::load(&sm.u.b.rs[mb * 16 + r16][kb * KB + kq]);
                     auto fb = MM::load(&sm.u.b.vt[nb * 16 + r16][kb * KB + kq]);
                     acc = MM::mma(fa, fb, acc);
                 }
-                // lane: U[i = mb*16 + 4*(lane>>4) + e][v = nb*16 + r16], stored in the scan's
-                // accumulator order: slot (value block nb, token block mb, lane)
+                // lane: U[i = mb*16 + 4*g4 + e][v = nb*16 + r16], scan accumulator order
                 float uu[4] = {acc[0], acc[1], acc[2], acc[3]};
                 store4<float>(ut + ((size_t)(nb * NB + mb) * 64 + lane) * 4, uu);
             }
