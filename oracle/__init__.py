@@ -24,9 +24,12 @@ _ip = ctypes.POINTER(ctypes.c_int32)
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB):
+        # GDN_ORACLE_LIB selects another build of the same source (the mutation tests load
+        # deliberately broken copies this way, in their own processes).
+        path = os.environ.get("GDN_ORACLE_LIB", LIB)
+        if path == LIB and not os.path.exists(LIB):
             build_oracle()
-        lib = ctypes.CDLL(LIB)
+        lib = ctypes.CDLL(path)
         lib.gdn_oracle_recurrence.restype = ctypes.c_int
         lib.gdn_oracle_recurrence.argtypes = [
             ctypes.c_int, _ip, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,

@@ -439,6 +439,24 @@ def test_deltalog_bf16_keys_exact_for_bf16_inputs():
                          .to(torch.bfloat16).double().numpy())) == 0.0
 
 
+def test_deltalog_fp32_keys_logged_as_bf16():
+    """[DeltaLog] §2.7: K_log is bf16. fp32 keys are logged as their round-to-nearest-even
+    bf16 values (torch's conversion as the independent rounding), not as the raw keys."""
+    n, dk, dv, M = 4, 32, 4, 5
+    r = _rng(15)
+    st = oracle.DeltaLogState(r.standard_normal((n, dk, dv)), M=M)
+    ks = []
+    for t in range(M - 1):
+        k = torch.tensor(_unit(r.standard_normal((n, dk)))).float().double().numpy()
+        ks.append(k)
+        st.step(_unit(r.standard_normal((n, dk))), k, r.standard_normal((n, dv)),
+                -r.uniform(0, 0.2, n), r.uniform(0, 1, n), klog_bf16=True)
+    ks = np.stack(ks, 1)
+    want = torch.tensor(ks).float().to(torch.bfloat16).double().numpy()
+    assert np.any(want != ks)
+    assert np.array_equal(st.klog, want)
+
+
 def test_deltalog_capacity_table():
     """[DeltaLog] §2.5 capacity table (golden): 21.125 / 17 / 14 MiB at B = 128."""
     from gated_delta_rule_prefill_amd.traffic import DeltaLogModel
