@@ -18,6 +18,7 @@ Also reported on the same JSON line (secondary workloads of the same metric):
   cpu_baseline: the fp64 oracle on the host cores over the same prefill workload
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-extras] [--no-cpu]
+       python bench.py --calibrate-copy --steps 3     (counter calibration only)
 """
 import argparse
 import hashlib
@@ -219,6 +220,19 @@ def cpu_baseline(budget_s=20.0):
                        f"({dt:.1f} s, one thread per (sequence, head) unit)")
 
 
+# ------------------------------------------------------------------- counter calibration
+def calibrate_copy(steps, nbytes=1 << 30):
+    """A plain device-to-device copy of known size (reads and writes `nbytes` each), run
+    under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE to turn the counters' units into bytes."""
+    src = torch.ones(nbytes // 4, device=DEV)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": nbytes,
+                      "bytes_written": nbytes, "launches": steps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -226,6 +240,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -235,6 +251,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.steps)
+        return
     gdn.load()
     digest = source_digest()
     log("prefill ...")
