@@ -15,7 +15,7 @@ namespace gdn {
 // (DKP = d_k rounded up to the MFMA contraction step, zero-padded)
 //   kgt   [d_k][CP]  e   K_g^T, K_g = K * e^{G_C - G}              (key-channel major)
 //   mmat  [C][CP]    e   M (lower triangular incl. diagonal)        row-major
-//   ut    [d_v][C]   f32 U^T (local residuals)                     (value-channel major)
+//   ut    [d_v][C]   e   U (local residuals), 16-column tiles in MFMA accumulator order
 //   decay [d_k]      f32 e^{G_C} per key channel
 struct PrefillWs {
     int32_t* chunk_info;   // [max_chunks][4]: seq, token start, length, 0
@@ -24,7 +24,7 @@ struct PrefillWs {
     void* qin;
     void* kgt;
     void* mmat;
-    float* ut;
+    void* ut;
     float* decay;
     void* dump;            // scratch words that absorb stores of lanes past a sequence end
     int64_t max_chunks;

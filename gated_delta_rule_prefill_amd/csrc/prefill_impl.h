@@ -591,7 +591,7 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
                 Frag<T>::template store_run<4>(wneg, i, c0, DKP, z);
             }
         }
-        float* ut = a.ws.ut + u * DV * C;
+        T* ut = reinterpret_cast<T*>(a.ws.ut) + u * DV * C;
         constexpr int NW = (DK / 16) * NB;  // W^T tiles: (channel block, token block)
         constexpr int NU = NB * (DV / 16);  // U tiles: (token block, value block)
         // tile order keeps the R fragments of one token block on one wave
@@ -621,7 +621,7 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
                 }
                 // lane: U[i = mb*16 + 4*g4 + e][v = nb*16 + r16], scan accumulator order
                 float uu[4] = {acc[0], acc[1], acc[2], acc[3]};
-                store4<float>(ut + ((size_t)(nb * NB + mb) * 64 + lane) * 4, uu);
+                store4<T>(ut + ((size_t)(nb * NB + mb) * 64 + lane) * 4, uu);
             }
         }
     }
@@ -663,7 +663,7 @@ __device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY>& op,
     const T* qin = reinterpret_cast<const T*>(a.ws.qin) + u * C * F::DKP;
     const T* mm = reinterpret_cast<const T*>(a.ws.mmat) + u * C * CP;
     const T* kgt = reinterpret_cast<const T*>(a.ws.kgt) + u * DK * CP;
-    const float* ut = a.ws.ut + u * DV * C;
+    const T* ut = reinterpret_cast<const T*>(a.ws.ut) + u * DV * C;
     const float* dec = a.ws.decay + u * DK;
     if constexpr (!PERKEY) op.dec0 = dec[0];  // one value per chunk (uniform address)
 #pragma unroll
@@ -678,8 +678,9 @@ __device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY>& op,
 #pragma unroll
             for (int kb = 0; kb < O::NK2; kb++)
                 op.am[r][kb] = MM::load(Frag<T>::ptr(mm, mb, kb, CP, lane));
-            op.u[r] = *reinterpret_cast<const f32x4*>(
-                ut + ((size_t)((vcol0 / 16) * F::NB + mb) * 64 + lane) * 4);
+            float u4[4];
+            load4<T>(ut + ((size_t)((vcol0 / 16) * F::NB + mb) * 64 + lane) * 4, u4);
+            op.u[r] = f32x4{u4[0], u4[1], u4[2], u4[3]};
         }
     }
 #pragma unroll
