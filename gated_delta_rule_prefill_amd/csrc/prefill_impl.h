@@ -21,10 +21,13 @@
 //         the only sequential part. A 16-column slice of the fp32 state lives in MFMA
 //         accumulators across the whole sequence; per chunk
 //           E = U - W S,  O = Q_in S + M E,  S <- Diag(e^{G_C}) S + K_g^T E
-//         with the next chunk's operands prefetched into registers during the current one.
+//         with E and O rows on separate waves and each wave's operands of the next chunk
+//         prefetched into its registers during the current one.
 //         The value tiles of one (sequence, head) are placed on the same XCD so the shared
 //         per-chunk operands are served from that XCD's L2.
 #pragma once
+#include <type_traits>
+
 #include "gdn_common.h"
 #include "gdn_launch.h"
 
@@ -630,82 +633,97 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
 // =====================================================================================
 // scan kernel: the sequential state pass over chunks
 // =====================================================================================
-template <typename T, int DK, int DV, int C, bool PERKEY>
+// One workgroup per (sequence, head, 16-column value tile) with 2 NB waves (NB = C / 16
+// token blocks); each wave keeps one role for the whole sequence:
+//   E wave w < NB      E rows of token block w:        E = U + (-W) S
+//   O wave w >= NB     O rows of token block w - NB:   O = Q_in S + M E
+// and every wave owns state row blocks rb = w + j NWV of the fp32 state slice, updated in
+// its MFMA accumulators: S <- Diag(e^{G_C}) S + K_g^T E.
+// Per chunk: barrier (S^T in LDS) -> E, Q_in S -> barrier (E in LDS) -> M E, state update,
+// S^T back to LDS. Each wave prefetches only its own operands of the next chunk into
+// registers (-W and U, or Q_in and M, plus its K_g^T rows): a single wave pulls only a
+// small share of a CU's vector-memory bandwidth, so the per-chunk operand stream is spread
+// over all waves of the workgroup.
+#ifndef SCAN_GROUP
+#define SCAN_GROUP 1
+#endif
+
+template <int C>
+struct ScanShape {
+    static constexpr int NB = C / 16;
+    static constexpr int NWV = 2 * NB;
+    static constexpr int THREADS = NWV * WAVE;
+};
+
+template <typename T, int DK, int DV, int C, bool PERKEY, bool EROLE>
 struct ScanOps {
     using F = PfCfg<T, DK, DV, C>;
     using frag = typename F::MM::frag;
     static constexpr int NK = F::DKP / F::KB;    // k-steps over (padded) d_k
     static constexpr int NK2 = F::CP / F::KB;    // k-steps over the chunk
-    static constexpr int MBW = (F::NB + PF_WAVES - 1) / PF_WAVES;         // token blocks / wave
-    static constexpr int RBW = (DK / 16 + PF_WAVES - 1) / PF_WAVES;       // state row blocks / wave
-    // every wave owns a full set of blocks: no runtime guard (keeps the loop branch-free,
-    // which lets the compiler wait only for the operands it needs, not for the prefetch)
-    static constexpr bool MB_FULL = F::NB % PF_WAVES == 0;
-    static constexpr bool RB_FULL = (DK / 16) % PF_WAVES == 0;
-    frag aw[MBW][NK];   // -W rows
-    frag aq[MBW][NK];   // Q_in rows
-    frag am[MBW][NK2];  // M rows
-    frag ak[RBW][NK2];  // K_g^T rows
-    f32x4 u[MBW];       // U^T slice in accumulator layout
-    f32x4 dec[PERKEY ? RBW : 1];  // per key: e^{G_C} for the lane's 4 state rows
-    float dec0;                   // scalar gate: e^{G_C}
+    static constexpr int NWV = ScanShape<C>::NWV;
+    static constexpr int RB = DK / 16;
+    static constexpr int RBW = (RB + NWV - 1) / NWV;   // state row blocks per wave
+    // with RB a multiple of the wave count every wave owns full row blocks and the loop
+    // stays branch-free (the compiler then waits only for the operands it needs)
+    static constexpr bool RB_FULL = RB % NWV == 0;
+    frag a[NK];                    // -W rows (E wave) or Q_in rows (O wave)
+    frag am[EROLE ? 1 : NK2];      // M rows (O wave)
+    f32x4 u;                       // U of the token block, accumulator layout (E wave)
+    frag ak[RBW][NK2];             // K_g^T rows of the wave's state row blocks
+    f32x4 dec[PERKEY ? RBW : 1];   // per key: e^{G_C} of the lane's 4 state rows
+    float dec0;                    // scalar gate: e^{G_C}
 };
 
-template <typename T, int DK, int DV, int C, bool PERKEY>
-__device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY>& op,
-                                              const PrefillArgs& a, size_t u, int vcol0) {
-    using O = ScanOps<T, DK, DV, C, PERKEY>;
+template <typename T, int DK, int DV, int C, bool PERKEY, bool EROLE>
+__device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROLE>& op,
+                                              const PrefillArgs& a, size_t u, int vcol0,
+                                              int mb, int w) {
+    using O = ScanOps<T, DK, DV, C, PERKEY, EROLE>;
     using F = PfCfg<T, DK, DV, C>;
     using MM = typename F::MM;
     constexpr int CP = F::CP;
-    const int lane = lane_id(), w = wave_id();
-    const T* wneg = reinterpret_cast<const T*>(a.ws.wneg) + u * C * F::DKP;
-    const T* qin = reinterpret_cast<const T*>(a.ws.qin) + u * C * F::DKP;
-    const T* mm = reinterpret_cast<const T*>(a.ws.mmat) + u * C * CP;
-    const T* kgt = reinterpret_cast<const T*>(a.ws.kgt) + u * DK * CP;
-    const T* ut = reinterpret_cast<const T*>(a.ws.ut) + u * DV * C;
+    const int lane = lane_id();
     const float* dec = a.ws.decay + u * DK;
-    if constexpr (!PERKEY) op.dec0 = dec[0];  // one value per chunk (uniform address)
+    if constexpr (!PERKEY) op.dec0 = dec[0];
+    if constexpr (EROLE) {
+        const T* wneg = reinterpret_cast<const T*>(a.ws.wneg) + u * C * F::DKP;
+        const T* ut = reinterpret_cast<const T*>(a.ws.ut) + u * DV * C;
 #pragma unroll
-    for (int r = 0; r < O::MBW; r++) {
-        const int mb = w + r * PF_WAVES;
-        if (O::MB_FULL || mb < F::NB) {
+        for (int kb = 0; kb < O::NK; kb++) op.a[kb] = MM::load(Frag<T>::ptr(wneg, mb, kb, F::DKP, lane));
+        float u4[4];
+        load4<T>(ut + ((size_t)((vcol0 / 16) * F::NB + mb) * 64 + lane) * 4, u4);
+        op.u = f32x4{u4[0], u4[1], u4[2], u4[3]};
+    } else {
+        const T* qin = reinterpret_cast<const T*>(a.ws.qin) + u * C * F::DKP;
+        const T* mm = reinterpret_cast<const T*>(a.ws.mmat) + u * C * CP;
 #pragma unroll
-            for (int kb = 0; kb < O::NK; kb++) {
-                op.aw[r][kb] = MM::load(Frag<T>::ptr(wneg, mb, kb, F::DKP, lane));
-                op.aq[r][kb] = MM::load(Frag<T>::ptr(qin, mb, kb, F::DKP, lane));
-            }
+        for (int kb = 0; kb < O::NK; kb++) op.a[kb] = MM::load(Frag<T>::ptr(qin, mb, kb, F::DKP, lane));
 #pragma unroll
-            for (int kb = 0; kb < O::NK2; kb++)
-                op.am[r][kb] = MM::load(Frag<T>::ptr(mm, mb, kb, CP, lane));
-            float u4[4];
-            load4<T>(ut + ((size_t)((vcol0 / 16) * F::NB + mb) * 64 + lane) * 4, u4);
-            op.u[r] = f32x4{u4[0], u4[1], u4[2], u4[3]};
-        }
+        for (int kt = 0; kt < O::NK2; kt++) op.am[kt] = MM::load(Frag<T>::ptr(mm, mb, kt, CP, lane));
     }
+    const T* kgt = reinterpret_cast<const T*>(a.ws.kgt) + u * DK * CP;
 #pragma unroll
-    for (int r = 0; r < O::RBW; r++) {
-        const int rb = w + r * PF_WAVES;
-        if (O::RB_FULL || rb < DK / 16) {
+    for (int j = 0; j < O::RBW; j++) {
+        const int rb = w + j * O::NWV;
+        if (O::RB_FULL || rb < O::RB) {
 #pragma unroll
-            for (int kb = 0; kb < O::NK2; kb++)
-                op.ak[r][kb] = MM::load(Frag<T>::ptr(kgt, rb, kb, CP, lane));
+            for (int kt = 0; kt < O::NK2; kt++)
+                op.ak[j][kt] = MM::load(Frag<T>::ptr(kgt, rb, kt, CP, lane));
             if constexpr (PERKEY)  // 4 distinct 16-byte words per wave: one cache line
-                op.dec[r] = *reinterpret_cast<const f32x4*>(dec + rb * 16 + (lane >> 4) * 4);
+                op.dec[j] = *reinterpret_cast<const f32x4*>(dec + rb * 16 + (lane >> 4) * 4);
         }
     }
 }
 
-#ifndef GDN_SCAN_PFD
-#define GDN_SCAN_PFD 1
-#endif
-
-template <typename T, int DK, int DV, int C, bool PERKEY, int PFD = GDN_SCAN_PFD>
-__global__ __launch_bounds__(PF_THREADS) void prefill_scan_kernel(PrefillArgs a) {
+template <typename T, int DK, int DV, int C, bool PERKEY>
+__global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(PrefillArgs a) {
     using F = PfCfg<T, DK, DV, C>;
     using MM = typename F::MM;
-    using O = ScanOps<T, DK, DV, C, PERKEY>;
-    constexpr int KB = F::KB, KPL = F::KPL, CP = F::CP;
+    constexpr int KB = F::KB, KPL = F::KPL, CP = F::CP, NB = F::NB;
+    constexpr int NWV = ScanShape<C>::NWV, THREADS = ScanShape<C>::THREADS;
+    constexpr int RB = DK / 16, RBW = (RB + NWV - 1) / NWV;
+    constexpr bool RB_FULL = RB % NWV == 0;
     constexpr int NVT = DV / SCAN_BV;
     __shared__ __align__(16) T st[SCAN_BV][F::LDK];   // S^T slice (MFMA B operand)
     __shared__ __align__(16) T et[SCAN_BV][F::LDC];   // E^T slice
@@ -718,7 +736,8 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_scan_kernel(PrefillArgs a)
     const int H = a.H;
     if (unit >= a.n_seqs * H) return;
     const int n = unit / H, h = unit - (unit / H) * H;
-    const int lane = lane_id(), w = wave_id(), r16 = lane & 15, kq = (lane >> 4) * KPL;
+    const int lane = lane_id(), w = wave_id(), r16 = lane & 15, g = lane >> 4;
+    const int kq = g * KPL;
     const int vcol0 = vt * SCAN_BV;
     // clamps keep inconsistent cu_seqlens inside the workspace and the token range
     const int c_begin = a.ws.seq_first[n];
@@ -729,139 +748,125 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_scan_kernel(PrefillArgs a)
     const bool init = valid && a.has_init != nullptr && a.has_init[n] != 0;
     float* S = valid ? a.state_pool + ((size_t)slot * H + h) * DK * DV : nullptr;
 
-    // state slice in accumulators: acc_s[r][e] = S[rb*16 + 4*(lane>>4) + e][vcol0 + r16]
-    f32x4 acc_s[O::RBW];
+    // state slice in accumulators: acc_s[j][e] = S[16 rb + 4 g + e][vcol0 + r16], rb = w + j NWV
+    f32x4 acc_s[RBW];
 #pragma unroll
-    for (int r = 0; r < O::RBW; r++) {
-        acc_s[r] = zero4();
-        const int rb = w + r * PF_WAVES;
-        if (rb < DK / 16) {
+    for (int j = 0; j < RBW; j++) {
+        acc_s[j] = zero4();
+        const int rb = w + j * NWV;
+        if (rb < RB) {
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const int row = rb * 16 + (lane >> 4) * 4 + e;
-                acc_s[r][e] = init ? S[(size_t)row * DV + vcol0 + r16] : 0.f;
-                st[r16][row] = from_f32<T>(acc_s[r][e]);
+                const int row = rb * 16 + 4 * g + e;
+                acc_s[j][e] = init ? S[(size_t)row * DV + vcol0 + r16] : 0.f;
+                st[r16][row] = from_f32<T>(acc_s[j][e]);
             }
         }
     }
     if constexpr (CP > C) {
-        for (int idx = threadIdx.x; idx < SCAN_BV * (CP - C); idx += PF_THREADS)
+        for (int idx = threadIdx.x; idx < SCAN_BV * (CP - C); idx += THREADS)
             et[idx / (CP - C)][C + idx % (CP - C)] = from_f32<T>(0.f);
     }
     if constexpr (F::DKP > DK) {  // padded state rows stay zero
-        for (int idx = threadIdx.x; idx < SCAN_BV * (F::DKP - DK); idx += PF_THREADS)
+        for (int idx = threadIdx.x; idx < SCAN_BV * (F::DKP - DK); idx += THREADS)
             st[idx / (F::DKP - DK)][DK + idx % (F::DKP - DK)] = from_f32<T>(0.f);
     }
 
     T* out = reinterpret_cast<T*>(a.o);
-    T* dump = reinterpret_cast<T*>(a.ws.dump) + threadIdx.x;
-    // one chunk of the sequential pass, operands already in registers
-    auto chunk_step = [&](const O& cur, int c) {
-        const int tok0 = t_begin + (c - c_begin) * C;
-        const int len = min(C, t_end - tok0);
-        lds_barrier();  // st holds S_0 of this chunk
-        f32x4 acc_o[O::MBW];
+    T* dump = reinterpret_cast<T*>(a.ws.dump) + lane;
+
+    // the sequential pass for one role; both roles meet the same two barriers per chunk
+    auto run = [&](auto role) {
+        constexpr bool E = decltype(role)::value;
+        using O = ScanOps<T, DK, DV, C, PERKEY, E>;
+        const int mb = E ? w : w - NB;
+        auto update_state = [&](const O& cur) {  // after the E barrier
 #pragma unroll
-        for (int r = 0; r < O::MBW; r++) {
-            const int mb = w + r * PF_WAVES;
-            acc_o[r] = zero4();
-            if (O::MB_FULL || mb < F::NB) {
-                f32x4 acc_e = cur.u[r];
+            for (int j = 0; j < RBW; j++) {
+                const int rb = w + j * NWV;
+                if (RB_FULL || rb < RB) {
 #pragma unroll
-                for (int kb = 0; kb < O::NK; kb++) {
-                    auto fb = MM::load(&st[r16][kb * KB + kq]);
-                    acc_e = MM::mma(cur.aw[r][kb], fb, acc_e);        // U - W S
-                    acc_o[r] = MM::mma(cur.aq[r][kb], fb, acc_o[r]);  // Q_in S
+                    for (int e = 0; e < 4; e++)
+                        acc_s[j][e] *= PERKEY ? cur.dec[PERKEY ? j : 0][e] : cur.dec0;
+#pragma unroll
+                    for (int kt = 0; kt < O::NK2; kt++) {
+                        auto fb = MM::load(&et[r16][kt * KB + kq]);
+                        acc_s[j] = MM::mma(cur.ak[j][kt], fb, acc_s[j]);  // + K_g^T E
+                    }
+                    float sv[4] = {acc_s[j][0], acc_s[j][1], acc_s[j][2], acc_s[j][3]};
+                    store4<T>(&st[r16][rb * 16 + 4 * g], sv);
                 }
-#pragma unroll
-                for (int e = 0; e < 4; e++) et[r16][mb * 16 + (lane >> 4) * 4 + e] = from_f32<T>(acc_e[e]);
             }
-        }
-        lds_barrier();  // et holds E
+        };
+        auto step = [&](const O& cur, int c) {
+            lds_barrier();  // st holds S_c^T
+            f32x4 acc = E ? cur.u : zero4();
 #pragma unroll
-        for (int r = 0; r < O::MBW; r++) {
-            const int mb = w + r * PF_WAVES;
-            if (O::MB_FULL || mb < F::NB) {
+            for (int kb = 0; kb < O::NK; kb++) {
+                auto fb = MM::load(&st[r16][kb * KB + kq]);
+                acc = MM::mma(cur.a[kb], fb, acc);  // E: U - W S;  O: Q_in S
+            }
+            if constexpr (E) {
+                float ev[4] = {acc[0], acc[1], acc[2], acc[3]};
+                store4<T>(&et[r16][mb * 16 + 4 * g], ev);
+            }
+            lds_barrier();  // et holds E_c
+            if constexpr (!E) {
 #pragma unroll
-                for (int kb = 0; kb < O::NK2; kb++) {
-                    auto fb = MM::load(&et[r16][kb * KB + kq]);
-                    acc_o[r] = MM::mma(cur.am[r][kb], fb, acc_o[r]);  // + M E
+                for (int kt = 0; kt < O::NK2; kt++) {
+                    auto fb = MM::load(&et[r16][kt * KB + kq]);
+                    acc = MM::mma(cur.am[kt], fb, acc);  // + M E
                 }
+                const int tok0 = t_begin + (c - c_begin) * C;
+                const int len = min(C, t_end - tok0);
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     // tokens past the sequence end go to a scratch word instead of a branch
-                    const int i = mb * 16 + (lane >> 4) * 4 + e;
+                    const int i = mb * 16 + 4 * g + e;
                     T* dst = i < len ? out + ((size_t)(tok0 + i) * H + h) * DV + vcol0 + r16 : dump;
-                    *dst = from_f32<T>(acc_o[r][e]);
+                    *dst = from_f32<T>(acc[e]);
                 }
             }
-        }
+            update_state(cur);
+        };
+        // Chunks go in groups of G: the operands of the next group are loaded while the
+        // current group is computed, so a load has G chunk times to arrive (the per-chunk
+        // time is otherwise bound by the memory latency). Prefetch indices are clamped to the
+        // last chunk so every load is unconditional.
+        constexpr int G = SCAN_GROUP;
+        const int clast = c_end - 1;
+        auto ld = [&](O (&ops)[G], int c) {
 #pragma unroll
-        for (int r = 0; r < O::RBW; r++) {
-            const int rb = w + r * PF_WAVES;
-            if (O::RB_FULL || rb < DK / 16) {
+            for (int i = 0; i < G; i++)
+                scan_load_ops<T, DK, DV, C, PERKEY, E>(ops[i], a, (size_t)min(c + i, clast) * H + h,
+                                                       vcol0, mb, w);
+        };
+        O opa[G], opb[G];
+        ld(opa, c_begin);
+        for (int c = c_begin; c < c_end; c += 2 * G) {
+            ld(opb, c + G);
 #pragma unroll
-                for (int e = 0; e < 4; e++) acc_s[r][e] *= PERKEY ? cur.dec[PERKEY ? r : 0][e] : cur.dec0;
+            for (int i = 0; i < G; i++)
+                if (c + i < c_end) step(opa[i], c + i);
+            if (c + G >= c_end) break;
+            ld(opa, c + 2 * G);
 #pragma unroll
-                for (int kb = 0; kb < O::NK2; kb++) {
-                    auto fb = MM::load(&et[r16][kb * KB + kq]);
-                    acc_s[r] = MM::mma(cur.ak[r][kb], fb, acc_s[r]);  // + K_g^T E
-                }
-#pragma unroll
-                for (int e = 0; e < 4; e++) st[r16][rb * 16 + (lane >> 4) * 4 + e] = from_f32<T>(acc_s[r][e]);
-            }
+            for (int i = 0; i < G; i++)
+                if (c + G + i < c_end) step(opb[i], c + G + i);
         }
     };
-    // Operand prefetch over the chunk sequence. PFD = prefetch distance in chunks: 0 loads a
-    // chunk's operands right before it is computed (fewest registers, latency hidden by other
-    // resident workgroups), 1 and 2 keep 2 or 3 rotating operand sets so the loads for chunk
-    // c+PFD are in flight while chunk c is computed. Prefetch indices are clamped to the last
-    // chunk so every load is unconditional.
     if (c_begin < c_end) {
-        const int clast = c_end - 1;
-        auto ld = [&](O& op, int c) {
-            scan_load_ops<T, DK, DV, C, PERKEY>(op, a, (size_t)min(c, clast) * H + h, vcol0);
-        };
-        if constexpr (PFD == 0) {
-            O op0;
-            for (int c = c_begin; c < c_end; c++) {
-                ld(op0, c);
-                chunk_step(op0, c);
-            }
-        } else if constexpr (PFD == 1) {
-            O op0, op1;
-            ld(op0, c_begin);
-            for (int c = c_begin; c < c_end; c += 2) {
-                ld(op1, c + 1);
-                chunk_step(op0, c);
-                if (c + 1 >= c_end) break;
-                ld(op0, c + 2);
-                chunk_step(op1, c + 1);
-            }
-        } else {
-            O op0, op1, op2;
-            ld(op0, c_begin);
-            ld(op1, c_begin + 1);
-            for (int c = c_begin; c < c_end; c += 3) {
-                ld(op2, c + 2);
-                chunk_step(op0, c);
-                if (c + 1 >= c_end) break;
-                ld(op0, c + 3);
-                chunk_step(op1, c + 1);
-                if (c + 2 >= c_end) break;
-                ld(op1, c + 4);
-                chunk_step(op2, c + 2);
-            }
-        }
+        if (w < NB) run(std::integral_constant<bool, true>());
+        else run(std::integral_constant<bool, false>());
     }
     if (valid) {
 #pragma unroll
-        for (int r = 0; r < O::RBW; r++) {
-            const int rb = w + r * PF_WAVES;
-            if (rb < DK / 16) {
+        for (int j = 0; j < RBW; j++) {
+            const int rb = w + j * NWV;
+            if (rb < RB) {
 #pragma unroll
                 for (int e = 0; e < 4; e++)
-                    S[(size_t)(rb * 16 + (lane >> 4) * 4 + e) * DV + vcol0 + r16] = acc_s[r][e];
+                    S[(size_t)(rb * 16 + 4 * g + e) * DV + vcol0 + r16] = acc_s[j][e];
             }
         }
     }
@@ -894,7 +899,7 @@ hipError_t prefill_launch_cfg(const PrefillArgs& a, hipStream_t s) {
     const int nvt = D / SCAN_BV;
     const int grid = ((units + 7) / 8) * 8 * nvt;
     hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY>), dim3((unsigned)grid),
-                       dim3(PF_THREADS), 0, s, a);
+                       dim3(ScanShape<C>::THREADS), 0, s, a);
     return hipGetLastError();
 }
 
