@@ -8,13 +8,13 @@
 // bound by the state stream, about 0.5 flop/byte), §2.1-2.4 (base + log, Algorithm 1,
 // Eqs. 4-7), §2.6 (one writer for the shared log metadata).
 //
-// Design (MI355X): one 256-thread workgroup owns one (request, head) state, d_k x d_v fp32
-// (64 KiB at d = 128). Each thread holds 4 adjacent value columns of d_k / (256 / (d_v/4))
+// Design (MI355X): one 512-thread workgroup owns one (request, head) state, d_k x d_v fp32
+// (64 KiB at d = 128). Each thread holds 4 adjacent value columns of d_k / (512 / (d_v/4))
 // rows in registers, so the state is read from HBM once, both column reductions
 // (vhat = Sbar^T k and Sbar^T q) come from the same registers, and the update is written
-// back once with 16-byte coalesced accesses along d_v. Reductions: xor-shuffles inside a
-// wave, one LDS exchange across the 4 waves. With B*H workgroups (4096 at B = 128, H = 32)
-// every CU keeps several 64 KiB streams in flight. Because one workgroup covers the whole
+// back once with 16-byte coalesced, non-temporal accesses along d_v. Reductions:
+// xor-shuffles inside a wave, one LDS exchange across the 8 waves. With B*H workgroups
+// (4096 at B = 128, H = 32) every CU keeps several 64 KiB streams in flight. Because one workgroup covers the whole
 // value range, the DeltaLog key-side replay coefficients are computed once per
 // (request, head) in-workgroup and a single thread is the one writer of K_log, Lambda_log,
 // lbar and L — no separate replay-prep launch and no scratch buffer.
@@ -24,18 +24,29 @@
 namespace gdn {
 
 constexpr float L2_EPS = 1e-6f;
-constexpr int DEC_THREADS = 256;
+constexpr int DEC_THREADS = 256;        // DeltaLog kernels
+constexpr int DENSE_THREADS = 512;      // dense decode: more state rows in flight per workgroup
 constexpr int DL_MAXLOG = 16;  // M - 1 <= 16
 
-template <int DK, int DV>
+template <int DK, int DV, int NT = DEC_THREADS>
 struct DecGeom {
     static constexpr int TPR = DV / 4;                 // threads per state row
-    static constexpr int RPP = DEC_THREADS / TPR;      // rows per pass
+    static constexpr int RPP = NT / TPR;               // rows per pass
     static constexpr int NP = (DK + RPP - 1) / RPP;    // passes
-    static constexpr int NWAVE = DEC_THREADS / WAVE;
+    static constexpr int NWAVE = NT / WAVE;
     // lanes of a wave that hold the same column group
     static constexpr int ROWS_PER_WAVE = WAVE / TPR;
 };
+
+// The state is touched exactly once per step: streamed with non-temporal loads and stores
+// so it does not displace other lines from the caches (measured: the state update runs
+// closer to the HBM rate this way).
+__device__ __forceinline__ f32x4 stream_load(const float* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+__device__ __forceinline__ void stream_store(float* p, f32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
 
 // Shared prologue: stage k, q (fp32, optionally L2-normalised), v, and per-key decay in
 // LDS; every wave computes the norms itself to avoid an extra barrier.
@@ -45,8 +56,8 @@ struct DecSmem {
     float q[DK];
     float v[DV];
     float gk[DK];
-    float red_v[DecGeom<DK, DV>::NWAVE][DV];
-    float red_q[DecGeom<DK, DV>::NWAVE][DV];
+    float red_v[DecGeom<DK, DV, DENSE_THREADS>::NWAVE][DV];
+    float red_q[DecGeom<DK, DV, DENSE_THREADS>::NWAVE][DV];
     float r[DV];
 };
 
@@ -76,8 +87,8 @@ __device__ __forceinline__ void kq_norms(const float* ks, const float* qs, float
 }
 
 template <typename T, int DK, int DV, bool PERKEY>
-__global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecodeArgs a) {
-    using G = DecGeom<DK, DV>;
+__global__ __launch_bounds__(DENSE_THREADS) void decode_kernel(DecodeArgs a) {
+    using G = DecGeom<DK, DV, DENSE_THREADS>;
     __shared__ DecSmem<T, DK, DV> sm;
     const int tid = threadIdx.x;
     const int H = a.H;
@@ -101,7 +112,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int p = 0; p < G::NP; p++) {
         const int r = r0 + p * G::RPP;
-        if (r < DK) st[p] = *reinterpret_cast<const f32x4*>(S + (size_t)r * DV + cg * 4);
+        if (r < DK) st[p] = stream_load(S + (size_t)r * DV + cg * 4);
     }
     const T* qp = reinterpret_cast<const T*>(a.q) + (size_t)bh * DK;
     const T* kp = reinterpret_cast<const T*>(a.k) + (size_t)bh * DK;
@@ -178,7 +189,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecodeArgs a) {
             f32x4 s = st[p];
 #pragma unroll
             for (int i = 0; i < 4; i++) s[i] += kr[p] * rr[i];
-            *reinterpret_cast<f32x4*>(S + (size_t)r * DV + cg * 4) = s;
+            stream_store(S + (size_t)r * DV + cg * 4, s);
         }
     }
 }
@@ -190,19 +201,19 @@ struct DlSmem {
     float q[DK];
     float v[DV];
     float klog[DL_MAXLOG][DK];
-    float ulog[DL_MAXLOG][DV];
+    alignas(16) float ulog[DL_MAXLOG][DV];
     float lam[DL_MAXLOG];
     float ck[DL_MAXLOG];  // e^{lp - Lambda_i} (k . K_i)
     float cq[DL_MAXLOG];  // e^{lp - Lambda_i} (q . K_i)
     float wl[DL_MAXLOG];  // e^{lp - Lambda_i}
-    float red_v[DecGeom<DK, DV>::NWAVE][DV];
-    float red_q[DecGeom<DK, DV>::NWAVE][DV];
+    float red_v[DecGeom<DK, DV, DENSE_THREADS>::NWAVE][DV];
+    float red_q[DecGeom<DK, DV, DENSE_THREADS>::NWAVE][DV];
     float b[DV];
 };
 
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(DEC_THREADS) void deltalog_kernel(DeltaLogArgs a) {
-    using G = DecGeom<DK, DV>;
+__global__ __launch_bounds__(DENSE_THREADS) void deltalog_kernel(DeltaLogArgs a) {
+    using G = DecGeom<DK, DV, DENSE_THREADS>;
     __shared__ DlSmem<DK, DV> sm;
     const int tid = threadIdx.x;
     const int H = a.H;
@@ -226,7 +237,7 @@ __global__ __launch_bounds__(DEC_THREADS) void deltalog_kernel(DeltaLogArgs a) {
 #pragma unroll
     for (int p = 0; p < G::NP; p++) {
         const int r = r0 + p * G::RPP;
-        if (r < DK) st[p] = *reinterpret_cast<const f32x4*>(S + (size_t)r * DV + cg * 4);
+        if (r < DK) st[p] = stream_load(S + (size_t)r * DV + cg * 4);
     }
     // clamp so that corrupted metadata can never index past the log buffers
     const int L = min(max(a.len[sh], 0), C);
@@ -241,11 +252,11 @@ __global__ __launch_bounds__(DEC_THREADS) void deltalog_kernel(DeltaLogArgs a) {
     if (tid < DV) sm.v[tid] = to_f32(vp[tid]);
     const uint16_t* kl = a.klog + sh * C * DK;
     const float* ul = a.ulog + sh * C * DV;
-    for (int i = tid; i < L * DK; i += DEC_THREADS) {
+    for (int i = tid; i < L * DK; i += DENSE_THREADS) {
         uint32_t bits = (uint32_t)kl[i] << 16;
         sm.klog[i / DK][i % DK] = __builtin_bit_cast(float, bits);
     }
-    for (int i = tid; i < L * DV; i += DEC_THREADS) sm.ulog[i / DV][i % DV] = ul[i];
+    for (int i = tid; i < L * DV; i += DENSE_THREADS) sm.ulog[i / DV][i % DV] = ul[i];
     if (tid < L) {
         float lam = a.lamlog[sh * C + tid];
         sm.lam[tid] = lam;
@@ -340,7 +351,9 @@ __global__ __launch_bounds__(DEC_THREADS) void deltalog_kernel(DeltaLogArgs a) {
         }
         return;
     }
-    // merge (Eq. 6): fold the log and the current update into the base, clear the log
+    // merge (Eq. 6): fold the log and the current update into the base, clear the log.
+    // Entry-outer order: each entry's 4 value columns of this thread are read from LDS once
+    // and applied to all of the thread's rows.
     lds_barrier();
     float bb[4];
 #pragma unroll
@@ -349,17 +362,28 @@ __global__ __launch_bounds__(DEC_THREADS) void deltalog_kernel(DeltaLogArgs a) {
     for (int p = 0; p < G::NP; p++) {
         const int r = r0 + p * G::RPP;
         if (r < DK) {
-            f32x4 s = st[p];
             const float kk = sm.k[r] * ik;
 #pragma unroll
-            for (int i = 0; i < 4; i++) s[i] = s[i] * dec + kk * bb[i];
-            for (int e = 0; e < L; e++) {
-                const float we = sm.wl[e] * sm.klog[e][r];
-#pragma unroll
-                for (int i = 0; i < 4; i++) s[i] += we * sm.ulog[e][cg * 4 + i];
-            }
-            *reinterpret_cast<f32x4*>(S + (size_t)r * DV + cg * 4) = s;
+            for (int i = 0; i < 4; i++) st[p][i] = st[p][i] * dec + kk * bb[i];
         }
+    }
+    for (int e = 0; e < L; e++) {
+        const f32x4 ue = *reinterpret_cast<const f32x4*>(&sm.ulog[e][cg * 4]);
+        const float we = sm.wl[e];
+#pragma unroll
+        for (int p = 0; p < G::NP; p++) {
+            const int r = r0 + p * G::RPP;
+            if (r < DK) {
+                const float c = we * sm.klog[e][r];
+#pragma unroll
+                for (int i = 0; i < 4; i++) st[p][i] += c * ue[i];
+            }
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < G::NP; p++) {
+        const int r = r0 + p * G::RPP;
+        if (r < DK) stream_store(S + (size_t)r * DV + cg * 4, st[p]);
     }
     if (tid == 0) {
         a.lbar[sh] = 0.f;
@@ -423,7 +447,7 @@ __global__ __launch_bounds__(DEC_THREADS) void deltalog_maint_kernel(DeltaLogArg
 // ------------------------------------------------------------------------------- launch
 template <typename T, int D>
 static hipError_t dec_dispatch_gate(const DecodeArgs& a, hipStream_t s) {
-    dim3 grid((unsigned)(a.batch * a.H)), block(DEC_THREADS);
+    dim3 grid((unsigned)(a.batch * a.H)), block(DENSE_THREADS);
     if (a.gate == 1)
         hipLaunchKernelGGL((decode_kernel<T, D, D, true>), grid, block, 0, s, a);
     else
@@ -450,7 +474,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
 
 template <typename T, int D>
 static hipError_t dl_launch(const DeltaLogArgs& a, hipStream_t s) {
-    dim3 grid((unsigned)(a.batch * a.H)), block(DEC_THREADS);
+    dim3 grid((unsigned)(a.batch * a.H)), block(DENSE_THREADS);
     hipLaunchKernelGGL((deltalog_kernel<T, D, D>), grid, block, 0, s, a);
     return hipGetLastError();
 }
