@@ -6,9 +6,10 @@
 // width-1 on the current token, then SiLU; zero history at a sequence start) and
 // "vLLM中Decode的实现" (one convolution over the concatenated q|k|v channels equals three).
 //
-// HBM-bound elementwise pass: each thread produces 8 adjacent channels of one token
-// (16-byte loads/stores for bf16), reading the current and previous width-1 tokens of the
-// same 8 channels (those rows are shared with the neighbouring tokens' threads through L2).
+// HBM-bound elementwise pass: each thread produces 8 adjacent channels (one 16-byte access
+// for bf16) of CONV_TT consecutive tokens, so the width-1 history rows it reads besides its
+// own tokens add (width-1)/CONV_TT to the read traffic. Rows are kept in registers in the
+// input type and widened to fp32 when used.
 #include "gdn_common.h"
 #include "gdn_launch.h"
 
@@ -18,7 +19,25 @@ constexpr int CONV_THREADS = 256;
 
 // Each thread produces 8 adjacent channels of CONV_TT consecutive tokens: the weights are
 // read once (float4 per channel), each x row once, and the window slides in registers.
-constexpr int CONV_TT = 8;
+constexpr int CONV_TT = 16;
+
+// 8 consecutive elements kept in their storage type
+template <typename T> struct Row8;
+template <> struct Row8<bf16> {
+    bf16x8 v;
+    __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+    __device__ __forceinline__ void zero() { v = Mma<bf16>::zero(); }
+    __device__ __forceinline__ float operator[](int i) const { return (float)v[i]; }
+};
+template <> struct Row8<float> {
+    f32x4 lo, hi;
+    __device__ __forceinline__ void load(const float* p) {
+        lo = *reinterpret_cast<const f32x4*>(p);
+        hi = *reinterpret_cast<const f32x4*>(p + 4);
+    }
+    __device__ __forceinline__ void zero() { lo = zero4(); hi = zero4(); }
+    __device__ __forceinline__ float operator[](int i) const { return i < 4 ? lo[i] : hi[i - 4]; }
+};
 
 template <typename T, int W>
 __global__ __launch_bounds__(CONV_THREADS) void conv1d_silu_kernel(ConvArgs a) {
@@ -51,16 +70,12 @@ __global__ __launch_bounds__(CONV_THREADS) void conv1d_silu_kernel(ConvArgs a) {
     const T* x = reinterpret_cast<const T*>(a.x);
     // rows t0-(W-1) .. t0+CONV_TT-1, zero outside [0, total_tokens)
     constexpr int NR = CONV_TT + W - 1;
-    float xr[NR][8];
+    Row8<T> xr[NR];
 #pragma unroll
     for (int r = 0; r < NR; r++) {
         const int src = t0 - (W - 1) + r;
-        if (src >= 0 && src < a.total_tokens) {
-            load8<T>(x + (size_t)src * a.channels + c0, xr[r]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; i++) xr[r][i] = 0.f;
-        }
+        if (src >= 0 && src < a.total_tokens) xr[r].load(x + (size_t)src * a.channels + c0);
+        else xr[r].zero();
     }
     const int pc = a.channels / a.planes;
     const int plane = c0 / pc;

@@ -127,9 +127,17 @@ __device__ __forceinline__ void store4<bf16>(bf16* p, const float in[4]) {
 
 // 8 consecutive elements <-> fp32 (one 16-byte access for bf16, two for fp32)
 template <typename T>
-__device__ __forceinline__ void load8(const T* p, float out[8]) {
-    load4<T>(p, out);
-    load4<T>(p + 4, out + 4);
+__device__ __forceinline__ void load8(const T* p, float out[8]);
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float out[8]) {
+    load4<float>(p, out);
+    load4<float>(p + 4, out + 4);
+}
+template <>
+__device__ __forceinline__ void load8<bf16>(const bf16* p, float out[8]) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; i++) out[i] = (float)v[i];
 }
 template <typename T>
 __device__ __forceinline__ void store8(T* p, const float in[8]);
