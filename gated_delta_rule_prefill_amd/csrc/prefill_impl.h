@@ -114,7 +114,8 @@ struct Frag {
 // One workgroup per (chunk, head); wave w owns token block w (16 tokens) for the row-wise
 // work. Phases (LDS barriers between them):
 //   P0  loads (K, Q, V straight into MFMA row fragments), L2 norm, gate prefix sums
-//   P1  Q_in, K_g^T, (beta K_in)^T via identity-MFMA transposes; A and M tiles
+//   P1  Q_in, K_g^T, (beta K_in)^T via identity-MFMA transposes; A and M tiles of the
+//       wave's own row block (its key and query rows stay in registers)
 //   P2  16x16 leaf inverses of I + A (forward substitution, one lane per column), V^T
 //   P3  2x2 block merges on fp32 MFMA (16 -> 32 -> 64), in place over A
 //   P4  -W and U on MFMA, written to the workspace
@@ -122,20 +123,19 @@ template <typename T, int DK, int DV, int C, bool PERKEY>
 struct PrepSmem {
     using F = PfCfg<T, DK, DV, C>;
     // live for the whole kernel
-    alignas(16) float ar[C][C + 1];   // A (strictly lower), then R = (I + A)^{-1} in place;
-                                      // the strictly upper part is merge scratch
     alignas(16) float bs[C];          // beta
     alignas(16) float eg[C];          // scalar gate: e^{G_i}
     alignas(16) float egc[C];         // scalar gate: e^{G_C - G_i}
     alignas(16) T kint[DK][F::LDC];   // (diag(beta) K_in)^T
     union {
-        struct {                      // P0-P1: keys and queries in fragment-major order
+        struct {                      // P0-P1: keys in fragment-major order, gates
             alignas(16) T ks[C * F::DKP];
-            alignas(16) T qs[C * F::DKP];
             alignas(16) float gs[PERKEY ? C : 1][PERKEY ? DK + 4 : C];  // cumulative log gate
             float gseg[PERKEY ? PF_THREADS / DK : 1][PERKEY ? DK : 1];    // segment totals
         } a;
-        struct {                      // P2-P4
+        struct {                      // from barrier #2 on
+            alignas(16) float ar[C][C + 1];  // A (strictly lower), then R = (I + A)^{-1} in
+                                             // place; the strictly upper part is merge scratch
             alignas(16) T rs[C][F::LDC];     // R as an MFMA operand
             alignas(16) T vt[DV][F::LDC];    // (diag(beta) V)^T
         } b;
@@ -281,13 +281,12 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
             }
         }
     }
-    // keys / queries to LDS in fragment-major order (conflict-free 16-byte accesses)
+    // keys to LDS in fragment-major order (conflict-free 16-byte accesses)
     if (own) {
 #pragma unroll
         for (int kb = 0; kb < NK; kb++) {
             const int off = ((w * NK + kb) * 64 + lane) * KPL;
             *reinterpret_cast<frag*>(&sm.u.a.ks[off]) = kf[kb];
-            *reinterpret_cast<frag*>(&sm.u.a.qs[off]) = qf[kb];
         }
     }
     if (tid < C) sm.bs[tid] = bval;
@@ -318,7 +317,7 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
             sm.egc[lane] = __expf(gC - x);
         }
     }
-    lds_barrier();  // #1: gates, beta, keys, queries in LDS
+    lds_barrier();  // #1: gates, beta, keys in LDS
 
     // --------------------------------------------------- P1a: own token block, row-wise
     frag idf[Ident<T>::N];
@@ -387,75 +386,75 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
     if (tid < DK) a.ws.decay[u * DK + tid] = __expf(gval<PERKEY, DK, C>(sm.u.a.gs, C - 1, tid));
 
     // ------------------------------------------------------- P1b: A and M tiles
+    // Wave w computes the tiles of its own row block (i block w, j blocks <= w): the key and
+    // query rows of block w are its own registers (B operands), only the j-block keys come
+    // from LDS. A is held in registers until the key/gate buffers are dead (barrier #2) and
+    // then written over them.
+    float atile[NB][4];
     {
-        constexpr int NT = NB * (NB + 1) / 2;
         T* mmat = reinterpret_cast<T*>(a.ws.mmat) + u * C * CP;
-        for (int t = w; t < NT; t += PF_WAVES) {
-            int ib = 0, rem = t;  // t -> (jb <= ib)
-            while (rem > ib) {
-                rem -= ib + 1;
-                ib++;
-            }
-            const int jb = rem;
-            const int ref = ib * 16;  // reference token: first of the i block
-            f32x4 accK = zero4(), accQ = zero4();
-            const int jrow = jb * 16 + r16, irow = ib * 16 + r16;
+        if (own) {
+            const int ib = w, ref = ib * 16, irow = row;
 #pragma unroll
-            for (int kb = 0; kb < NK; kb++) {
-                const frag ka = MM::load(&sm.u.a.ks[((jb * NK + kb) * 64 + lane) * KPL]);
-                const frag kbv = MM::load(&sm.u.a.ks[((ib * NK + kb) * 64 + lane) * KPL]);
-                const frag qbv = MM::load(&sm.u.a.qs[((ib * NK + kb) * 64 + lane) * KPL]);
-                frag fa, fbk, fbq;
-                if constexpr (PERKEY) {
+            for (int jb = 0; jb < NB; jb++) {
+                if (jb > ib) continue;
+                f32x4 accK = zero4(), accQ = zero4();
+                const int jrow = jb * 16 + r16;
 #pragma unroll
-                    for (int e = 0; e < KPL; e++) {
-                        const int ch = kb * KB + g4 * KPL + e;
-                        float aj = 0.f, bk = 0.f, bq = 0.f;
-                        if (ch < DK) {  // padded channels contribute zero
-                            const float gr = sm.u.a.gs[ref][ch];
-                            const float fj = __expf(gr - sm.u.a.gs[jrow][ch]);
-                            const float fi = __expf(sm.u.a.gs[irow][ch] - gr);
+                for (int kb = 0; kb < NK; kb++) {
+                    const frag ka = MM::load(&sm.u.a.ks[((jb * NK + kb) * 64 + lane) * KPL]);
+                    frag fa, fbk, fbq;
+                    if constexpr (PERKEY) {
+#pragma unroll
+                        for (int e = 0; e < KPL; e++) {
+                            const int ch = kb * KB + g4 * KPL + e;
+                            float aj = 0.f, bk = 0.f, bq = 0.f;
+                            if (ch < DK) {  // padded channels contribute zero
+                                const float gr = sm.u.a.gs[ref][ch];
+                                const float fj = __expf(gr - sm.u.a.gs[jrow][ch]);
+                                const float fi = __expf(sm.u.a.gs[irow][ch] - gr);
+                                if constexpr (KPL == 1) {
+                                    aj = to_f32(ka) * fj;
+                                    bk = to_f32(kf[kb]) * fi;
+                                    bq = to_f32(qf[kb]) * fi;
+                                } else {
+                                    aj = to_f32(ka[e]) * fj;
+                                    bk = to_f32(kf[kb][e]) * fi;
+                                    bq = to_f32(qf[kb][e]) * fi;
+                                }
+                            }
                             if constexpr (KPL == 1) {
-                                aj = to_f32(ka) * fj;
-                                bk = to_f32(kbv) * fi;
-                                bq = to_f32(qbv) * fi;
+                                fa = from_f32<T>(aj);
+                                fbk = from_f32<T>(bk);
+                                fbq = from_f32<T>(bq);
                             } else {
-                                aj = to_f32(ka[e]) * fj;
-                                bk = to_f32(kbv[e]) * fi;
-                                bq = to_f32(qbv[e]) * fi;
+                                fa[e] = from_f32<T>(aj);
+                                fbk[e] = from_f32<T>(bk);
+                                fbq[e] = from_f32<T>(bq);
                             }
                         }
-                        if constexpr (KPL == 1) {
-                            fa = from_f32<T>(aj);
-                            fbk = from_f32<T>(bk);
-                            fbq = from_f32<T>(bq);
-                        } else {
-                            fa[e] = from_f32<T>(aj);
-                            fbk[e] = from_f32<T>(bk);
-                            fbq[e] = from_f32<T>(bq);
-                        }
+                    } else {
+                        fa = ka;
+                        fbk = kf[kb];
+                        fbq = qf[kb];
                     }
-                } else {
-                    fa = ka;
-                    fbk = kbv;
-                    fbq = qbv;
+                    accK = MM::mma(fa, fbk, accK);
+                    accQ = MM::mma(fa, fbq, accQ);
                 }
-                accK = MM::mma(fa, fbk, accK);
-                accQ = MM::mma(fa, fbq, accQ);
-            }
-            // lane holds D[j = jb*16 + 4*g4 + e][i = ib*16 + r16]
-            const int i = irow;
-            const float gi = PERKEY ? 0.f : sm.u.a.gs[0][i];
-            float mrow[4];
+                // lane holds D[j = jb*16 + 4*g4 + e][i = ib*16 + r16]
+                const int i = irow;
+                const float gi = PERKEY ? 0.f : sm.u.a.gs[0][i];
+                float mrow[4];
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int j = jb * 16 + g4 * 4 + e;
-                float dec = 1.f;
-                if constexpr (!PERKEY) dec = (j <= i) ? __expf(gi - sm.u.a.gs[0][j]) : 0.f;
-                if (j < i) sm.ar[i][j] = sm.bs[i] * accK[e] * dec;
-                mrow[e] = (j <= i) ? a.scale * accQ[e] * dec : 0.f;
+                for (int e = 0; e < 4; e++) {
+                    const int j = jb * 16 + g4 * 4 + e;
+                    float dec = 1.f;
+                    if constexpr (!PERKEY) dec = (j <= i) ? __expf(gi - sm.u.a.gs[0][j]) : 0.f;
+                    atile[jb][e] = sm.bs[i] * accK[e] * dec;
+                    mrow[e] = (j <= i) ? a.scale * accQ[e] * dec : 0.f;
+                }
+                Frag<T>::template store_run<4>(mmat, i, jb * 16 + g4 * 4, CP, mrow);
             }
-            Frag<T>::template store_run<4>(mmat, i, jb * 16 + g4 * 4, CP, mrow);
         }
         // zero the upper tiles and the padding columns of M
         for (int idx = tid; idx < C * (CP / 4); idx += PF_THREADS) {
@@ -466,7 +465,19 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
             }
         }
     }
-    lds_barrier();  // #2: A complete; keys, queries and gates are dead from here on
+    lds_barrier();  // #2: keys and gates are dead from here on
+    if (own) {
+#pragma unroll
+        for (int jb = 0; jb < NB; jb++) {
+            if (jb > w) continue;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int j = jb * 16 + g4 * 4 + e;
+                if (j < row) sm.u.b.ar[row][j] = atile[jb][e];
+            }
+        }
+    }
+    lds_barrier();  // #2b: A in place
 
     // ------------------------------------------- P2: leaf inverses, V^T, R zero padding
     if (w == 0) {
@@ -479,7 +490,7 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
 #pragma unroll
             for (int r = 1; r < 16; r++)
 #pragma unroll
-                for (int kk = 0; kk < r; kk++) av[r][kk] = sm.ar[b0 + r][b0 + kk];
+                for (int kk = 0; kk < r; kk++) av[r][kk] = sm.u.b.ar[b0 + r][b0 + kk];
             float x[16];
 #pragma unroll
             for (int r = 0; r < 16; r++) x[r] = (r == col) ? 1.f : 0.f;
@@ -492,7 +503,7 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
             }
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                sm.ar[b0 + r][b0 + col] = x[r];
+                sm.u.b.ar[b0 + r][b0 + col] = x[r];
                 sm.u.b.rs[b0 + r][b0 + col] = from_f32<T>(x[r]);
             }
         }
@@ -536,17 +547,17 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
 #pragma unroll
             for (int s4 = 0; s4 < 4; s4++) {
                 const int k = 4 * g4 + s4;
-                t1 = Mma<float>::mma(sm.ar[hi + r16][lo + k], sm.ar[lo + k][lo + r16], t1);
+                t1 = Mma<float>::mma(sm.u.b.ar[hi + r16][lo + k], sm.u.b.ar[lo + k][lo + r16], t1);
             }
             f32x4 rr = zero4();
 #pragma unroll
             for (int s4 = 0; s4 < 4; s4++) {
                 const int k = 4 * g4 + s4;
-                rr = Mma<float>::mma(sm.ar[hi + r16][hi + k], t1[s4], rr);
+                rr = Mma<float>::mma(sm.u.b.ar[hi + r16][hi + k], t1[s4], rr);
             }
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                sm.ar[hi + 4 * g4 + e][lo + r16] = -rr[e];
+                sm.u.b.ar[hi + 4 * g4 + e][lo + r16] = -rr[e];
                 sm.u.b.rs[hi + 4 * g4 + e][lo + r16] = from_f32<T>(-rr[e]);
             }
         }
@@ -561,23 +572,23 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
         for (int kb = 0; kb < 8; kb++) {
             const int k = 4 * kb + g4;
             // R[k][col] is zero above the diagonal blocks (that part of ar was never written)
-            const float rb = (tc == 1 && k < 16) ? 0.f : sm.ar[k][16 * tc + r16];
-            t2 = Mma<float>::mma(sm.ar[32 + 16 * tr + r16][k], rb, t2);
+            const float rb = (tc == 1 && k < 16) ? 0.f : sm.u.b.ar[k][16 * tc + r16];
+            t2 = Mma<float>::mma(sm.u.b.ar[32 + 16 * tr + r16][k], rb, t2);
         }
 #pragma unroll
-        for (int e = 0; e < 4; e++) sm.ar[16 * tr + 4 * g4 + e][32 + 16 * tc + r16] = t2[e];
+        for (int e = 0; e < 4; e++) sm.u.b.ar[16 * tr + 4 * g4 + e][32 + 16 * tc + r16] = t2[e];
         lds_barrier();  // #5
         f32x4 rr = zero4();
 #pragma unroll
         for (int kb = 0; kb < 8; kb++) {
             const int k = 4 * kb + g4;
-            const float ra = (tr == 0 && k >= 16) ? 0.f : sm.ar[32 + 16 * tr + r16][32 + k];
-            rr = Mma<float>::mma(ra, sm.ar[k][32 + 16 * tc + r16], rr);
+            const float ra = (tr == 0 && k >= 16) ? 0.f : sm.u.b.ar[32 + 16 * tr + r16][32 + k];
+            rr = Mma<float>::mma(ra, sm.u.b.ar[k][32 + 16 * tc + r16], rr);
         }
         // the A quarter ar[32:64, 0:32] was last read before barrier #5: overwrite with R_21
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            sm.ar[32 + 16 * tr + 4 * g4 + e][16 * tc + r16] = -rr[e];
+            sm.u.b.ar[32 + 16 * tr + 4 * g4 + e][16 * tc + r16] = -rr[e];
             sm.u.b.rs[32 + 16 * tr + 4 * g4 + e][16 * tc + r16] = from_f32<T>(-rr[e]);
         }
     }
