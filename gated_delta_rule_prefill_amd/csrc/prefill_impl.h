@@ -655,10 +655,6 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
 // registers (-W and U, or Q_in and M, plus its K_g^T rows): a single wave pulls only a
 // small share of a CU's vector-memory bandwidth, so the per-chunk operand stream is spread
 // over all waves of the workgroup.
-#ifndef SCAN_GROUP
-#define SCAN_GROUP 1
-#endif
-
 template <int C>
 struct ScanShape {
     static constexpr int NB = C / 16;
@@ -666,7 +662,7 @@ struct ScanShape {
     static constexpr int THREADS = NWV * WAVE;
 };
 
-template <typename T, int DK, int DV, int C, bool PERKEY, bool EROLE>
+template <typename T, int DK, int DV, int C, bool PERKEY, bool EROLE, int NVB>
 struct ScanOps {
     using F = PfCfg<T, DK, DV, C>;
     using frag = typename F::MM::frag;
@@ -680,17 +676,17 @@ struct ScanOps {
     static constexpr bool RB_FULL = RB % NWV == 0;
     frag a[NK];                    // -W rows (E wave) or Q_in rows (O wave)
     frag am[EROLE ? 1 : NK2];      // M rows (O wave)
-    f32x4 u;                       // U of the token block, accumulator layout (E wave)
+    f32x4 u[NVB];                  // U of the token block per value tile (E wave)
     frag ak[RBW][NK2];             // K_g^T rows of the wave's state row blocks
     f32x4 dec[PERKEY ? RBW : 1];   // per key: e^{G_C} of the lane's 4 state rows
     float dec0;                    // scalar gate: e^{G_C}
 };
 
-template <typename T, int DK, int DV, int C, bool PERKEY, bool EROLE>
-__device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROLE>& op,
+template <typename T, int DK, int DV, int C, bool PERKEY, bool EROLE, int NVB>
+__device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROLE, NVB>& op,
                                               const PrefillArgs& a, size_t u, int vcol0,
                                               int mb, int w) {
-    using O = ScanOps<T, DK, DV, C, PERKEY, EROLE>;
+    using O = ScanOps<T, DK, DV, C, PERKEY, EROLE, NVB>;
     using F = PfCfg<T, DK, DV, C>;
     using MM = typename F::MM;
     constexpr int CP = F::CP;
@@ -702,9 +698,12 @@ __device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROL
         const T* ut = reinterpret_cast<const T*>(a.ws.ut) + u * DV * C;
 #pragma unroll
         for (int kb = 0; kb < O::NK; kb++) op.a[kb] = MM::load(Frag<T>::ptr(wneg, mb, kb, F::DKP, lane));
-        float u4[4];
-        load4<T>(ut + ((size_t)((vcol0 / 16) * F::NB + mb) * 64 + lane) * 4, u4);
-        op.u = f32x4{u4[0], u4[1], u4[2], u4[3]};
+#pragma unroll
+        for (int v = 0; v < NVB; v++) {
+            float u4[4];
+            load4<T>(ut + ((size_t)((vcol0 / 16 + v) * F::NB + mb) * 64 + lane) * 4, u4);
+            op.u[v] = f32x4{u4[0], u4[1], u4[2], u4[3]};
+        }
     } else {
         const T* qin = reinterpret_cast<const T*>(a.ws.qin) + u * C * F::DKP;
         const T* mm = reinterpret_cast<const T*>(a.ws.mmat) + u * C * CP;
@@ -727,17 +726,22 @@ __device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROL
     }
 }
 
-template <typename T, int DK, int DV, int C, bool PERKEY>
+// NVB value tiles of 16 columns per workgroup: 1 gives the most workgroups (a single long
+// sequence), 2-8 divide the per-column operand stream when there are many (sequence, head)
+// units to fill the chip with.
+template <typename T, int DK, int DV, int C, bool PERKEY, int NVB>
 __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(PrefillArgs a) {
     using F = PfCfg<T, DK, DV, C>;
     using MM = typename F::MM;
+    using frag = typename MM::frag;
     constexpr int KB = F::KB, KPL = F::KPL, CP = F::CP, NB = F::NB;
     constexpr int NWV = ScanShape<C>::NWV, THREADS = ScanShape<C>::THREADS;
     constexpr int RB = DK / 16, RBW = (RB + NWV - 1) / NWV;
     constexpr bool RB_FULL = RB % NWV == 0;
-    constexpr int NVT = DV / SCAN_BV;
-    __shared__ __align__(16) T st[SCAN_BV][F::LDK];   // S^T slice (MFMA B operand)
-    __shared__ __align__(16) T et[SCAN_BV][F::LDC];   // E^T slice
+    constexpr int BV = SCAN_BV * NVB;
+    constexpr int NVT = DV / BV;
+    __shared__ __align__(16) T st[BV][F::LDK];   // S^T slice (MFMA B operand)
+    __shared__ __align__(16) T et[BV][F::LDC];   // E^T slice
 
     // XCD-aware unit mapping: all value tiles of a (sequence, head) on one XCD
     const int id = blockIdx.x;
@@ -749,7 +753,7 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
     const int n = unit / H, h = unit - (unit / H) * H;
     const int lane = lane_id(), w = wave_id(), r16 = lane & 15, g = lane >> 4;
     const int kq = g * KPL;
-    const int vcol0 = vt * SCAN_BV;
+    const int vcol0 = vt * BV;
     // clamps keep inconsistent cu_seqlens inside the workspace and the token range
     const int c_begin = a.ws.seq_first[n];
     const int c_end = (int)min((int64_t)a.ws.seq_first[n + 1], a.ws.max_chunks);
@@ -759,27 +763,31 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
     const bool init = valid && a.has_init != nullptr && a.has_init[n] != 0;
     float* S = valid ? a.state_pool + ((size_t)slot * H + h) * DK * DV : nullptr;
 
-    // state slice in accumulators: acc_s[j][e] = S[16 rb + 4 g + e][vcol0 + r16], rb = w + j NWV
-    f32x4 acc_s[RBW];
+    // state slice in accumulators:
+    //   acc_s[j][v][e] = S[16 rb + 4 g + e][vcol0 + 16 v + r16],  rb = w + j NWV
+    f32x4 acc_s[RBW][NVB];
 #pragma unroll
     for (int j = 0; j < RBW; j++) {
-        acc_s[j] = zero4();
         const int rb = w + j * NWV;
-        if (rb < RB) {
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int row = rb * 16 + 4 * g + e;
-                acc_s[j][e] = init ? S[(size_t)row * DV + vcol0 + r16] : 0.f;
-                st[r16][row] = from_f32<T>(acc_s[j][e]);
+        for (int v = 0; v < NVB; v++) {
+            acc_s[j][v] = zero4();
+            if (rb < RB) {
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int row = rb * 16 + 4 * g + e;
+                    acc_s[j][v][e] = init ? S[(size_t)row * DV + vcol0 + 16 * v + r16] : 0.f;
+                    st[16 * v + r16][row] = from_f32<T>(acc_s[j][v][e]);
+                }
             }
         }
     }
     if constexpr (CP > C) {
-        for (int idx = threadIdx.x; idx < SCAN_BV * (CP - C); idx += THREADS)
+        for (int idx = threadIdx.x; idx < BV * (CP - C); idx += THREADS)
             et[idx / (CP - C)][C + idx % (CP - C)] = from_f32<T>(0.f);
     }
     if constexpr (F::DKP > DK) {  // padded state rows stay zero
-        for (int idx = threadIdx.x; idx < SCAN_BV * (F::DKP - DK); idx += THREADS)
+        for (int idx = threadIdx.x; idx < BV * (F::DKP - DK); idx += THREADS)
             st[idx / (F::DKP - DK)][DK + idx % (F::DKP - DK)] = from_f32<T>(0.f);
     }
 
@@ -789,81 +797,90 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
     // the sequential pass for one role; both roles meet the same two barriers per chunk
     auto run = [&](auto role) {
         constexpr bool E = decltype(role)::value;
-        using O = ScanOps<T, DK, DV, C, PERKEY, E>;
+        using O = ScanOps<T, DK, DV, C, PERKEY, E, NVB>;
         const int mb = E ? w : w - NB;
         auto update_state = [&](const O& cur) {  // after the E barrier
+            frag fe[NVB][O::NK2];
+#pragma unroll
+            for (int v = 0; v < NVB; v++)
+#pragma unroll
+                for (int kt = 0; kt < O::NK2; kt++) fe[v][kt] = MM::load(&et[16 * v + r16][kt * KB + kq]);
 #pragma unroll
             for (int j = 0; j < RBW; j++) {
                 const int rb = w + j * NWV;
                 if (RB_FULL || rb < RB) {
 #pragma unroll
-                    for (int e = 0; e < 4; e++)
-                        acc_s[j][e] *= PERKEY ? cur.dec[PERKEY ? j : 0][e] : cur.dec0;
+                    for (int v = 0; v < NVB; v++) {
 #pragma unroll
-                    for (int kt = 0; kt < O::NK2; kt++) {
-                        auto fb = MM::load(&et[r16][kt * KB + kq]);
-                        acc_s[j] = MM::mma(cur.ak[j][kt], fb, acc_s[j]);  // + K_g^T E
+                        for (int e = 0; e < 4; e++)
+                            acc_s[j][v][e] *= PERKEY ? cur.dec[PERKEY ? j : 0][e] : cur.dec0;
+#pragma unroll
+                        for (int kt = 0; kt < O::NK2; kt++)
+                            acc_s[j][v] = MM::mma(cur.ak[j][kt], fe[v][kt], acc_s[j][v]);  // + K_g^T E
+                        float sv[4] = {acc_s[j][v][0], acc_s[j][v][1], acc_s[j][v][2], acc_s[j][v][3]};
+                        store4<T>(&st[16 * v + r16][rb * 16 + 4 * g], sv);
                     }
-                    float sv[4] = {acc_s[j][0], acc_s[j][1], acc_s[j][2], acc_s[j][3]};
-                    store4<T>(&st[r16][rb * 16 + 4 * g], sv);
                 }
             }
         };
         auto step = [&](const O& cur, int c) {
             lds_barrier();  // st holds S_c^T
-            f32x4 acc = E ? cur.u : zero4();
+            f32x4 acc[NVB];
 #pragma unroll
-            for (int kb = 0; kb < O::NK; kb++) {
-                auto fb = MM::load(&st[r16][kb * KB + kq]);
-                acc = MM::mma(cur.a[kb], fb, acc);  // E: U - W S;  O: Q_in S
-            }
+            for (int v = 0; v < NVB; v++) acc[v] = E ? cur.u[E ? v : 0] : zero4();
+#pragma unroll
+            for (int kb = 0; kb < O::NK; kb++)
+#pragma unroll
+                for (int v = 0; v < NVB; v++) {
+                    auto fb = MM::load(&st[16 * v + r16][kb * KB + kq]);
+                    acc[v] = MM::mma(cur.a[kb], fb, acc[v]);  // E: U - W S;  O: Q_in S
+                }
             if constexpr (E) {
-                float ev[4] = {acc[0], acc[1], acc[2], acc[3]};
-                store4<T>(&et[r16][mb * 16 + 4 * g], ev);
+#pragma unroll
+                for (int v = 0; v < NVB; v++) {
+                    float ev[4] = {acc[v][0], acc[v][1], acc[v][2], acc[v][3]};
+                    store4<T>(&et[16 * v + r16][mb * 16 + 4 * g], ev);
+                }
             }
             lds_barrier();  // et holds E_c
             if constexpr (!E) {
 #pragma unroll
-                for (int kt = 0; kt < O::NK2; kt++) {
-                    auto fb = MM::load(&et[r16][kt * KB + kq]);
-                    acc = MM::mma(cur.am[kt], fb, acc);  // + M E
-                }
+                for (int kt = 0; kt < O::NK2; kt++)
+#pragma unroll
+                    for (int v = 0; v < NVB; v++) {
+                        auto fb = MM::load(&et[16 * v + r16][kt * KB + kq]);
+                        acc[v] = MM::mma(cur.am[kt], fb, acc[v]);  // + M E
+                    }
                 const int tok0 = t_begin + (c - c_begin) * C;
                 const int len = min(C, t_end - tok0);
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    // tokens past the sequence end go to a scratch word instead of a branch
-                    const int i = mb * 16 + 4 * g + e;
-                    T* dst = i < len ? out + ((size_t)(tok0 + i) * H + h) * DV + vcol0 + r16 : dump;
-                    *dst = from_f32<T>(acc[e]);
-                }
+                for (int v = 0; v < NVB; v++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        // tokens past the sequence end go to a scratch word instead of a branch
+                        const int i = mb * 16 + 4 * g + e;
+                        T* dst = i < len ? out + ((size_t)(tok0 + i) * H + h) * DV + vcol0 + 16 * v + r16
+                                         : dump;
+                        *dst = from_f32<T>(acc[v][e]);
+                    }
             }
             update_state(cur);
         };
-        // Chunks go in groups of G: the operands of the next group are loaded while the
-        // current group is computed, so a load has G chunk times to arrive (the per-chunk
-        // time is otherwise bound by the memory latency). Prefetch indices are clamped to the
-        // last chunk so every load is unconditional.
-        constexpr int G = SCAN_GROUP;
+        // operands of chunk c + 1 are loaded while chunk c is computed; prefetch indices are
+        // clamped to the last chunk so every load is unconditional
         const int clast = c_end - 1;
-        auto ld = [&](O (&ops)[G], int c) {
-#pragma unroll
-            for (int i = 0; i < G; i++)
-                scan_load_ops<T, DK, DV, C, PERKEY, E>(ops[i], a, (size_t)min(c + i, clast) * H + h,
-                                                       vcol0, mb, w);
+        auto ld = [&](O& op, int c) {
+            scan_load_ops<T, DK, DV, C, PERKEY, E, NVB>(op, a, (size_t)min(c, clast) * H + h,
+                                                        vcol0, mb, w);
         };
-        O opa[G], opb[G];
-        ld(opa, c_begin);
-        for (int c = c_begin; c < c_end; c += 2 * G) {
-            ld(opb, c + G);
-#pragma unroll
-            for (int i = 0; i < G; i++)
-                if (c + i < c_end) step(opa[i], c + i);
-            if (c + G >= c_end) break;
-            ld(opa, c + 2 * G);
-#pragma unroll
-            for (int i = 0; i < G; i++)
-                if (c + G + i < c_end) step(opb[i], c + G + i);
+        O op0, op1;
+        ld(op0, c_begin);
+        for (int c = c_begin; c < c_end; c += 2) {
+            ld(op1, c + 1);
+            step(op0, c);
+            if (c + 1 >= c_end) break;
+            ld(op0, c + 2);
+            step(op1, c + 1);
         }
     };
     if (c_begin < c_end) {
@@ -876,8 +893,10 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
             const int rb = w + j * NWV;
             if (rb < RB) {
 #pragma unroll
-                for (int e = 0; e < 4; e++)
-                    S[(size_t)(rb * 16 + 4 * g + e) * DV + vcol0 + r16] = acc_s[j][e];
+                for (int v = 0; v < NVB; v++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        S[(size_t)(rb * 16 + 4 * g + e) * DV + vcol0 + 16 * v + r16] = acc_s[j][v][e];
             }
         }
     }
@@ -906,11 +925,27 @@ hipError_t prefill_launch_cfg(const PrefillArgs& a, hipStream_t s) {
     const int64_t nchunk = a.ws.max_chunks;
     if (nchunk > 0)
         hipLaunchKernelGGL(prep, dim3((unsigned)(nchunk * a.H)), dim3(PF_THREADS), smem, s, a);
+    // The value width per workgroup (NVB 16-column tiles) is the widest that still leaves
+    // at least one workgroup per CU: wider tiles share each chunk's operand stream over more
+    // columns (fewer bytes per column), narrower ones run more sequential chains at once.
     const int units = a.n_seqs * a.H;
-    const int nvt = D / SCAN_BV;
-    const int grid = ((units + 7) / 8) * 8 * nvt;
-    hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY>), dim3((unsigned)grid),
-                       dim3(ScanShape<C>::THREADS), 0, s, a);
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        ncu = 256;
+    }
+    const int64_t tiles = (int64_t)units * (D / SCAN_BV);
+    int nvb = 1;
+    while (nvb * 2 <= D / SCAN_BV && tiles / (nvb * 2) >= ncu) nvb *= 2;
+    const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * (D / (SCAN_BV * nvb)));
+    const dim3 block(ScanShape<C>::THREADS);
+    switch (nvb) {
+        case 1: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, 1>), dim3(grid), block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, D >= 32 ? 2 : 1>), dim3(grid), block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, D >= 64 ? 4 : 1>), dim3(grid), block, 0, s, a); break;
+        default: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, D >= 128 ? 8 : 1>), dim3(grid), block, 0, s, a); break;
+    }
     return hipGetLastError();
 }
 

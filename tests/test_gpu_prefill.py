@@ -61,6 +61,22 @@ def test_prefill_vs_oracle(dtype, d, chunk, perkey, lengths, init, l2):
     _check(x, o, pool, o_ref, s_ref)
 
 
+@pytest.mark.parametrize("nseq,dtype,perkey", [(48, torch.bfloat16, True),
+                                               (48, torch.float32, False),
+                                               (64, torch.bfloat16, False),
+                                               (64, torch.float32, True)])
+def test_many_sequences_wide_value_tiles(nseq, dtype, perkey):
+    """Enough (sequence, head) units that the scan gives each workgroup several 16-column
+    value tiles: 48 (two tiles) or 64 (four tiles) ragged sequences x 4 heads at d = 64."""
+    say(f"case many sequences n={nseq} {dtype} perkey={perkey}")
+    lengths = torch.randint(0, 140, (nseq,), generator=torch.Generator().manual_seed(21)).tolist()
+    x = inputs.random_prefill(21, lengths, H=4, dk=64, dv=64, dtype=dtype, perkey=perkey,
+                              with_init=True)
+    o, pool = run_prefill(x)
+    o_ref, s_ref = oracle_prefill(x)
+    _check(x, o, pool, o_ref, s_ref)
+
+
 @pytest.mark.parametrize("perkey", [False, True])
 def test_chunk_size_invariance(perkey):
     """The chunk size is an execution choice: C = 16, 32, 64 give the same result."""
