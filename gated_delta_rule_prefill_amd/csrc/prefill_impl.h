@@ -742,6 +742,7 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
     constexpr int NVT = DV / BV;
     __shared__ __align__(16) T st[BV][F::LDK];   // S^T slice (MFMA B operand)
     __shared__ __align__(16) T et[BV][F::LDC];   // E^T slice
+    __shared__ __align__(16) T ot[NB][NVB][16][16];  // O tiles of the O waves, row-major
 
     // XCD-aware unit mapping: all value tiles of a (sequence, head) on one XCD
     const int id = blockIdx.x;
@@ -792,7 +793,7 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
     }
 
     T* out = reinterpret_cast<T*>(a.o);
-    T* dump = reinterpret_cast<T*>(a.ws.dump) + lane;
+    T* dump = reinterpret_cast<T*>(a.ws.dump) + 4 * lane;  // 64 lanes x 4 elements <= 1 KiB
 
     // the sequential pass for one role; both roles meet the same two barriers per chunk
     auto run = [&](auto role) {
@@ -851,18 +852,26 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
                         auto fb = MM::load(&et[16 * v + r16][kt * KB + kq]);
                         acc[v] = MM::mma(cur.am[kt], fb, acc[v]);  // + M E
                     }
+                // the accumulator holds 4 tokens of one column per lane; a row-major pass
+                // through LDS lets every lane store 4 adjacent columns of one token at once
                 const int tok0 = t_begin + (c - c_begin) * C;
                 const int len = min(C, t_end - tok0);
 #pragma unroll
                 for (int v = 0; v < NVB; v++)
 #pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        // tokens past the sequence end go to a scratch word instead of a branch
-                        const int i = mb * 16 + 4 * g + e;
-                        T* dst = i < len ? out + ((size_t)(tok0 + i) * H + h) * DV + vcol0 + 16 * v + r16
-                                         : dump;
-                        *dst = from_f32<T>(acc[v][e]);
-                    }
+                    for (int e = 0; e < 4; e++) ot[mb][v][4 * g + e][r16] = from_f32<T>(acc[v][e]);
+                asm volatile("" ::: "memory");  // LDS accesses of one wave complete in order
+                const int orow = lane >> 2, oc = (lane & 3) * 4;
+                const int i = mb * 16 + orow;
+#pragma unroll
+                for (int v = 0; v < NVB; v++) {
+                    float ov[4];
+                    load4<T>(&ot[mb][v][orow][oc], ov);
+                    // tokens past the sequence end go to a scratch area instead of a branch
+                    T* dst = i < len ? out + ((size_t)(tok0 + i) * H + h) * DV + vcol0 + 16 * v + oc
+                                     : dump;
+                    store4<T>(dst, ov);
+                }
             }
             update_state(cur);
         };
