@@ -233,14 +233,26 @@ __global__ __launch_bounds__(DENSE_THREADS) void deltalog_kernel(DeltaLogArgs a)
     const int cg = tid % G::TPR;
     const int r0 = tid / G::TPR;
     float* S = a.base + sh * DK * DV;
+    // clamp so that corrupted metadata can never index past the log buffers
+    const int L = min(max(a.len[sh], 0), C);
+    // The log (at most 16 x (d_k bf16 + d_v fp32)) is requested before the base stream, in
+    // 16-byte pieces (8 keys or 4 values per thread), so its staging and the key-side replay
+    // do not wait behind the 64 KiB base read.
+    const uint16_t* kl = a.klog + sh * C * DK;
+    const float* ul = a.ulog + sh * C * DV;
+    constexpr int KPIECES = DL_MAXLOG * DK / 8, UPIECES = DL_MAXLOG * DV / 4;
+    static_assert(KPIECES <= DENSE_THREADS && UPIECES <= DENSE_THREADS, "one piece per thread");
+    const bool kpiece = tid * 8 < L * DK, upiece = tid * 4 < L * DV;
+    bf16x8 kraw;
+    f32x4 uraw;
+    if (kpiece) kraw = *reinterpret_cast<const bf16x8*>(kl + tid * 8);
+    if (upiece) uraw = *reinterpret_cast<const f32x4*>(ul + tid * 4);
     f32x4 st[G::NP];
 #pragma unroll
     for (int p = 0; p < G::NP; p++) {
         const int r = r0 + p * G::RPP;
         if (r < DK) st[p] = stream_load(S + (size_t)r * DV + cg * 4);
     }
-    // clamp so that corrupted metadata can never index past the log buffers
-    const int L = min(max(a.len[sh], 0), C);
     const float lp = a.lbar[sh] + a.g[bh];  // Algorithm 1: accumulate the decay first
     const T* qp = reinterpret_cast<const T*>(a.q) + (size_t)bh * DK;
     const T* kp = reinterpret_cast<const T*>(a.k) + (size_t)bh * DK;
@@ -250,13 +262,15 @@ __global__ __launch_bounds__(DENSE_THREADS) void deltalog_kernel(DeltaLogArgs a)
         sm.q[tid] = to_f32(qp[tid]);
     }
     if (tid < DV) sm.v[tid] = to_f32(vp[tid]);
-    const uint16_t* kl = a.klog + sh * C * DK;
-    const float* ul = a.ulog + sh * C * DV;
-    for (int i = tid; i < L * DK; i += DENSE_THREADS) {
-        uint32_t bits = (uint32_t)kl[i] << 16;
-        sm.klog[i / DK][i % DK] = __builtin_bit_cast(float, bits);
+    if (kpiece) {
+        const int e = tid * 8 / DK, c0 = tid * 8 % DK;
+#pragma unroll
+        for (int i = 0; i < 8; i++) sm.klog[e][c0 + i] = (float)kraw[i];
     }
-    for (int i = tid; i < L * DV; i += DENSE_THREADS) sm.ulog[i / DV][i % DV] = ul[i];
+    if (upiece) {
+        const int e = tid * 4 / DV, c0 = tid * 4 % DV;
+        *reinterpret_cast<f32x4*>(&sm.ulog[e][c0]) = uraw;
+    }
     if (tid < L) {
         float lam = a.lamlog[sh * C + tid];
         sm.lam[tid] = lam;
