@@ -107,24 +107,33 @@ __global__ __launch_bounds__(DENSE_THREADS) void decode_kernel(DecodeArgs a) {
     const int r0 = tid / G::TPR;
     float* S = a.pool + ((size_t)slot * H + h) * DK * DV;
 
-    // issue the state stream first
+    // the token's vectors first (their staging and the norms then overlap the state read),
+    // then the state stream
+    const T* qp = reinterpret_cast<const T*>(a.q) + (size_t)bh * DK;
+    const T* kp = reinterpret_cast<const T*>(a.k) + (size_t)bh * DK;
+    const T* vp = reinterpret_cast<const T*>(a.v) + (size_t)bh * DV;
+    float kx = 0.f, qx = 0.f, gx = 0.f, vx = 0.f;
+    if (tid < DK) {
+        kx = to_f32(kp[tid]);
+        qx = to_f32(qp[tid]);
+        if (PERKEY) gx = a.g[(size_t)bh * DK + tid];
+    }
+    if (tid < DV) vx = to_f32(vp[tid]);
+    const float beta = a.beta[bh];
+    const float gs = PERKEY ? 0.f : a.g[bh];
     f32x4 st[G::NP];
 #pragma unroll
     for (int p = 0; p < G::NP; p++) {
         const int r = r0 + p * G::RPP;
         if (r < DK) st[p] = stream_load(S + (size_t)r * DV + cg * 4);
     }
-    const T* qp = reinterpret_cast<const T*>(a.q) + (size_t)bh * DK;
-    const T* kp = reinterpret_cast<const T*>(a.k) + (size_t)bh * DK;
-    const T* vp = reinterpret_cast<const T*>(a.v) + (size_t)bh * DV;
     if (tid < DK) {
-        sm.k[tid] = to_f32(kp[tid]);
-        sm.q[tid] = to_f32(qp[tid]);
-        if (PERKEY) sm.gk[tid] = __expf(a.g[(size_t)bh * DK + tid]);
+        sm.k[tid] = kx;
+        sm.q[tid] = qx;
+        if (PERKEY) sm.gk[tid] = __expf(gx);
     }
-    if (tid < DV) sm.v[tid] = to_f32(vp[tid]);
-    const float beta = a.beta[bh];
-    const float alpha = PERKEY ? 1.f : __expf(a.g[bh]);
+    if (tid < DV) sm.v[tid] = vx;
+    const float alpha = PERKEY ? 1.f : __expf(gs);
     lds_barrier();
 
     float ik, iq, kq;
