@@ -644,17 +644,18 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
 // =====================================================================================
 // scan kernel: the sequential state pass over chunks
 // =====================================================================================
-// One workgroup per (sequence, head, 16-column value tile) with 2 NB waves (NB = C / 16
-// token blocks); each wave keeps one role for the whole sequence:
-//   E wave w < NB      E rows of token block w:        E = U + (-W) S
-//   O wave w >= NB     O rows of token block w - NB:   O = Q_in S + M E
-// and every wave owns state row blocks rb = w + j NWV of the fp32 state slice, updated in
-// its MFMA accumulators: S <- Diag(e^{G_C}) S + K_g^T E.
-// Per chunk: barrier (S^T in LDS) -> E, Q_in S -> barrier (E in LDS) -> M E, state update,
-// S^T back to LDS. Each wave prefetches only its own operands of the next chunk into
-// registers (-W and U, or Q_in and M, plus its K_g^T rows): a single wave pulls only a
-// small share of a CU's vector-memory bandwidth, so the per-chunk operand stream is spread
-// over all waves of the workgroup.
+// One workgroup per (sequence, head, value tile) with 2 NB waves (NB = C / 16 token
+// blocks); each wave keeps one role for the whole sequence:
+//   E wave w < NB      E rows of token block w:  E = U + (-W) S, and the state row blocks
+//                      rb = w + j NB of the fp32 state slice, kept in its MFMA accumulators:
+//                      S <- Diag(e^{G_C}) S + K_g^T E
+//   O wave w >= NB     O rows of token block w - NB: O = Q_in S + M E, and the output stores
+// Per chunk: barrier (S^T in LDS) -> E, Q_in S -> barrier (E in LDS) -> state update and
+// S^T back to LDS (E waves) while the O waves finish M E and store O. Each wave prefetches
+// only its own operands of the next chunk into registers (-W, U and K_g^T rows, or Q_in
+// and M): a single wave pulls only a small share of a CU's vector-memory bandwidth, so the
+// per-chunk operand stream is spread over all waves of the workgroup. The split keeps the
+// two roles' work after the E barrier about equal (measured per phase with cycle stamps).
 template <int C>
 struct ScanShape {
     static constexpr int NB = C / 16;
@@ -668,21 +669,24 @@ struct ScanOps {
     using frag = typename F::MM::frag;
     static constexpr int NK = F::DKP / F::KB;    // k-steps over (padded) d_k
     static constexpr int NK2 = F::CP / F::KB;    // k-steps over the chunk
-    static constexpr int NWV = ScanShape<C>::NWV;
+    static constexpr int NB = C / 16;
     static constexpr int RB = DK / 16;
-    static constexpr int RBW = (RB + NWV - 1) / NWV;   // state row blocks per wave
-    // with RB a multiple of the wave count every wave owns full row blocks and the loop
+    static constexpr int RBW = (RB + NB - 1) / NB;   // state row blocks per E wave
+    // with RB a multiple of the E-wave count every E wave owns full row blocks and the loop
     // stays branch-free (the compiler then waits only for the operands it needs)
-    static constexpr bool RB_FULL = RB % NWV == 0;
+    static constexpr bool RB_FULL = RB % NB == 0;
     frag a[NK];                    // -W rows (E wave) or Q_in rows (O wave)
     frag am[EROLE ? 1 : NK2];      // M rows (O wave)
     f32x4 u[NVB];                  // U of the token block per value tile (E wave)
-    frag ak[RBW][NK2];             // K_g^T rows of the wave's state row blocks
+    frag ak[EROLE ? RBW : 1][NK2]; // K_g^T rows of the wave's state row blocks (E wave)
     f32x4 dec[PERKEY ? RBW : 1];   // per key: e^{G_C} of the lane's 4 state rows
     float dec0;                    // scalar gate: e^{G_C}
 };
 
-template <typename T, int DK, int DV, int C, bool PERKEY, bool EROLE, int NVB>
+// Operand loads of one chunk for one wave, in two parts issued at different points of the
+// previous chunk: part 0 (first needed: -W and U, or Q_in) and part 1 (K_g^T rows and decay,
+// or M). Issuing a wave's whole set at once stalls it on a full vector-memory queue.
+template <int PART, typename T, int DK, int DV, int C, bool PERKEY, bool EROLE, int NVB>
 __device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROLE, NVB>& op,
                                               const PrefillArgs& a, size_t u, int vcol0,
                                               int mb, int w) {
@@ -692,36 +696,42 @@ __device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROL
     constexpr int CP = F::CP;
     const int lane = lane_id();
     const float* dec = a.ws.decay + u * DK;
-    if constexpr (!PERKEY) op.dec0 = dec[0];
-    if constexpr (EROLE) {
-        const T* wneg = reinterpret_cast<const T*>(a.ws.wneg) + u * C * F::DKP;
-        const T* ut = reinterpret_cast<const T*>(a.ws.ut) + u * DV * C;
+    if constexpr (PART == 0) {
+        if constexpr (EROLE) {
+            const T* wneg = reinterpret_cast<const T*>(a.ws.wneg) + u * C * F::DKP;
+            const T* ut = reinterpret_cast<const T*>(a.ws.ut) + u * DV * C;
 #pragma unroll
-        for (int kb = 0; kb < O::NK; kb++) op.a[kb] = MM::load(Frag<T>::ptr(wneg, mb, kb, F::DKP, lane));
+            for (int kb = 0; kb < O::NK; kb++) op.a[kb] = MM::load(Frag<T>::ptr(wneg, mb, kb, F::DKP, lane));
 #pragma unroll
-        for (int v = 0; v < NVB; v++) {
-            float u4[4];
-            load4<T>(ut + ((size_t)((vcol0 / 16 + v) * F::NB + mb) * 64 + lane) * 4, u4);
-            op.u[v] = f32x4{u4[0], u4[1], u4[2], u4[3]};
+            for (int v = 0; v < NVB; v++) {
+                float u4[4];
+                load4<T>(ut + ((size_t)((vcol0 / 16 + v) * F::NB + mb) * 64 + lane) * 4, u4);
+                op.u[v] = f32x4{u4[0], u4[1], u4[2], u4[3]};
+            }
+        } else {
+            const T* qin = reinterpret_cast<const T*>(a.ws.qin) + u * C * F::DKP;
+#pragma unroll
+            for (int kb = 0; kb < O::NK; kb++) op.a[kb] = MM::load(Frag<T>::ptr(qin, mb, kb, F::DKP, lane));
         }
     } else {
-        const T* qin = reinterpret_cast<const T*>(a.ws.qin) + u * C * F::DKP;
-        const T* mm = reinterpret_cast<const T*>(a.ws.mmat) + u * C * CP;
+        if constexpr (EROLE) {
+            if constexpr (!PERKEY) op.dec0 = dec[0];
+            const T* kgt = reinterpret_cast<const T*>(a.ws.kgt) + u * DK * CP;
 #pragma unroll
-        for (int kb = 0; kb < O::NK; kb++) op.a[kb] = MM::load(Frag<T>::ptr(qin, mb, kb, F::DKP, lane));
+            for (int j = 0; j < O::RBW; j++) {
+                const int rb = w + j * O::NB;
+                if (O::RB_FULL || rb < O::RB) {
 #pragma unroll
-        for (int kt = 0; kt < O::NK2; kt++) op.am[kt] = MM::load(Frag<T>::ptr(mm, mb, kt, CP, lane));
-    }
-    const T* kgt = reinterpret_cast<const T*>(a.ws.kgt) + u * DK * CP;
+                    for (int kt = 0; kt < O::NK2; kt++)
+                        op.ak[j][kt] = MM::load(Frag<T>::ptr(kgt, rb, kt, CP, lane));
+                    if constexpr (PERKEY)  // 4 distinct 16-byte words per wave: one cache line
+                        op.dec[j] = *reinterpret_cast<const f32x4*>(dec + rb * 16 + (lane >> 4) * 4);
+                }
+            }
+        } else {
+            const T* mm = reinterpret_cast<const T*>(a.ws.mmat) + u * C * CP;
 #pragma unroll
-    for (int j = 0; j < O::RBW; j++) {
-        const int rb = w + j * O::NWV;
-        if (O::RB_FULL || rb < O::RB) {
-#pragma unroll
-            for (int kt = 0; kt < O::NK2; kt++)
-                op.ak[j][kt] = MM::load(Frag<T>::ptr(kgt, rb, kt, CP, lane));
-            if constexpr (PERKEY)  // 4 distinct 16-byte words per wave: one cache line
-                op.dec[j] = *reinterpret_cast<const f32x4*>(dec + rb * 16 + (lane >> 4) * 4);
+            for (int kt = 0; kt < O::NK2; kt++) op.am[kt] = MM::load(Frag<T>::ptr(mm, mb, kt, CP, lane));
         }
     }
 }
@@ -735,9 +745,9 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
     using MM = typename F::MM;
     using frag = typename MM::frag;
     constexpr int KB = F::KB, KPL = F::KPL, CP = F::CP, NB = F::NB;
-    constexpr int NWV = ScanShape<C>::NWV, THREADS = ScanShape<C>::THREADS;
-    constexpr int RB = DK / 16, RBW = (RB + NWV - 1) / NWV;
-    constexpr bool RB_FULL = RB % NWV == 0;
+    constexpr int THREADS = ScanShape<C>::THREADS;
+    constexpr int RB = DK / 16, RBW = (RB + NB - 1) / NB;   // state row blocks per E wave
+    constexpr bool RB_FULL = RB % NB == 0;
     constexpr int BV = SCAN_BV * NVB;
     constexpr int NVT = DV / BV;
     __shared__ __align__(16) T st[BV][F::LDK];   // S^T slice (MFMA B operand)
@@ -764,16 +774,17 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
     const bool init = valid && a.has_init != nullptr && a.has_init[n] != 0;
     float* S = valid ? a.state_pool + ((size_t)slot * H + h) * DK * DV : nullptr;
 
-    // state slice in accumulators:
-    //   acc_s[j][v][e] = S[16 rb + 4 g + e][vcol0 + 16 v + r16],  rb = w + j NWV
+    // state slice in the E waves' accumulators:
+    //   acc_s[j][v][e] = S[16 rb + 4 g + e][vcol0 + 16 v + r16],  rb = w + j NB  (w < NB)
+    const bool ewave = w < NB;
     f32x4 acc_s[RBW][NVB];
 #pragma unroll
     for (int j = 0; j < RBW; j++) {
-        const int rb = w + j * NWV;
+        const int rb = w + j * NB;
 #pragma unroll
         for (int v = 0; v < NVB; v++) {
             acc_s[j][v] = zero4();
-            if (rb < RB) {
+            if (ewave && rb < RB) {
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int row = rb * 16 + 4 * g + e;
@@ -800,7 +811,7 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
         constexpr bool E = decltype(role)::value;
         using O = ScanOps<T, DK, DV, C, PERKEY, E, NVB>;
         const int mb = E ? w : w - NB;
-        auto update_state = [&](const O& cur) {  // after the E barrier
+        auto update_state = [&](const O& cur) {  // E waves, after the E barrier
             frag fe[NVB][O::NK2];
 #pragma unroll
             for (int v = 0; v < NVB; v++)
@@ -808,7 +819,7 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
                 for (int kt = 0; kt < O::NK2; kt++) fe[v][kt] = MM::load(&et[16 * v + r16][kt * KB + kq]);
 #pragma unroll
             for (int j = 0; j < RBW; j++) {
-                const int rb = w + j * NWV;
+                const int rb = w + j * NB;
                 if (RB_FULL || rb < RB) {
 #pragma unroll
                     for (int v = 0; v < NVB; v++) {
@@ -824,8 +835,18 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
                 }
             }
         };
-        auto step = [&](const O& cur, int c) {
+        // operands of chunk c + 1 are loaded while chunk c is computed; prefetch indices are
+        // clamped to the last chunk so every load is unconditional
+        const int clast = c_end - 1;
+        auto ld = [&](auto part, O& op, int c) {
+            scan_load_ops<decltype(part)::value, T, DK, DV, C, PERKEY, E, NVB>(
+                op, a, (size_t)min(c, clast) * H + h, vcol0, mb, w);
+        };
+        using part0 = std::integral_constant<int, 0>;
+        using part1 = std::integral_constant<int, 1>;
+        auto step = [&](const O& cur, O& nxt, int c) {
             lds_barrier();  // st holds S_c^T
+            ld(part1(), nxt, c + 1);
             f32x4 acc[NVB];
 #pragma unroll
             for (int v = 0; v < NVB; v++) acc[v] = E ? cur.u[E ? v : 0] : zero4();
@@ -844,6 +865,7 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
                 }
             }
             lds_barrier();  // et holds E_c
+            ld(part0(), nxt, c + 1);
             if constexpr (!E) {
 #pragma unroll
                 for (int kt = 0; kt < O::NK2; kt++)
@@ -872,34 +894,27 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
                                      : dump;
                     store4<T>(dst, ov);
                 }
+            } else {
+                update_state(cur);
             }
-            update_state(cur);
-        };
-        // operands of chunk c + 1 are loaded while chunk c is computed; prefetch indices are
-        // clamped to the last chunk so every load is unconditional
-        const int clast = c_end - 1;
-        auto ld = [&](O& op, int c) {
-            scan_load_ops<T, DK, DV, C, PERKEY, E, NVB>(op, a, (size_t)min(c, clast) * H + h,
-                                                        vcol0, mb, w);
         };
         O op0, op1;
-        ld(op0, c_begin);
+        ld(part0(), op0, c_begin);
+        ld(part1(), op0, c_begin);
         for (int c = c_begin; c < c_end; c += 2) {
-            ld(op1, c + 1);
-            step(op0, c);
+            step(op0, op1, c);
             if (c + 1 >= c_end) break;
-            ld(op0, c + 2);
-            step(op1, c + 1);
+            step(op1, op0, c + 1);
         }
     };
     if (c_begin < c_end) {
         if (w < NB) run(std::integral_constant<bool, true>());
         else run(std::integral_constant<bool, false>());
     }
-    if (valid) {
+    if (valid && ewave) {
 #pragma unroll
         for (int j = 0; j < RBW; j++) {
-            const int rb = w + j * NWV;
+            const int rb = w + j * NB;
             if (rb < RB) {
 #pragma unroll
                 for (int v = 0; v < NVB; v++)
