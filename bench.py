@@ -83,15 +83,21 @@ def counter_traffic(name, digest):
 
 
 # ------------------------------------------------------------------------------ prefill
-def bench_prefill(steps, warmup):
+def bench_prefill(steps, warmup, ckpt_every=None):
+    """The prefill pass; with ckpt_every, the same pass also exporting the state every
+    ckpt_every tokens into slots of its own."""
     sets = []
     for seed in range(3):
         x = inputs.prefill_config(seed)
         sets.append([t.to(DEV) for t in (x.q, x.k, x.v, x.g, x.beta)])
     cu = x.cu_seqlens.to(DEV)
     T, H, d = x.q.shape
-    pool = torch.zeros((1, H, d, d), device=DEV)
+    pos = list(range(ckpt_every, T, ckpt_every)) if ckpt_every else []
+    pool = torch.zeros((1 + len(pos), H, d, d), device=DEV)
     slots = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ck_cu = torch.tensor([0, len(pos)], dtype=torch.int32, device=DEV)
+    ck_pos = torch.tensor(pos, dtype=torch.int32, device=DEV)
+    ck_slots = torch.arange(1, 1 + len(pos), dtype=torch.int32, device=DEV)
     need = gdn.gdn_prefill_workspace_bytes(H, d, d, torch.bfloat16, False, 1, T, x.chunk)
     ws = torch.empty(need, dtype=torch.uint8, device=DEV)
     o = torch.empty((T, H, d), dtype=torch.bfloat16, device=DEV)
@@ -100,13 +106,32 @@ def bench_prefill(steps, warmup):
     def step():
         q, k, v, g, b = sets[it[0] % 3]
         it[0] += 1
-        gdn.gdn_prefill_chunked(q, k, v, g, b, cu, x.chunk, pool, slots, scale=x.scale, o=o,
-                                workspace=ws)
+        if ckpt_every:
+            gdn.gdn_prefill_chunked_ckpt(q, k, v, g, b, cu, x.chunk, pool, slots, ck_cu, ck_pos,
+                                         ck_slots, scale=x.scale, o=o, workspace=ws)
+        else:
+            gdn.gdn_prefill_chunked(q, k, v, g, b, cu, x.chunk, pool, slots, scale=x.scale,
+                                    o=o, workspace=ws)
 
     ms, wall = ev_time(step, steps, warmup)
     byts = traffic.prefill_bytes(T, H, d, d, 2, False, 1, False)
     flops = traffic.prefill_flops([T], H, d, d, x.chunk)
-    return dict(ms=ms, wall=wall, tokens=T, bytes=byts, flops=flops, H=H, d=d, ws_bytes=need)
+    return dict(ms=ms, wall=wall, tokens=T, bytes=byts, flops=flops, H=H, d=d, ws_bytes=need,
+                n_ckpt=len(pos), ckpt_bytes=len(pos) * H * d * d * 4)
+
+
+def bench_prefill_ckpt(steps, warmup, plain_ms):
+    """Cost of exporting intermediate states inside the prefill: every 640 tokens (a hybrid
+    cache block) and at every chunk boundary (every block-size multiple kept)."""
+    out = {"workload": "GDN chunked prefill T=8192 H=16 d=128 chunk 64 bf16, exporting the "
+                       "fp32 state every N tokens", "ms_plain": plain_ms}
+    for every in (640, 64):
+        r = bench_prefill(steps, warmup, ckpt_every=every)
+        out[f"every_{every}"] = dict(n_ckpt=r["n_ckpt"], ms=r["ms"],
+                                     extra_ms=r["ms"] - plain_ms,
+                                     export_MiB=r["ckpt_bytes"] / 2**20,
+                                     tokens_per_s=r["tokens"] / (r["ms"] * 1e-3))
+    return out
 
 
 # ------------------------------------------------------------------------------- decode
@@ -237,9 +262,11 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-ckpt", action="store_true",
+                    help="skip the checkpoint-export runs (they launch the same kernels)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -286,6 +313,9 @@ def main():
                      "mfma_frac_bf16": p["flops"] / secs / traffic.BF16_MFMA_PEAK},
     }
     if not args.no_extras:
+        if not args.no_ckpt:
+            log("prefill with checkpoints ...")
+            line["prefill_ckpt"] = bench_prefill_ckpt(args.steps, args.warmup, p["ms"])
         log("decode ...")
         line["decode"] = bench_decode(args.steps, args.warmup)
         log("deltalog ...")

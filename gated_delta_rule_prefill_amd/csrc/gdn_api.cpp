@@ -90,26 +90,13 @@ int deltalog_pool_checks(const gdn_deltalog_pool_t* pool) {
     return GDN_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int gdn_prefill_workspace_bytes(const gdn_dims_t* dims, int32_t n_seqs, int32_t total_tokens,
-                                int32_t chunk, size_t* bytes) {
-    int st = prefill_common_checks(dims, n_seqs, total_tokens, chunk);
-    if (st) return st;
-    if (bytes == nullptr) return fail(GDN_ERR_NULL, "bytes is NULL");
-    *bytes = gdn::prefill_ws_layout(dims->dtype, dims->num_heads, dims->d_k, dims->d_v, chunk,
-                                    n_seqs, total_tokens, nullptr, nullptr);
-    return ok();
-}
-
-int gdn_prefill_chunked(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
-                        const float* g, const float* beta, const int32_t* cu_seqlens,
-                        int32_t n_seqs, int32_t total_tokens, int32_t chunk,
-                        float* state_pool, int32_t n_slots, const int32_t* slots,
-                        const int32_t* has_init, void* o, void* workspace, size_t ws_bytes,
-                        void* stream) {
+// Shared by gdn_prefill_chunked (no checkpoints) and gdn_prefill_chunked_ckpt.
+int prefill_run(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
+                const float* g, const float* beta, const int32_t* cu_seqlens, int32_t n_seqs,
+                int32_t total_tokens, int32_t chunk, float* state_pool, int32_t n_slots,
+                const int32_t* slots, const int32_t* has_init, const int32_t* ckpt_cu,
+                const int32_t* ckpt_pos, const int32_t* ckpt_slots, int32_t n_ckpt, void* o,
+                void* workspace, size_t ws_bytes, void* stream, const char* what) {
     int st = prefill_common_checks(dims, n_seqs, total_tokens, chunk);
     if (st) return st;
     if (n_seqs == 0) return ok();
@@ -118,6 +105,12 @@ int gdn_prefill_chunked(const gdn_dims_t* dims, const void* q, const void* k, co
     OPT_PTR(has_init);
     REQUIRE_PTR(state_pool);
     if (n_slots < 1) return fail(GDN_ERR_SHAPE, "n_slots must be >= 1 (got %d)", n_slots);
+    if (n_ckpt < 0) return fail(GDN_ERR_SHAPE, "n_ckpt must be >= 0 (got %d)", n_ckpt);
+    if (n_ckpt > 0) {
+        REQUIRE_PTR(ckpt_cu);
+        REQUIRE_PTR(ckpt_pos);
+        REQUIRE_PTR(ckpt_slots);
+    }
     if (total_tokens > 0) {
         REQUIRE_PTR(q);
         REQUIRE_PTR(k);
@@ -156,9 +149,50 @@ int gdn_prefill_chunked(const gdn_dims_t* dims, const void* q, const void* k, co
     a.slots = slots;
     a.has_init = has_init;
     a.o = o;
+    a.ckpt_cu = n_ckpt > 0 ? ckpt_cu : nullptr;
+    a.ckpt_pos = n_ckpt > 0 ? ckpt_pos : nullptr;
+    a.ckpt_slots = n_ckpt > 0 ? ckpt_slots : nullptr;
+    a.n_ckpt = n_ckpt;
     a.ws = ws;
-    return launch_status(gdn::launch_prefill(a, static_cast<hipStream_t>(stream)),
-                         "gdn_prefill_chunked");
+    return launch_status(gdn::launch_prefill(a, static_cast<hipStream_t>(stream)), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_prefill_workspace_bytes(const gdn_dims_t* dims, int32_t n_seqs, int32_t total_tokens,
+                                int32_t chunk, size_t* bytes) {
+    int st = prefill_common_checks(dims, n_seqs, total_tokens, chunk);
+    if (st) return st;
+    if (bytes == nullptr) return fail(GDN_ERR_NULL, "bytes is NULL");
+    *bytes = gdn::prefill_ws_layout(dims->dtype, dims->num_heads, dims->d_k, dims->d_v, chunk,
+                                    n_seqs, total_tokens, nullptr, nullptr);
+    return ok();
+}
+
+int gdn_prefill_chunked(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, const int32_t* cu_seqlens,
+                        int32_t n_seqs, int32_t total_tokens, int32_t chunk,
+                        float* state_pool, int32_t n_slots, const int32_t* slots,
+                        const int32_t* has_init, void* o, void* workspace, size_t ws_bytes,
+                        void* stream) {
+    return prefill_run(dims, q, k, v, g, beta, cu_seqlens, n_seqs, total_tokens, chunk,
+                       state_pool, n_slots, slots, has_init, nullptr, nullptr, nullptr, 0, o,
+                       workspace, ws_bytes, stream, "gdn_prefill_chunked");
+}
+
+int gdn_prefill_chunked_ckpt(const gdn_dims_t* dims, const void* q, const void* k,
+                             const void* v, const float* g, const float* beta,
+                             const int32_t* cu_seqlens, int32_t n_seqs, int32_t total_tokens,
+                             int32_t chunk, float* state_pool, int32_t n_slots,
+                             const int32_t* slots, const int32_t* has_init,
+                             const int32_t* ckpt_cu, const int32_t* ckpt_pos,
+                             const int32_t* ckpt_slots, int32_t n_ckpt, void* o,
+                             void* workspace, size_t ws_bytes, void* stream) {
+    return prefill_run(dims, q, k, v, g, beta, cu_seqlens, n_seqs, total_tokens, chunk,
+                       state_pool, n_slots, slots, has_init, ckpt_cu, ckpt_pos, ckpt_slots,
+                       n_ckpt, o, workspace, ws_bytes, stream, "gdn_prefill_chunked_ckpt");
 }
 
 int gdn_decode_step(const gdn_dims_t* dims, const void* q, const void* k, const void* v,

@@ -79,6 +79,10 @@ __device__ __forceinline__ void lds_barrier() {
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (WAVE - 1)); }
 __device__ __forceinline__ int wave_id() { return (int)(threadIdx.x / WAVE); }
+// Compiler-only memory fence: memory operations are not moved across it (no wait is
+// emitted). Placed after a prefetch so the loads are issued there and not sunk below the
+// arithmetic that follows.
+__device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
 
 // Sum across lanes that share (lane % width) ... reduction over the `width`-lane groups
 // formed by xor distances 1..width/2.

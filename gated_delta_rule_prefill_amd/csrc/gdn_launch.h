@@ -42,6 +42,11 @@ struct PrefillArgs {
     const int32_t* slots;
     const int32_t* has_init;
     void* o;
+    // state checkpoints inside the sequences (all null / 0 = none): the entries of sequence
+    // n are [ckpt_cu[n], ckpt_cu[n + 1]); entry i asks for the state after ckpt_pos[i]
+    // tokens of the sequence, stored in pool slot ckpt_slots[i]
+    const int32_t *ckpt_cu, *ckpt_pos, *ckpt_slots;
+    int n_ckpt;
     PrefillWs ws;
 };
 

@@ -26,6 +26,7 @@
 //         The value tiles of one (sequence, head) are placed on the same XCD so the shared
 //         per-chunk operands are served from that XCD's L2.
 #pragma once
+#include <climits>
 #include <type_traits>
 
 #include "gdn_common.h"
@@ -739,7 +740,9 @@ __device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROL
 // NVB value tiles of 16 columns per workgroup: 1 gives the most workgroups (a single long
 // sequence), 2-8 divide the per-column operand stream when there are many (sequence, head)
 // units to fill the chip with.
-template <typename T, int DK, int DV, int C, bool PERKEY, int NVB>
+// CKPT: also export the states a checkpoint list asks for (its own instantiation, so the
+// pass without checkpoints carries none of the bookkeeping).
+template <typename T, int DK, int DV, int C, bool PERKEY, int NVB, bool CKPT>
 __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(PrefillArgs a) {
     using F = PfCfg<T, DK, DV, C>;
     using MM = typename F::MM;
@@ -762,7 +765,10 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
     const int H = a.H;
     if (unit >= a.n_seqs * H) return;
     const int n = unit / H, h = unit - (unit / H) * H;
-    const int lane = lane_id(), w = wave_id(), r16 = lane & 15, g = lane >> 4;
+    // the wave index is uniform across a wave; saying so keeps role and checkpoint branches
+    // scalar
+    const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
+    const int r16 = lane & 15, g = lane >> 4;
     const int kq = g * KPL;
     const int vcol0 = vt * BV;
     // clamps keep inconsistent cu_seqlens inside the workspace and the token range
@@ -806,6 +812,65 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
     T* out = reinterpret_cast<T*>(a.o);
     T* dump = reinterpret_cast<T*>(a.ws.dump) + 4 * lane;  // 64 lanes x 4 elements <= 1 KiB
 
+    // the E waves write their state rows (fp32, from the accumulators) to a pool slot
+    auto store_state = [&](float* dst) {
+#pragma unroll
+        for (int j = 0; j < RBW; j++) {
+            const int rb = w + j * NB;
+            if (rb < RB) {
+#pragma unroll
+                for (int v = 0; v < NVB; v++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        dst[(size_t)(rb * 16 + 4 * g + e) * DV + vcol0 + 16 * v + r16] = acc_s[j][v][e];
+            }
+        }
+    };
+    // Checkpoints (E waves). ck.chunk is the chunk whose completion gives the next stored
+    // entry (INT_MAX: none). Entries are fetched 64 at a time, one per lane, and read back
+    // with readlane, so finding the next one issues no load unless a batch runs out.
+    struct {
+        int next, end, base, pv, sv, high, chunk, slot;
+    } ck{0, 0, 0, 0, -1, INT_MIN, INT_MAX, -1};
+    const int len = t_end - t_begin;
+    auto ck_fetch = [&]() {  // the batch of entries starting at ck.next
+        ck.base = ck.next;
+        const int i = ck.base + lane;
+        ck.pv = i < ck.end ? a.ckpt_pos[i] : 0;
+        ck.sv = i < ck.end ? a.ckpt_slots[i] : -1;
+    };
+    // Entry i is stored iff its offset p is usable (0 < p <= length, p a multiple of C or
+    // the length) and no earlier entry of the sequence has a larger offset.
+    auto ck_advance = [&]() {
+        ck.chunk = INT_MAX;
+        while (ck.next < ck.end) {
+            if (ck.next - ck.base == WAVE) ck_fetch();
+            const int p = __builtin_amdgcn_readlane(ck.pv, ck.next - ck.base);
+            const int sl = __builtin_amdgcn_readlane(ck.sv, ck.next - ck.base);
+            ck.next++;
+            const bool use = p > 0 && p <= len && (p % C == 0 || p == len) && p >= ck.high;
+            ck.high = max(ck.high, p);
+            if (use) {
+                ck.chunk = c_begin + (p + C - 1) / C - 1;
+                ck.slot = sl;
+                break;
+            }
+        }
+    };
+    if (CKPT && ewave) {
+        ck.next = max(a.ckpt_cu[n], 0);
+        ck.end = min(a.ckpt_cu[n + 1], a.n_ckpt);
+        ck_fetch();
+        ck_advance();
+    }
+    auto ck_hit = [&](int c) {  // after the state update of chunk c == ck.chunk
+        do {
+            if (ck.slot >= 0 && ck.slot < a.n_slots)
+                store_state(a.state_pool + ((size_t)ck.slot * H + h) * DK * DV);
+            ck_advance();
+        } while (ck.chunk == c);
+    };
+
     // the sequential pass for one role; both roles meet the same two barriers per chunk
     auto run = [&](auto role) {
         constexpr bool E = decltype(role)::value;
@@ -847,6 +912,7 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
         auto step = [&](const O& cur, O& nxt, int c) {
             lds_barrier();  // st holds S_c^T
             ld(part1(), nxt, c + 1);
+            sched_fence();
             f32x4 acc[NVB];
 #pragma unroll
             for (int v = 0; v < NVB; v++) acc[v] = E ? cur.u[E ? v : 0] : zero4();
@@ -866,6 +932,7 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
             }
             lds_barrier();  // et holds E_c
             ld(part0(), nxt, c + 1);
+            sched_fence();
             if constexpr (!E) {
 #pragma unroll
                 for (int kt = 0; kt < O::NK2; kt++)
@@ -896,40 +963,44 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
                 }
             } else {
                 update_state(cur);
+                if constexpr (CKPT)
+                    if (c == ck.chunk) ck_hit(c);
             }
         };
         O op0, op1;
         ld(part0(), op0, c_begin);
         ld(part1(), op0, c_begin);
-        for (int c = c_begin; c < c_end; c += 2) {
+        // two chunks per iteration, then the odd one (a break in the middle of the body
+        // compiles to a slower loop)
+        int c = c_begin;
+        for (; c + 1 < c_end; c += 2) {
             step(op0, op1, c);
-            if (c + 1 >= c_end) break;
             step(op1, op0, c + 1);
         }
+        if (c < c_end) step(op0, op1, c);
     };
     if (c_begin < c_end) {
         if (w < NB) run(std::integral_constant<bool, true>());
         else run(std::integral_constant<bool, false>());
     }
-    if (valid && ewave) {
-#pragma unroll
-        for (int j = 0; j < RBW; j++) {
-            const int rb = w + j * NB;
-            if (rb < RB) {
-#pragma unroll
-                for (int v = 0; v < NVB; v++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++)
-                        S[(size_t)(rb * 16 + 4 * g + e) * DV + vcol0 + 16 * v + r16] = acc_s[j][v][e];
-            }
-        }
-    }
+    if (valid && ewave) store_state(S);
 }
 
 // =====================================================================================
 // dispatch for one element type
 // =====================================================================================
 __global__ void seq_first_kernel(const int32_t* cu, int n_seqs, int C, int32_t* seq_first);
+
+template <typename T, int D, int C, bool PERKEY, bool CKPT>
+void scan_launch(const PrefillArgs& a, int nvb, unsigned grid, hipStream_t s) {
+    const dim3 block(ScanShape<C>::THREADS);
+    switch (nvb) {
+        case 1: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, 1, CKPT>), dim3(grid), block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, D >= 32 ? 2 : 1, CKPT>), dim3(grid), block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, D >= 64 ? 4 : 1, CKPT>), dim3(grid), block, 0, s, a); break;
+        default: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, D >= 128 ? 8 : 1, CKPT>), dim3(grid), block, 0, s, a); break;
+    }
+}
 
 template <typename T, int D, int C, bool PERKEY>
 hipError_t prefill_launch_cfg(const PrefillArgs& a, hipStream_t s) {
@@ -963,13 +1034,8 @@ hipError_t prefill_launch_cfg(const PrefillArgs& a, hipStream_t s) {
     int nvb = 1;
     while (nvb * 2 <= D / SCAN_BV && tiles / (nvb * 2) >= ncu) nvb *= 2;
     const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * (D / (SCAN_BV * nvb)));
-    const dim3 block(ScanShape<C>::THREADS);
-    switch (nvb) {
-        case 1: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, 1>), dim3(grid), block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, D >= 32 ? 2 : 1>), dim3(grid), block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, D >= 64 ? 4 : 1>), dim3(grid), block, 0, s, a); break;
-        default: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, D >= 128 ? 8 : 1>), dim3(grid), block, 0, s, a); break;
-    }
+    if (a.ckpt_cu != nullptr) scan_launch<T, D, C, PERKEY, true>(a, nvb, grid, s);
+    else scan_launch<T, D, C, PERKEY, false>(a, nvb, grid, s);
     return hipGetLastError();
 }
 

@@ -46,6 +46,8 @@ _SIGS = {
     "gdn_prefill_workspace_bytes": [_DIMS, _I, _I, _I, ctypes.POINTER(_SZ)],
     "gdn_prefill_chunked": [_DIMS, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _I, _P, _P, _P, _P,
                             _SZ, _P],
+    "gdn_prefill_chunked_ckpt": [_DIMS, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _I, _P, _P,
+                                 _P, _P, _P, _I, _P, _P, _SZ, _P],
     "gdn_decode_step": [_DIMS, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, _P],
     "gdn_deltalog_workspace_bytes": [_DIMS, _I, _I, ctypes.POINTER(_SZ)],
     "gdn_decode_deltalog": [_DIMS, _P, _P, _P, _P, _P, _POOL, _I, _P, _I, _P, _P, _SZ, _P],
@@ -162,6 +164,32 @@ def gdn_prefill_chunked(q, k, v, g, beta, cu_seqlens, chunk, state_pool, slots, 
         ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
         int(n), int(T), int(chunk), _ptr(state_pool), int(state_pool.shape[0]), _ptr(slots),
         _ptr(has_init), _ptr(o), _ptr(workspace), int(workspace.numel()), _stream(stream)))
+    return o
+
+
+def gdn_prefill_chunked_ckpt(q, k, v, g, beta, cu_seqlens, chunk, state_pool, slots,
+                             ckpt_cu, ckpt_pos, ckpt_slots, has_init=None, scale=1.0,
+                             qk_l2norm=False, o=None, workspace=None, stream=None):
+    """Chunked prefill that also writes the state after ckpt_pos[i] tokens of its sequence
+    into pool slot ckpt_slots[i]; the entries of sequence n are ckpt_cu[n]:ckpt_cu[n+1]
+    (all three int32 device tensors). Other arguments as gdn_prefill_chunked. Returns o."""
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    n = cu_seqlens.numel() - 1
+    perkey = g.dim() == 3
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+    need = gdn_prefill_workspace_bytes(H, dk, dv, _dtype_code(q), perkey, n, T, chunk)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dev(q, k, v, g, beta, cu_seqlens, state_pool, slots, has_init, ckpt_cu, ckpt_pos,
+         ckpt_slots, o, workspace)
+    dims = make_dims(H, dk, dv, _dtype_code(q), perkey, scale, qk_l2norm)
+    _check("gdn_prefill_chunked_ckpt", lib().gdn_prefill_chunked_ckpt(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+        int(n), int(T), int(chunk), _ptr(state_pool), int(state_pool.shape[0]), _ptr(slots),
+        _ptr(has_init), _ptr(ckpt_cu), _ptr(ckpt_pos), _ptr(ckpt_slots), int(ckpt_pos.numel()),
+        _ptr(o), _ptr(workspace), int(workspace.numel()), _stream(stream)))
     return o
 
 

@@ -132,6 +132,42 @@ int gdn_prefill_chunked(const gdn_dims_t* dims, const void* q, const void* k, co
                         const int32_t* has_init, void* o, void* workspace, size_t ws_bytes,
                         void* stream);
 
+/* Chunked prefill that also exports intermediate states ("internal checkpoints").
+ * A prefix cache can only resume a linear-attention layer where a state was saved, and
+ * saving one at every block boundary costs a full d_k x d_v write each time, so engines ask
+ * for states at a few chosen token offsets only. One forward then covers the whole prompt
+ * and the kernel writes the state at those offsets into slots reserved for them
+ * ([LA-Infra] "Linear Attention的Prefix Cache", part "S 到底存几份？": a backend with an
+ * internal checkpoint runs [0, 2000) in one step and exports S@1920 or S@1984 on the way;
+ * the offset from the step's first token must be a multiple of the kernel's chunk size).
+ * Arguments and results are those of gdn_prefill_chunked, plus:
+ *   ckpt_cu     [n_seqs + 1] int32 (device): the checkpoints of sequence n are entries
+ *               ckpt_cu[n] .. ckpt_cu[n + 1] - 1 (ckpt_cu[0] = 0, non-decreasing,
+ *               ckpt_cu[n_seqs] = n_ckpt)
+ *   ckpt_pos    [n_ckpt] int32 (device): token offset p within the sequence (counted from its
+ *               first token in this call); the state after the sequence's first p tokens,
+ *               starting from its initial state, is exported. An offset is usable when
+ *               0 < p <= length and (p % chunk == 0 or p == length). Entry i is stored iff
+ *               its offset is usable and no earlier entry of the same sequence has a larger
+ *               offset (entries with equal offsets all receive the state); any other entry
+ *               is skipped and writes nothing.
+ *   ckpt_slots  [n_ckpt] int32 (device): pool slot receiving the exported state (fp32,
+ *               [H, d_k, d_v], all heads); a slot outside [0, n_slots) skips the entry (a
+ *               null block). Checkpoint slots must be distinct from each other and from the
+ *               `slots` of this call (the writes of one launch are not ordered).
+ *   n_ckpt      number of entries (>= 0). With n_ckpt == 0 the three arrays may be NULL and
+ *               the call equals gdn_prefill_chunked.
+ * The exported state is bit-identical to the final state of a gdn_prefill_chunked call over
+ * the same p tokens with the same chunk size. */
+int gdn_prefill_chunked_ckpt(const gdn_dims_t* dims, const void* q, const void* k,
+                             const void* v, const float* g, const float* beta,
+                             const int32_t* cu_seqlens, int32_t n_seqs, int32_t total_tokens,
+                             int32_t chunk, float* state_pool, int32_t n_slots,
+                             const int32_t* slots, const int32_t* has_init,
+                             const int32_t* ckpt_cu, const int32_t* ckpt_pos,
+                             const int32_t* ckpt_slots, int32_t n_ckpt, void* o,
+                             void* workspace, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------------- decode */
 
 /* One recurrent step for a batch of requests, one token each, states read and written in

@@ -21,7 +21,8 @@ def _declared():
 
 def test_header_declares_the_abi():
     names = _declared()
-    for n in ("gdn_prefill_chunked", "gdn_prefill_workspace_bytes", "gdn_decode_step",
+    for n in ("gdn_prefill_chunked", "gdn_prefill_chunked_ckpt",
+              "gdn_prefill_workspace_bytes", "gdn_decode_step",
               "gdn_decode_deltalog", "gdn_deltalog_workspace_bytes", "gdn_deltalog_reset",
               "gdn_deltalog_materialize", "gdn_conv1d_silu", "gdn_status_string",
               "gdn_last_error", "gdn_abi_version"):
@@ -73,6 +74,35 @@ def _prefill(dims, ws_bytes=1 << 40, **kw):
 def test_prefill_rejects_bad_arguments(kw, status):
     assert _prefill(_dims(), **kw) == status
     assert gdn.gdn_last_error() != ""
+
+
+def _prefill_ckpt(dims, ws_bytes=1 << 40, n_ckpt=3, ckpt_cu=FAKE, ckpt_pos=FAKE,
+                  ckpt_slots=FAKE, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, cu=FAKE, n=2, T=100, chunk=64,
+             pool=FAKE, n_slots=4, slots=FAKE, has_init=None, o=FAKE, ws=FAKE)
+    a.update(kw)
+    return gdn.load().gdn_prefill_chunked_ckpt(
+        ctypes.byref(dims), a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["n"], a["T"],
+        a["chunk"], a["pool"], a["n_slots"], a["slots"], a["has_init"], ckpt_cu, ckpt_pos,
+        ckpt_slots, n_ckpt, a["o"], a["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_ckpt=-1), 2), (dict(ckpt_cu=None), 1), (dict(ckpt_pos=None), 1),
+    (dict(ckpt_slots=None), 1), (dict(ckpt_pos=FAKE + 4), 4), (dict(ckpt_slots=FAKE + 8), 4),
+    (dict(q=None), 1), (dict(chunk=8), 3), (dict(n_slots=0), 2),
+])
+def test_prefill_ckpt_rejects_bad_arguments(kw, status):
+    assert _prefill_ckpt(_dims(), **kw) == status
+    assert gdn.gdn_last_error() != ""
+
+
+def test_prefill_ckpt_zero_checkpoints_and_zero_sequences_need_no_arrays():
+    # n_seqs == 0 is a no-op before any launch; with n_ckpt == 0 the arrays may be NULL
+    assert _prefill_ckpt(_dims(), n=0, n_ckpt=0, ckpt_cu=None, ckpt_pos=None,
+                         ckpt_slots=None, q=None, ws=None) == 0
+    assert _prefill_ckpt(_dims(), n_ckpt=0, ckpt_cu=None, ckpt_pos=None, ckpt_slots=None,
+                         ws=None) == 1  # the workspace check still applies
 
 
 @pytest.mark.parametrize("dims,status", [
