@@ -159,6 +159,32 @@ def bench_decode(steps, warmup, layers=4):
                 workload="dense decode B=128 H=32 d=128, 256-slot fp32 pool, 4 rotating layers")
 
 
+def bench_spec(steps, warmup, B=128, P=4):
+    """Verify step of speculative decoding: B requests x P positions (3 drafts), H = 32,
+    d = 128, bf16 tokens, over a B*P-slot fp32 pool (1 GiB)."""
+    H, d = 32, 128
+    n_slots = B * P
+    pool = inputs.decode_pool(20, n_slots, H, d, d).to(DEV)
+    table, acc = inputs.spec_slot_table(21, n_slots, B, P)
+    table, acc = table.to(DEV), acc.to(DEV)
+    rounds = [[t.to(DEV) for t in inputs.spec_round(22 + i, B, P, H, d, d)] for i in range(2)]
+    o = torch.empty((B, P, H, d), dtype=torch.bfloat16, device=DEV)
+    it = [0]
+
+    def step():
+        q, k, v, g, b = rounds[it[0] % 2]
+        it[0] += 1
+        gdn.gdn_decode_spec(q, k, v, g, b, pool, table, acc, scale=d ** -0.5, o=o)
+
+    ms, _ = ev_time(step, steps, warmup)
+    byts = traffic.spec_bytes(B, P, H, d, d, 2, False)
+    return dict(ms_per_step=ms, GBps=byts / (ms * 1e-3) / 1e9,
+                hbm_frac=byts / (ms * 1e-3) / traffic.HBM_PEAK_BPS,
+                verified_tokens_per_s=B * P / (ms * 1e-3),
+                workload=f"spec-decode verify B={B}, {P} positions (3 drafts), H=32, d=128, "
+                         f"bf16 tokens, {n_slots}-slot fp32 pool (1 GiB)")
+
+
 def bench_deltalog(cycles=4, warm_cycles=1, M=8):
     B, H, d = 512, 32, 128
     base = inputs.decode_pool(1, B, H, d, d).to(DEV)
@@ -318,6 +344,8 @@ def main():
             line["prefill_ckpt"] = bench_prefill_ckpt(args.steps, args.warmup, p["ms"])
         log("decode ...")
         line["decode"] = bench_decode(args.steps, args.warmup)
+        log("spec verify ...")
+        line["spec_decode"] = bench_spec(args.steps, args.warmup)
         log("deltalog ...")
         line["deltalog"] = bench_deltalog()
         log("kda ...")

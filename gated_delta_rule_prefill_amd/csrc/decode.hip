@@ -18,6 +18,7 @@
 // value range, the DeltaLog key-side replay coefficients are computed once per
 // (request, head) in-workgroup and a single thread is the one writer of K_log, Lambda_log,
 // lbar and L — no separate replay-prep launch and no scratch buffer.
+#include "gdn.h"
 #include "gdn_common.h"
 #include "gdn_launch.h"
 
@@ -86,6 +87,91 @@ __device__ __forceinline__ void kq_norms(const float* ks, const float* qs, float
     kq = skq * ik * iq;
 }
 
+// One token of the gated delta rule on the state slice this thread holds in registers
+// (st[p] = S[r0 + p RPP][4 cg .. 4 cg + 3]):
+//   Sbar = Diag(decay) S;  vhat = Sbar^T k;  r = beta (v - vhat);  S <- Sbar + k r^T;
+//   o = scale S^T q = scale (Sbar^T q + (k . q) r).
+// k, q, v (fp32, unnormalised) and gk (e^{g} per key channel) are staged in LDS; ik, iq are
+// the L2 scales of k and q (1 without normalisation) and kq = (k . q) ik iq. Both column
+// reductions come from the same registers: xor-shuffles inside a wave, then one LDS
+// exchange across the waves. Returns the output column `tid` (meaningful for tid < d_v).
+// Ends with every thread past the exchange, so the caller may restage LDS afterwards only
+// behind another barrier.
+template <int DK, int DV, bool PERKEY, int NP>
+__device__ __forceinline__ float token_update(f32x4 (&st)[NP], const float* k, const float* q,
+                                              const float* v, const float* gk, float alpha,
+                                              float beta, float ik, float iq, float kq,
+                                              float scale, float (*red_v)[DV],
+                                              float (*red_q)[DV], float* rbuf) {
+    using G = DecGeom<DK, DV, DENSE_THREADS>;
+    static_assert(NP == G::NP, "state registers per thread");
+    const int tid = threadIdx.x;
+    const int cg = tid % G::TPR;
+    const int r0 = tid / G::TPR;
+    // decay and the two column reductions from the same registers
+    float pv[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
+    float kr[G::NP];
+#pragma unroll
+    for (int p = 0; p < G::NP; p++) {
+        const int r = r0 + p * G::RPP;
+        if (r < DK) {
+            const float dec = PERKEY ? gk[r] : alpha;
+            const float kk = k[r] * ik, qq = q[r] * iq;
+            kr[p] = kk;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                float s = st[p][i] * dec;
+                st[p][i] = s;
+                pv[i] += s * kk;
+                pq[i] += s * qq;
+            }
+        }
+    }
+    // reduce across the lanes of this wave that share the column group
+#pragma unroll
+    for (int off = G::TPR; off < WAVE; off <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            pv[i] += __shfl_xor(pv[i], off, WAVE);
+            pq[i] += __shfl_xor(pq[i], off, WAVE);
+        }
+    }
+    const int w = wave_id();
+    if (lane_id() < G::TPR) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            red_v[w][cg * 4 + i] = pv[i];
+            red_q[w][cg * 4 + i] = pq[i];
+        }
+    }
+    lds_barrier();
+    float out = 0.f;
+    if (tid < DV) {
+        float vh = 0.f, sh = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < G::NWAVE; ww++) {
+            vh += red_v[ww][tid];
+            sh += red_q[ww][tid];
+        }
+        const float r = beta * (v[tid] - vh);
+        rbuf[tid] = r;
+        out = scale * (sh + kq * r);
+    }
+    lds_barrier();
+    float rr[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) rr[i] = rbuf[cg * 4 + i];
+#pragma unroll
+    for (int p = 0; p < G::NP; p++) {
+        const int r = r0 + p * G::RPP;
+        if (r < DK) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) st[p][i] += kr[p] * rr[i];
+        }
+    }
+    return out;
+}
+
 template <typename T, int DK, int DV, bool PERKEY>
 __global__ __launch_bounds__(DENSE_THREADS) void decode_kernel(DecodeArgs a) {
     using G = DecGeom<DK, DV, DENSE_THREADS>;
@@ -138,67 +224,113 @@ __global__ __launch_bounds__(DENSE_THREADS) void decode_kernel(DecodeArgs a) {
 
     float ik, iq, kq;
     kq_norms<DK>(sm.k, sm.q, ik, iq, kq, a.l2norm != 0);
+    const float out = token_update<DK, DV, PERKEY>(st, sm.k, sm.q, sm.v, sm.gk, alpha, beta, ik,
+                                                   iq, kq, a.scale, sm.red_v, sm.red_q, sm.r);
+    if (tid < DV) o[tid] = from_f32<T>(out);
+#pragma unroll
+    for (int p = 0; p < G::NP; p++) {
+        const int r = r0 + p * G::RPP;
+        if (r < DK) stream_store(S + (size_t)r * DV + cg * 4, st[p]);
+    }
+}
 
-    // decay and the two column reductions from the same registers
-    float pv[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
-    float kr[G::NP];
+// Multi-token verify step of speculative decoding. Each request feeds n_pos tokens (the
+// confirmed token and the drafts); the state after every position is stored in that
+// position's slot, and the round starts from the slot of column num_accepted - 1 of the
+// previous round, so a rejected draft is rolled back by choosing a column, with no copy
+// ([LA-Infra] "推测解码：验证后如何恢复状态"; [Handbook] "投机解码与 PD 分离").
+// One workgroup per (request, head) keeps the state in registers across the positions:
+// one 64 KiB read and n_pos 64 KiB writes per head at d = 128.
+constexpr int SPEC_MAX_POS = GDN_SPEC_MAX_POS;
+
+// The reduction buffers are static; the n_pos positions' vectors live in dynamic LDS sized
+// by the call (at d = 128 and 4 positions 15 KiB in all, so 4 workgroups share a CU):
+//   k[P][DK], q[P][DK], v[P][DV], gk[P][DK] (per-key gate only), alpha[P], beta[P]
+template <int DK, int DV>
+struct SpecSmem {
+    float red_v[DecGeom<DK, DV, DENSE_THREADS>::NWAVE][DV];
+    float red_q[DecGeom<DK, DV, DENSE_THREADS>::NWAVE][DV];
+    float r[DV];
+};
+template <int DK, int DV, bool PERKEY>
+constexpr size_t spec_dyn_bytes(int P) {
+    return (size_t)P * ((PERKEY ? 3 : 2) * DK + DV + 2) * sizeof(float);
+}
+
+template <typename T, int DK, int DV, bool PERKEY>
+__global__ __launch_bounds__(DENSE_THREADS) void spec_decode_kernel(DecodeArgs a) {
+    using G = DecGeom<DK, DV, DENSE_THREADS>;
+    __shared__ SpecSmem<DK, DV> sm;
+    extern __shared__ __align__(16) float spec_dyn[];
+    const int tid = threadIdx.x;
+    const int H = a.H, P = a.n_pos;
+    float* ks = spec_dyn;
+    float* qs = ks + P * DK;
+    float* vs = qs + P * DK;
+    float* gks = vs + P * DV;
+    float* alphas = gks + (PERKEY ? P * DK : 0);
+    float* betas = alphas + P;
+    const int bh = blockIdx.x;
+    const int b = bh / H, h = bh - (bh / H) * H;
+    const int32_t* row = a.slots + (size_t)b * P;
+    const int col = a.num_accepted[b] - 1;
+    const int slot0 = (col >= 0 && col < P) ? row[col] : -1;
+    // o[b, j, h, :] lives at o + ((b P + j) H + h) d_v
+    T* o = reinterpret_cast<T*>(a.o) + ((size_t)b * P * H + h) * DV;
+    if (slot0 < 0 || slot0 >= a.n_slots) {  // inactive request: zero outputs, no state access
+        for (int i = tid; i < P * (DV / 4); i += DENSE_THREADS) {
+            float z[4] = {0.f, 0.f, 0.f, 0.f};
+            store4<T>(o + (size_t)(i / (DV / 4)) * H * DV + (i % (DV / 4)) * 4, z);
+        }
+        return;
+    }
+    const int cg = tid % G::TPR;
+    const int r0 = tid / G::TPR;
+    // all positions' vectors are staged before the state stream completes
+    const T* qp = reinterpret_cast<const T*>(a.q);
+    const T* kp = reinterpret_cast<const T*>(a.k);
+    const T* vp = reinterpret_cast<const T*>(a.v);
+    for (int i = tid; i < P * DK; i += DENSE_THREADS) {
+        const int j = i / DK, c = i - j * DK;
+        const size_t t = ((size_t)b * P + j) * H + h;
+        ks[i] = to_f32(kp[t * DK + c]);
+        qs[i] = to_f32(qp[t * DK + c]);
+        if (PERKEY) gks[i] = __expf(a.g[t * DK + c]);
+    }
+    for (int i = tid; i < P * DV; i += DENSE_THREADS) {
+        const int j = i / DV, c = i - j * DV;
+        vs[i] = to_f32(vp[(((size_t)b * P + j) * H + h) * DV + c]);
+    }
+    if (tid < P) {
+        const size_t t = ((size_t)b * P + tid) * H + h;
+        betas[tid] = a.beta[t];
+        alphas[tid] = PERKEY ? 1.f : __expf(a.g[t]);
+    }
+    const float* S0 = a.pool + ((size_t)slot0 * H + h) * DK * DV;
+    f32x4 st[G::NP];
 #pragma unroll
     for (int p = 0; p < G::NP; p++) {
         const int r = r0 + p * G::RPP;
-        if (r < DK) {
-            const float dec = PERKEY ? sm.gk[r] : alpha;
-            const float kk = sm.k[r] * ik, qq = sm.q[r] * iq;
-            kr[p] = kk;
+        if (r < DK) st[p] = stream_load(S0 + (size_t)r * DV + cg * 4);
+    }
+    lds_barrier();
+    for (int j = 0; j < P; j++) {
+        float ik, iq, kq;
+        const float* kj = ks + j * DK;
+        const float* qj = qs + j * DK;
+        kq_norms<DK>(kj, qj, ik, iq, kq, a.l2norm != 0);
+        const float out = token_update<DK, DV, PERKEY>(st, kj, qj, vs + j * DV, gks + j * DK,
+                                                       alphas[j], betas[j], ik, iq, kq,
+                                                       a.scale, sm.red_v, sm.red_q, sm.r);
+        if (tid < DV) o[(size_t)j * H * DV + tid] = from_f32<T>(out);
+        const int sj = row[j];
+        if (sj >= 0 && sj < a.n_slots) {
+            float* Sj = a.pool + ((size_t)sj * H + h) * DK * DV;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                float s = st[p][i] * dec;
-                st[p][i] = s;
-                pv[i] += s * kk;
-                pq[i] += s * qq;
+            for (int p = 0; p < G::NP; p++) {
+                const int r = r0 + p * G::RPP;
+                if (r < DK) stream_store(Sj + (size_t)r * DV + cg * 4, st[p]);
             }
-        }
-    }
-    // reduce across the lanes of this wave that share the column group
-#pragma unroll
-    for (int off = G::TPR; off < WAVE; off <<= 1) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            pv[i] += __shfl_xor(pv[i], off, WAVE);
-            pq[i] += __shfl_xor(pq[i], off, WAVE);
-        }
-    }
-    const int w = wave_id();
-    if (lane_id() < G::TPR) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            sm.red_v[w][cg * 4 + i] = pv[i];
-            sm.red_q[w][cg * 4 + i] = pq[i];
-        }
-    }
-    lds_barrier();
-    if (tid < DV) {
-        float vh = 0.f, sh = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < G::NWAVE; ww++) {
-            vh += sm.red_v[ww][tid];
-            sh += sm.red_q[ww][tid];
-        }
-        const float r = beta * (sm.v[tid] - vh);
-        sm.r[tid] = r;
-        o[tid] = from_f32<T>(a.scale * (sh + kq * r));
-    }
-    lds_barrier();
-    float rr[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) rr[i] = sm.r[cg * 4 + i];
-#pragma unroll
-    for (int p = 0; p < G::NP; p++) {
-        const int r = r0 + p * G::RPP;
-        if (r < DK) {
-            f32x4 s = st[p];
-#pragma unroll
-            for (int i = 0; i < 4; i++) s[i] += kr[p] * rr[i];
-            stream_store(S + (size_t)r * DV + cg * 4, s);
         }
     }
 }
@@ -471,10 +603,18 @@ __global__ __launch_bounds__(DEC_THREADS) void deltalog_maint_kernel(DeltaLogArg
 template <typename T, int D>
 static hipError_t dec_dispatch_gate(const DecodeArgs& a, hipStream_t s) {
     dim3 grid((unsigned)(a.batch * a.H)), block(DENSE_THREADS);
-    if (a.gate == 1)
+    if (a.num_accepted != nullptr) {
+        const size_t dyn_pk = spec_dyn_bytes<D, D, true>(a.n_pos);
+        const size_t dyn_sc = spec_dyn_bytes<D, D, false>(a.n_pos);
+        if (a.gate == 1)
+            hipLaunchKernelGGL((spec_decode_kernel<T, D, D, true>), grid, block, dyn_pk, s, a);
+        else
+            hipLaunchKernelGGL((spec_decode_kernel<T, D, D, false>), grid, block, dyn_sc, s, a);
+    } else if (a.gate == 1) {
         hipLaunchKernelGGL((decode_kernel<T, D, D, true>), grid, block, 0, s, a);
-    else
+    } else {
         hipLaunchKernelGGL((decode_kernel<T, D, D, false>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -157,6 +157,49 @@ int prefill_run(const gdn_dims_t* dims, const void* q, const void* k, const void
     return launch_status(gdn::launch_prefill(a, static_cast<hipStream_t>(stream)), what);
 }
 
+// Shared by gdn_decode_step (spec = false: one token, num_accepted unused) and
+// gdn_decode_spec (spec = true: n_pos tokens per request, num_accepted required).
+int decode_run(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
+               const float* g, const float* beta, float* state_pool, int32_t n_slots,
+               const int32_t* slots, bool spec, const int32_t* num_accepted, int32_t batch,
+               int32_t n_pos, void* o, void* stream, const char* what) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (batch < 0) return fail(GDN_ERR_SHAPE, "batch must be >= 0 (got %d)", batch);
+    if (batch == 0) return ok();
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(g);
+    REQUIRE_PTR(beta);
+    REQUIRE_PTR(state_pool);
+    REQUIRE_PTR(slots);
+    REQUIRE_PTR(o);
+    if (spec) REQUIRE_PTR(num_accepted);
+    if (n_slots < 1) return fail(GDN_ERR_SHAPE, "n_slots must be >= 1 (got %d)", n_slots);
+    gdn::DecodeArgs a;
+    a.dtype = dims->dtype;
+    a.gate = dims->gate;
+    a.H = dims->num_heads;
+    a.dk = dims->d_k;
+    a.dv = dims->d_v;
+    a.l2norm = dims->qk_l2norm;
+    a.scale = dims->scale;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.pool = state_pool;
+    a.n_slots = n_slots;
+    a.slots = slots;
+    a.batch = batch;
+    a.o = o;
+    a.num_accepted = spec ? num_accepted : nullptr;
+    a.n_pos = n_pos;
+    return launch_status(gdn::launch_decode(a, static_cast<hipStream_t>(stream)), what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -198,39 +241,19 @@ int gdn_prefill_chunked_ckpt(const gdn_dims_t* dims, const void* q, const void* 
 int gdn_decode_step(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
                     const float* g, const float* beta, float* state_pool, int32_t n_slots,
                     const int32_t* slots, int32_t batch, void* o, void* stream) {
-    int st = check_dims(dims);
-    if (st) return st;
-    if (batch < 0) return fail(GDN_ERR_SHAPE, "batch must be >= 0 (got %d)", batch);
-    if (batch == 0) return ok();
-    REQUIRE_PTR(q);
-    REQUIRE_PTR(k);
-    REQUIRE_PTR(v);
-    REQUIRE_PTR(g);
-    REQUIRE_PTR(beta);
-    REQUIRE_PTR(state_pool);
-    REQUIRE_PTR(slots);
-    REQUIRE_PTR(o);
-    if (n_slots < 1) return fail(GDN_ERR_SHAPE, "n_slots must be >= 1 (got %d)", n_slots);
-    gdn::DecodeArgs a;
-    a.dtype = dims->dtype;
-    a.gate = dims->gate;
-    a.H = dims->num_heads;
-    a.dk = dims->d_k;
-    a.dv = dims->d_v;
-    a.l2norm = dims->qk_l2norm;
-    a.scale = dims->scale;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.g = g;
-    a.beta = beta;
-    a.pool = state_pool;
-    a.n_slots = n_slots;
-    a.slots = slots;
-    a.batch = batch;
-    a.o = o;
-    return launch_status(gdn::launch_decode(a, static_cast<hipStream_t>(stream)),
-                         "gdn_decode_step");
+    return decode_run(dims, q, k, v, g, beta, state_pool, n_slots, slots, false, nullptr, batch,
+                      1, o, stream, "gdn_decode_step");
+}
+
+int gdn_decode_spec(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
+                    const float* g, const float* beta, float* state_pool, int32_t n_slots,
+                    const int32_t* spec_slots, const int32_t* num_accepted, int32_t batch,
+                    int32_t n_pos, void* o, void* stream) {
+    if (n_pos < 1 || n_pos > GDN_SPEC_MAX_POS)
+        return fail(GDN_ERR_UNSUPPORTED, "n_pos must be in [1, %d] (got %d)", GDN_SPEC_MAX_POS,
+                    n_pos);
+    return decode_run(dims, q, k, v, g, beta, state_pool, n_slots, spec_slots, true,
+                      num_accepted, batch, n_pos, o, stream, "gdn_decode_spec");
 }
 
 int gdn_deltalog_workspace_bytes(const gdn_dims_t* dims, int32_t batch, int32_t M,

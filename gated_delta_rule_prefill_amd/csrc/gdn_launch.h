@@ -71,9 +71,13 @@ struct DecodeArgs {
     const float *g, *beta;
     float* pool;
     int n_slots;
-    const int32_t* slots;
+    const int32_t* slots;  // [batch] (one token), or [batch][n_pos] (verify step)
     int batch;
     void* o;
+    // verify step of speculative decoding (null / 1 for the one-token step): n_pos tokens
+    // per request, the initial state read from slots[b][num_accepted[b] - 1]
+    const int32_t* num_accepted;
+    int n_pos;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -49,6 +49,7 @@ _SIGS = {
     "gdn_prefill_chunked_ckpt": [_DIMS, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _I, _P, _P,
                                  _P, _P, _P, _I, _P, _P, _SZ, _P],
     "gdn_decode_step": [_DIMS, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, _P],
+    "gdn_decode_spec": [_DIMS, _P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _P, _P],
     "gdn_deltalog_workspace_bytes": [_DIMS, _I, _I, ctypes.POINTER(_SZ)],
     "gdn_decode_deltalog": [_DIMS, _P, _P, _P, _P, _P, _POOL, _I, _P, _I, _P, _P, _SZ, _P],
     "gdn_deltalog_reset": [_DIMS, _POOL, _I, _P, _I, _P],
@@ -211,6 +212,25 @@ def gdn_decode_step(q, k, v, g, beta, state_pool, slots, scale=1.0, qk_l2norm=Fa
 
 
 # --------------------------------------------------------------------------- DeltaLog
+def gdn_decode_spec(q, k, v, g, beta, state_pool, spec_slots, num_accepted, scale=1.0,
+                    qk_l2norm=False, o=None, stream=None):
+    """Speculative-decoding verify step. q, k [B,P,H,dk]; v [B,P,H,dv]; g [B,P,H] or
+    [B,P,H,dk] fp32; beta [B,P,H] fp32; state_pool [slots,H,dk,dv] fp32; spec_slots [B,P]
+    int32; num_accepted [B] int32. Returns o [B,P,H,dv]."""
+    B, P, H, dk = q.shape
+    dv = v.shape[3]
+    perkey = g.dim() == 4
+    if o is None:
+        o = torch.empty((B, P, H, dv), dtype=q.dtype, device=q.device)
+    _dev(q, k, v, g, beta, state_pool, spec_slots, num_accepted, o)
+    dims = make_dims(H, dk, dv, _dtype_code(q), perkey, scale, qk_l2norm)
+    _check("gdn_decode_spec", lib().gdn_decode_spec(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
+        int(state_pool.shape[0]), _ptr(spec_slots), _ptr(num_accepted), int(B), int(P), _ptr(o),
+        _stream(stream)))
+    return o
+
+
 class DeltaLogPool:
     """Device buffers of a DeltaLog state pool (layouts of gdn_deltalog_pool_t)."""
 

@@ -172,6 +172,26 @@ class DecodeStream:
                 beta_from_normal(b).contiguous())
 
 
+def spec_round(seed: int, batch: int, n_pos: int, H: int, dk: int, dv: int, dtype=BF16,
+               perkey: bool = False, prenorm: bool = True):
+    """One verify round of speculative decoding: n_pos tokens per request, drawn as the
+    one-token decode recipe for batch * n_pos rows and laid out [batch, n_pos, H, d]."""
+    q, k, v, g, b = DecodeStream(seed, batch * n_pos, H, dk, dv, dtype=dtype, perkey=perkey,
+                                 prenorm=prenorm).next()
+    shp = (batch, n_pos)
+    return (q.view(*shp, H, dk), k.view(*shp, H, dk), v.view(*shp, H, dv),
+            g.view(*shp, *g.shape[1:]), b.view(*shp, H))
+
+
+def spec_slot_table(seed: int, n_slots: int, batch: int, n_pos: int):
+    """Distinct pool slots per (request, position) ([batch, n_pos] int32, a random
+    permutation prefix) and num_accepted in [1, n_pos] per request."""
+    gen = _gen(seed)
+    table = torch.randperm(n_slots, generator=gen)[:batch * n_pos].view(batch, n_pos)
+    acc = torch.randint(1, n_pos + 1, (batch,), generator=gen)
+    return table.to(torch.int32).contiguous(), acc.to(torch.int32).contiguous()
+
+
 @dataclass
 class KdaVarlenInputs:
     x: torch.Tensor           # [T, 3*H*d] bf16, raw fused q|k|v projection output

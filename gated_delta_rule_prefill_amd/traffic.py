@@ -90,3 +90,12 @@ class DeltaLogModel:
 
     def profitable(self):
         return self.c_state * (1 - 1.0 / self.M) > self.c_log() + 2 * self.c_decay
+
+
+def spec_bytes(B: int, n_pos: int, H: int, dk: int, dv: int, e: int, perkey: bool) -> int:
+    """Verify step of speculative decoding: per (request, head) one fp32 state read and
+    n_pos state writes, plus the n_pos tokens' q, k, v, gates and the outputs."""
+    state = 4 * dk * dv
+    per_tok = (2 * dk + 2 * dv) * e + 4 * (dk if perkey else 1) + 4
+    return B * H * (state * (1 + n_pos) + n_pos * per_tok) + 4 * B * n_pos + 4 * B
+

@@ -187,6 +187,41 @@ int gdn_decode_step(const gdn_dims_t* dims, const void* q, const void* k, const 
                     const float* g, const float* beta, float* state_pool, int32_t n_slots,
                     const int32_t* slots, int32_t batch, void* o, void* stream);
 
+/* Largest number of tokens per request in one gdn_decode_spec call. */
+#define GDN_SPEC_MAX_POS 16
+
+/* Verify step of speculative decoding: every request feeds n_pos tokens (the last confirmed
+ * token and n_pos - 1 draft tokens) through the recurrence of gdn_decode_step, and the state
+ * after each position is kept in a slot of its own, so that after verification the next
+ * round can continue from the state of the last accepted position by choosing its slot
+ * instead of copying it back ([LA-Infra] "推测解码：验证后如何恢复状态": one slot per
+ * candidate position in a [requests, 1 + num_spec] index table, the next round reading
+ * state_pool[table[r, num_accepted - 1]]; [Handbook] "投机解码与 PD 分离").
+ * Per request b and head h, with c = num_accepted[b] - 1:
+ *   S = pool[spec_slots[b, c]];
+ *   for j = 0 .. n_pos - 1:  S <- step(S, token (b, j));  o[b, j] = scale S^T q_{b,j};
+ *                            pool[spec_slots[b, j]] = S.
+ *   q, k        [batch, n_pos, H, d_k] dtype;  v, o [batch, n_pos, H, d_v] dtype
+ *   g           [batch, n_pos, H] or [batch, n_pos, H, d_k] fp32;  beta [batch, n_pos, H] fp32
+ *   state_pool  [n_slots, H, d_k, d_v] fp32
+ *   spec_slots  [batch, n_pos] int32 (device): the request's slot for each position. A slot
+ *               outside [0, n_slots) at position j means "do not keep this state" (the
+ *               position is still computed). Valid slots must be distinct within one call;
+ *               the starting slot spec_slots[b, c] is among them and is read before it is
+ *               overwritten at position c.
+ *   num_accepted [batch] int32 (device): 1 + the number of draft tokens accepted in the
+ *               previous round (1 for a request that just left prefill, its state in
+ *               spec_slots[b, 0]). A request whose c is outside [0, n_pos), or whose starting
+ *               slot is outside [0, n_slots), is inactive: its outputs are zeros and no
+ *               state is read or written.
+ *   n_pos       1 .. GDN_SPEC_MAX_POS (GDN_ERR_UNSUPPORTED otherwise)
+ * batch == 0 is a valid no-op. With n_pos == 1 and num_accepted == 1 the call computes
+ * exactly what gdn_decode_step computes, bit for bit. */
+int gdn_decode_spec(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
+                    const float* g, const float* beta, float* state_pool, int32_t n_slots,
+                    const int32_t* spec_slots, const int32_t* num_accepted, int32_t batch,
+                    int32_t n_pos, void* o, void* stream);
+
 /* ----------------------------------------------------------------------------- DeltaLog */
 
 /* DeltaLog state pool ([DeltaLog] §2.1 symbol table). All arrays are device memory:

@@ -22,7 +22,7 @@ def _declared():
 def test_header_declares_the_abi():
     names = _declared()
     for n in ("gdn_prefill_chunked", "gdn_prefill_chunked_ckpt",
-              "gdn_prefill_workspace_bytes", "gdn_decode_step",
+              "gdn_prefill_workspace_bytes", "gdn_decode_step", "gdn_decode_spec",
               "gdn_decode_deltalog", "gdn_deltalog_workspace_bytes", "gdn_deltalog_reset",
               "gdn_deltalog_materialize", "gdn_conv1d_silu", "gdn_status_string",
               "gdn_last_error", "gdn_abi_version"):
@@ -146,6 +146,28 @@ def test_decode_rejects_bad_arguments():
     assert lib.gdn_decode_step(ctypes.byref(d), None, *args[1:], 4, FAKE, 8, FAKE, None) == 1
     assert lib.gdn_decode_step(ctypes.byref(d), *args, 0, FAKE, 8, FAKE, None) == 2
     assert lib.gdn_decode_step(None, *args, 4, FAKE, 8, FAKE, None) == 1
+
+
+def _spec(dims, n_pos=4, batch=8, num_accepted=FAKE, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, pool=FAKE, n_slots=64, slots=FAKE, o=FAKE)
+    a.update(kw)
+    return gdn.load().gdn_decode_spec(
+        ctypes.byref(dims), a["q"], a["k"], a["v"], a["g"], a["beta"], a["pool"], a["n_slots"],
+        a["slots"], num_accepted, batch, n_pos, a["o"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_pos=0), 3), (dict(n_pos=17), 3), (dict(num_accepted=None), 1),
+    (dict(num_accepted=FAKE + 4), 4), (dict(slots=None), 1), (dict(q=FAKE + 2), 4),
+    (dict(batch=-1), 2), (dict(n_slots=0), 2),
+])
+def test_decode_spec_rejects_bad_arguments(kw, status):
+    assert _spec(_dims(), **kw) == status
+    assert gdn.gdn_last_error() != ""
+
+
+def test_decode_spec_zero_batch_is_a_noop():
+    assert _spec(_dims(), batch=0, q=None, num_accepted=None) == 0
 
 
 def test_deltalog_rejects_bad_arguments():
