@@ -185,15 +185,17 @@ def bench_spec(steps, warmup, B=128, P=4):
                          f"bf16 tokens, {n_slots}-slot fp32 pool (1 GiB)")
 
 
-def bench_deltalog(cycles=4, warm_cycles=1, M=8):
+def bench_deltalog(cycles=4, warm_cycles=1, M=8, perkey=False):
+    """DeltaLog decode vs the dense decode step on the same inputs, averaged over whole merge
+    cycles; perkey: the KDA variant (per-key decay, lbar and Lambda d_k wide)."""
     B, H, d = 512, 32, 128
     base = inputs.decode_pool(1, B, H, d, d).to(DEV)
     slots = inputs.decode_slots(0, B, B).to(DEV)
-    stream = inputs.DecodeStream(0, B, H, d, d)
+    stream = inputs.DecodeStream(0, B, H, d, d, perkey=perkey)
     toks = [[t.to(DEV) for t in stream.next()] for _ in range(M)]
     o = torch.empty((B, H, d), dtype=torch.bfloat16, device=DEV)
     dense = base.clone()
-    pool = gdn.DeltaLogPool(base, M)
+    pool = gdn.DeltaLogPool(base, M, perkey=perkey)
     it = [0]
 
     def dl_step():
@@ -209,14 +211,15 @@ def bench_deltalog(cycles=4, warm_cycles=1, M=8):
     ms_dl, _ = ev_time(dl_step, cycles * M, warm_cycles * M)   # whole merge cycles
     it[0] = 0
     ms_dn, _ = ev_time(dense_step, cycles * M, warm_cycles * M)
-    m = traffic.DeltaLogModel(B, H, d, d, M)
-    common = traffic.decode_bytes(B, H, d, d, 2, False) - 2 * m.c_state
+    m = traffic.DeltaLogModel(B, H, d, d, M, d_lambda=d if perkey else 1)
+    common = traffic.decode_bytes(B, H, d, d, 2, perkey) - 2 * m.c_state
     return dict(ms_dense=ms_dn, ms_deltalog_cycle_avg=ms_dl, speedup=ms_dn / ms_dl,
                 dense_GBps=m.t_dense(common) / (ms_dn * 1e-3) / 1e9,
                 deltalog_model_GBps=m.t_delta(common) / (ms_dl * 1e-3) / 1e9,
                 modelled_speedup=m.t_dense(common) / m.t_delta(common),
                 tokens_per_s_dense=B / (ms_dn * 1e-3), tokens_per_s_deltalog=B / (ms_dl * 1e-3),
-                workload="B=512 H=32 d=128 fp32 state (1 GiB), M=8, cycle average")
+                workload=f"B=512 H=32 d=128 fp32 state (1 GiB), M={M}, cycle average"
+                         + (", per-key (KDA) decay" if perkey else ""))
 
 
 def bench_kda(steps=3, warmup=1):
@@ -348,6 +351,8 @@ def main():
         line["spec_decode"] = bench_spec(args.steps, args.warmup)
         log("deltalog ...")
         line["deltalog"] = bench_deltalog()
+        log("kda deltalog ...")
+        line["deltalog_kda"] = bench_deltalog(M=4, perkey=True)
         log("kda ...")
         line["kda_prefill"] = bench_kda()
     if not args.no_cpu:

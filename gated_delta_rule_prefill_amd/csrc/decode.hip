@@ -336,12 +336,15 @@ __global__ __launch_bounds__(DENSE_THREADS) void spec_decode_kernel(DecodeArgs a
 }
 
 // ------------------------------------------------------------------------------ DeltaLog
-template <int DK, int DV>
+template <int DK, int DV, bool PERKEY>
 struct DlSmem {
     float k[DK];
     float q[DK];
     float v[DV];
-    float klog[DL_MAXLOG][DK];
+    float klog[DL_MAXLOG][DK];     // logged keys; per-key gate: replaced by the decayed keys
+    float lamk[PERKEY ? DL_MAXLOG : 1][DK];  // per-key Lambda_i
+    float lp[PERKEY ? DK : 1];     // per-key lbar' = lbar + g
+    float dk[PERKEY ? DK : 1];     // per-key e^{lbar'}
     alignas(16) float ulog[DL_MAXLOG][DV];
     float lam[DL_MAXLOG];
     float ck[DL_MAXLOG];  // e^{lp - Lambda_i} (k . K_i)
@@ -352,10 +355,15 @@ struct DlSmem {
     float b[DV];
 };
 
-template <typename T, int DK, int DV>
+// PERKEY: KDA-style per-key-channel decay. lbar and every Lambda_i are d_k wide, D(x) is
+// diag(e^x) over key rows, so the replay of entry i weighs key channel c by
+// e^{lbar'_c - Lambda_{i,c}}: the logged key is replaced in LDS by that decayed key, and the
+// replay coefficients and the merge then use it unchanged ([DeltaLog] §2.7, the KDA row).
+template <typename T, int DK, int DV, bool PERKEY>
 __global__ __launch_bounds__(DENSE_THREADS) void deltalog_kernel(DeltaLogArgs a) {
     using G = DecGeom<DK, DV, DENSE_THREADS>;
-    __shared__ DlSmem<DK, DV> sm;
+    __shared__ DlSmem<DK, DV, PERKEY> sm;
+    constexpr int DL = PERKEY ? DK : 1;  // width of lbar and Lambda
     const int tid = threadIdx.x;
     const int H = a.H;
     const int bh = blockIdx.x;
@@ -381,20 +389,30 @@ __global__ __launch_bounds__(DENSE_THREADS) void deltalog_kernel(DeltaLogArgs a)
     // do not wait behind the 64 KiB base read.
     const uint16_t* kl = a.klog + sh * C * DK;
     const float* ul = a.ulog + sh * C * DV;
+    const float* lamp = a.lamlog + sh * C * DL;
     constexpr int KPIECES = DL_MAXLOG * DK / 8, UPIECES = DL_MAXLOG * DV / 4;
-    static_assert(KPIECES <= DENSE_THREADS && UPIECES <= DENSE_THREADS, "one piece per thread");
+    static_assert(KPIECES <= DENSE_THREADS && UPIECES <= DENSE_THREADS &&
+                  DL_MAXLOG * DK / 4 <= DENSE_THREADS, "one piece per thread");
     const bool kpiece = tid * 8 < L * DK, upiece = tid * 4 < L * DV;
+    const bool lpiece = PERKEY && tid * 4 < L * DK;
     bf16x8 kraw;
-    f32x4 uraw;
+    f32x4 uraw, lraw;
     if (kpiece) kraw = *reinterpret_cast<const bf16x8*>(kl + tid * 8);
     if (upiece) uraw = *reinterpret_cast<const f32x4*>(ul + tid * 4);
+    if (lpiece) lraw = *reinterpret_cast<const f32x4*>(lamp + tid * 4);
     f32x4 st[G::NP];
 #pragma unroll
     for (int p = 0; p < G::NP; p++) {
         const int r = r0 + p * G::RPP;
         if (r < DK) st[p] = stream_load(S + (size_t)r * DV + cg * 4);
     }
-    const float lp = a.lbar[sh] + a.g[bh];  // Algorithm 1: accumulate the decay first
+    // Algorithm 1: accumulate the decay first
+    const float lp = PERKEY ? 0.f : a.lbar[sh] + a.g[bh];
+    if (PERKEY && tid < DK) {
+        const float x = a.lbar[sh * DK + tid] + a.g[(size_t)bh * DK + tid];
+        sm.lp[tid] = x;
+        sm.dk[tid] = __expf(x);
+    }
     const T* qp = reinterpret_cast<const T*>(a.q) + (size_t)bh * DK;
     const T* kp = reinterpret_cast<const T*>(a.k) + (size_t)bh * DK;
     const T* vp = reinterpret_cast<const T*>(a.v) + (size_t)bh * DV;
@@ -412,7 +430,11 @@ __global__ __launch_bounds__(DENSE_THREADS) void deltalog_kernel(DeltaLogArgs a)
         const int e = tid * 4 / DV, c0 = tid * 4 % DV;
         *reinterpret_cast<f32x4*>(&sm.ulog[e][c0]) = uraw;
     }
-    if (tid < L) {
+    if (lpiece) {
+        const int e = tid * 4 / DK, c0 = tid * 4 % DK;
+        *reinterpret_cast<f32x4*>(&sm.lamk[e][c0]) = lraw;
+    }
+    if (!PERKEY && tid < L) {
         float lam = a.lamlog[sh * C + tid];
         sm.lam[tid] = lam;
         sm.wl[tid] = __expf(lp - lam);
@@ -428,24 +450,31 @@ __global__ __launch_bounds__(DENSE_THREADS) void deltalog_kernel(DeltaLogArgs a)
         for (int e = w; e < L; e += G::NWAVE) {
             float sk = 0.f, sq = 0.f;
             for (int i = l; i < DK; i += WAVE) {
-                sk += sm.k[i] * sm.klog[e][i];
-                sq += sm.q[i] * sm.klog[e][i];
+                float ke = sm.klog[e][i];
+                if (PERKEY) {  // decayed key, kept for the merge
+                    ke *= __expf(sm.lp[i] - sm.lamk[e][i]);
+                    sm.klog[e][i] = ke;
+                }
+                sk += sm.k[i] * ke;
+                sq += sm.q[i] * ke;
             }
             sk = group_sum<WAVE>(sk);
             sq = group_sum<WAVE>(sq);
             if (l == 0) {
-                sm.ck[e] = sm.wl[e] * sk * ik;
-                sm.cq[e] = sm.wl[e] * sq * iq;
+                sm.ck[e] = (PERKEY ? 1.f : sm.wl[e]) * sk * ik;
+                sm.cq[e] = (PERKEY ? 1.f : sm.wl[e]) * sq * iq;
             }
         }
     }
-    // base reads (undecayed base; the scalar factor e^{lp} is applied after the reduction)
+    // base reads (undecayed base; the scalar factor e^{lp} is applied after the reduction,
+    // a per-key factor with the key row)
     float pv[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int p = 0; p < G::NP; p++) {
         const int r = r0 + p * G::RPP;
         if (r < DK) {
-            const float kk = sm.k[r] * ik, qq = sm.q[r] * iq;
+            const float dr = PERKEY ? sm.dk[r] : 1.f;
+            const float kk = sm.k[r] * ik * dr, qq = sm.q[r] * iq * dr;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 pv[i] += st[p][i] * kk;
@@ -472,7 +501,7 @@ __global__ __launch_bounds__(DENSE_THREADS) void deltalog_kernel(DeltaLogArgs a)
         }
     }
     lds_barrier();
-    const float dec = __expf(lp);
+    const float dec = PERKEY ? 1.f : __expf(lp);
     if (tid < DV) {
         float vh = 0.f, shq = 0.f;
 #pragma unroll
@@ -499,11 +528,16 @@ __global__ __launch_bounds__(DENSE_THREADS) void deltalog_kernel(DeltaLogArgs a)
             bf16 kb = (bf16)(sm.k[tid] * ik);
             a.klog[(sh * C + L) * DK + tid] = __builtin_bit_cast(uint16_t, kb);
         }
-        if (tid == 0) {
+        if (PERKEY) {
+            if (tid < DK) {
+                a.lamlog[(sh * C + L) * DK + tid] = sm.lp[tid];
+                a.lbar[sh * DK + tid] = sm.lp[tid];
+            }
+        } else if (tid == 0) {
             a.lamlog[sh * C + L] = lp;
             a.lbar[sh] = lp;
-            a.len[sh] = L + 1;
         }
+        if (tid == 0) a.len[sh] = L + 1;
         return;
     }
     // merge (Eq. 6): fold the log and the current update into the base, clear the log.
@@ -518,13 +552,14 @@ __global__ __launch_bounds__(DENSE_THREADS) void deltalog_kernel(DeltaLogArgs a)
         const int r = r0 + p * G::RPP;
         if (r < DK) {
             const float kk = sm.k[r] * ik;
+            const float dr = PERKEY ? sm.dk[r] : dec;
 #pragma unroll
-            for (int i = 0; i < 4; i++) st[p][i] = st[p][i] * dec + kk * bb[i];
+            for (int i = 0; i < 4; i++) st[p][i] = st[p][i] * dr + kk * bb[i];
         }
     }
     for (int e = 0; e < L; e++) {
         const f32x4 ue = *reinterpret_cast<const f32x4*>(&sm.ulog[e][cg * 4]);
-        const float we = sm.wl[e];
+        const float we = PERKEY ? 1.f : sm.wl[e];  // per key: klog holds the decayed key
 #pragma unroll
         for (int p = 0; p < G::NP; p++) {
             const int r = r0 + p * G::RPP;
@@ -540,19 +575,19 @@ __global__ __launch_bounds__(DENSE_THREADS) void deltalog_kernel(DeltaLogArgs a)
         const int r = r0 + p * G::RPP;
         if (r < DK) stream_store(S + (size_t)r * DV + cg * 4, st[p]);
     }
-    if (tid == 0) {
-        a.lbar[sh] = 0.f;
-        a.len[sh] = 0;
-    }
+    if (tid < DL) a.lbar[sh * DL + tid] = 0.f;
+    if (tid == 0) a.len[sh] = 0;
 }
 
 // reset (mode 0) or materialize (mode 1) the listed slots; grid = n * H
-template <int DK, int DV>
+template <int DK, int DV, bool PERKEY>
 __global__ __launch_bounds__(DEC_THREADS) void deltalog_maint_kernel(DeltaLogArgs a, int mode) {
     using G = DecGeom<DK, DV>;
-    __shared__ float klog[DL_MAXLOG][DK];
+    constexpr int DL = PERKEY ? DK : 1;
+    __shared__ float klog[DL_MAXLOG][DK];  // per key: the decayed keys
     __shared__ float ulog[DL_MAXLOG][DV];
     __shared__ float wl[DL_MAXLOG];
+    __shared__ float dk[PERKEY ? DK : 1];
     const int tid = threadIdx.x;
     const int H = a.H;
     const int n = blockIdx.x / H, h = blockIdx.x % H;
@@ -562,17 +597,21 @@ __global__ __launch_bounds__(DEC_THREADS) void deltalog_maint_kernel(DeltaLogArg
     if (mode == 1) {
         const int C = a.M - 1;
         const int L = min(max(a.len[sh], 0), C);
-        const float lb = a.lbar[sh];
+        const float* lb = a.lbar + sh * DL;
         const uint16_t* kl = a.klog + sh * C * DK;
         const float* ul = a.ulog + sh * C * DV;
+        const float* lam = a.lamlog + sh * C * DL;
         for (int i = tid; i < L * DK; i += DEC_THREADS) {
             uint32_t bits = (uint32_t)kl[i] << 16;
-            klog[i / DK][i % DK] = __builtin_bit_cast(float, bits);
+            float kv = __builtin_bit_cast(float, bits);
+            if (PERKEY) kv *= __expf(lb[i % DK] - lam[i]);
+            klog[i / DK][i % DK] = kv;
         }
         for (int i = tid; i < L * DV; i += DEC_THREADS) ulog[i / DV][i % DV] = ul[i];
-        if (tid < L) wl[tid] = __expf(lb - a.lamlog[sh * C + tid]);
+        if (!PERKEY && tid < L) wl[tid] = __expf(lb[0] - lam[tid]);
+        if (PERKEY && tid < DK) dk[tid] = __expf(lb[tid]);
         lds_barrier();
-        const float dec = __expf(lb);
+        const float dec = PERKEY ? 1.f : __expf(lb[0]);
         const int cg = tid % G::TPR;
         const int r0 = tid / G::TPR;
         float* S = a.base + sh * DK * DV;
@@ -581,10 +620,11 @@ __global__ __launch_bounds__(DEC_THREADS) void deltalog_maint_kernel(DeltaLogArg
             const int r = r0 + p * G::RPP;
             if (r < DK) {
                 f32x4 s = *reinterpret_cast<const f32x4*>(S + (size_t)r * DV + cg * 4);
+                const float dr = PERKEY ? dk[r] : dec;
 #pragma unroll
-                for (int i = 0; i < 4; i++) s[i] *= dec;
+                for (int i = 0; i < 4; i++) s[i] *= dr;
                 for (int e = 0; e < L; e++) {
-                    const float we = wl[e] * klog[e][r];
+                    const float we = (PERKEY ? 1.f : wl[e]) * klog[e][r];
 #pragma unroll
                     for (int i = 0; i < 4; i++) s[i] += we * ulog[e][cg * 4 + i];
                 }
@@ -593,10 +633,8 @@ __global__ __launch_bounds__(DEC_THREADS) void deltalog_maint_kernel(DeltaLogArg
         }
         lds_barrier();
     }
-    if (tid == 0) {
-        a.lbar[sh] = 0.f;
-        a.len[sh] = 0;
-    }
+    if (tid < DL) a.lbar[sh * DL + tid] = 0.f;
+    if (tid == 0) a.len[sh] = 0;
 }
 
 // ------------------------------------------------------------------------------- launch
@@ -638,7 +676,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
 template <typename T, int D>
 static hipError_t dl_launch(const DeltaLogArgs& a, hipStream_t s) {
     dim3 grid((unsigned)(a.batch * a.H)), block(DENSE_THREADS);
-    hipLaunchKernelGGL((deltalog_kernel<T, D, D>), grid, block, 0, s, a);
+    if (a.gate == 1)
+        hipLaunchKernelGGL((deltalog_kernel<T, D, D, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((deltalog_kernel<T, D, D, false>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
@@ -662,7 +703,10 @@ hipError_t launch_deltalog(const DeltaLogArgs& a, hipStream_t s) {
 template <int D>
 static hipError_t dlm_launch(const DeltaLogArgs& a, int mode, hipStream_t s) {
     dim3 grid((unsigned)(a.batch * a.H)), block(DEC_THREADS);
-    hipLaunchKernelGGL((deltalog_maint_kernel<D, D>), grid, block, 0, s, a, mode);
+    if (a.gate == 1)
+        hipLaunchKernelGGL((deltalog_maint_kernel<D, D, true>), grid, block, 0, s, a, mode);
+    else
+        hipLaunchKernelGGL((deltalog_maint_kernel<D, D, false>), grid, block, 0, s, a, mode);
     return hipGetLastError();
 }
 

@@ -271,6 +271,7 @@ static gdn::DeltaLogArgs dl_args(const gdn_dims_t* dims, const gdn_deltalog_pool
                                  int32_t n_slots, const int32_t* slots, int32_t n) {
     gdn::DeltaLogArgs a = {};
     a.dtype = dims->dtype;
+    a.gate = dims->gate;
     a.H = dims->num_heads;
     a.dk = dims->d_k;
     a.dv = dims->d_v;
@@ -297,8 +298,6 @@ int gdn_decode_deltalog(const gdn_dims_t* dims, const void* q, const void* k, co
     (void)ws_bytes;
     int st = check_dims(dims);
     if (st) return st;
-    if (dims->gate != GDN_GATE_SCALAR)
-        return fail(GDN_ERR_UNSUPPORTED, "DeltaLog decode supports the scalar gate only");
     if (batch < 0) return fail(GDN_ERR_SHAPE, "batch must be >= 0 (got %d)", batch);
     st = deltalog_pool_checks(pool);
     if (st) return st;
@@ -327,8 +326,6 @@ static int deltalog_maint(const gdn_dims_t* dims, const gdn_deltalog_pool_t* poo
                           int mode, const char* what) {
     int st = check_dims(dims);
     if (st) return st;
-    if (dims->gate != GDN_GATE_SCALAR)
-        return fail(GDN_ERR_UNSUPPORTED, "DeltaLog supports the scalar gate only");
     st = deltalog_pool_checks(pool);
     if (st) return st;
     if (n < 0) return fail(GDN_ERR_SHAPE, "n must be >= 0 (got %d)", n);

@@ -82,7 +82,7 @@ struct DecodeArgs {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 struct DeltaLogArgs {
-    int dtype, H, dk, dv, l2norm, M;
+    int dtype, gate, H, dk, dv, l2norm, M;  // gate 1: lbar and Lambda are d_k wide
     float scale;
     const void *q, *k, *v;
     const float *g, *beta;

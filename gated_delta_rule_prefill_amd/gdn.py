@@ -234,16 +234,18 @@ def gdn_decode_spec(q, k, v, g, beta, state_pool, spec_slots, num_accepted, scal
 class DeltaLogPool:
     """Device buffers of a DeltaLog state pool (layouts of gdn_deltalog_pool_t)."""
 
-    def __init__(self, base, M):
+    def __init__(self, base, M, perkey=False):
         n_slots, H, dk, dv = base.shape
         C = M - 1
+        dl = (dk,) if perkey else ()
         dev = base.device
         self.base = base
         self.M = int(M)
-        self.lbar = torch.zeros((n_slots, H), dtype=torch.float32, device=dev)
+        self.perkey = bool(perkey)
+        self.lbar = torch.zeros((n_slots, H, *dl), dtype=torch.float32, device=dev)
         self.klog = torch.zeros((n_slots, H, C, dk), dtype=torch.int16, device=dev)
         self.ulog = torch.zeros((n_slots, H, C, dv), dtype=torch.float32, device=dev)
-        self.lamlog = torch.zeros((n_slots, H, C), dtype=torch.float32, device=dev)
+        self.lamlog = torch.zeros((n_slots, H, C, *dl), dtype=torch.float32, device=dev)
         self.len = torch.zeros((n_slots, H), dtype=torch.int32, device=dev)
 
     @property
@@ -272,6 +274,8 @@ def gdn_decode_deltalog(q, k, v, g, beta, pool: DeltaLogPool, slots, scale=1.0,
     if o is None:
         o = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
     _dev(q, k, v, g, beta, slots, o)
+    if (g.dim() == 3) != pool.perkey:
+        raise ValueError("gate kind does not match the DeltaLog pool layout")
     dims = make_dims(H, dk, dv, _dtype_code(q), g.dim() == 3, scale, qk_l2norm)
     ps = pool.struct()
     _check("gdn_decode_deltalog", lib().gdn_decode_deltalog(
@@ -282,7 +286,7 @@ def gdn_decode_deltalog(q, k, v, g, beta, pool: DeltaLogPool, slots, scale=1.0,
 
 def _dl_maint(name, pool, slots, stream):
     n_slots, H, dk, dv = pool.base.shape
-    dims = make_dims(H, dk, dv, GDN_DTYPE_F32, False, 1.0, False)
+    dims = make_dims(H, dk, dv, GDN_DTYPE_F32, pool.perkey, 1.0, False)
     _dev(slots)
     ps = pool.struct()
     _check(name, getattr(lib(), name)(ctypes.byref(dims), ctypes.byref(ps), pool.n_slots,

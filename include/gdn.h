@@ -232,7 +232,11 @@ int gdn_decode_spec(const gdn_dims_t* dims, const void* q, const void* k, const 
  *   lamlog  [n_slots, H, M-1, d_l] fp32   lbar snapshot at insertion (Lambda_i)
  *   len     [n_slots, H] int32            current log length L, 0 <= L <= M-1
  *   M       merge interval (log capacity M-1), 2 <= M <= 17
- * d_l = 1 (GDN scalar gate). Precisions follow [DeltaLog] §2.7 (K bf16, U fp32). */
+ * d_l = 1 with GDN_GATE_SCALAR (one decay per head); d_l = d_k with GDN_GATE_PER_KEY
+ * (KDA-style: lbar and every Lambda_i hold one log-decay per key channel, and D(x) below is
+ * diag(e^x) over the key rows; [DeltaLog] §2.7, the KDA row). The gate kind of every call on
+ * a pool must match the layout it was created with. Precisions follow [DeltaLog] §2.7
+ * (K bf16, U, Lambda, lbar and the base fp32). */
 typedef struct {
     float* base;
     float* lbar;
@@ -258,8 +262,8 @@ int gdn_deltalog_workspace_bytes(const gdn_dims_t* dims, int32_t batch, int32_t 
  *   L == M-1 (merge, Eq. 6): Sbar = D(lbar') Sbar + sum_i D(lbar' - Lambda_i) K_i U_i^T
  *                             + k b^T;  lbar = 0;  L = 0.
  * The logical state after every step equals the dense decode state (Eq. 7) up to the bf16
- * rounding of logged keys. Slots, layouts and inactive rows as gdn_decode_step.
- * Only GDN_GATE_SCALAR is supported (GDN_ERR_UNSUPPORTED otherwise).
+ * rounding of logged keys. Slots, layouts and inactive rows as gdn_decode_step. Both gate
+ * kinds are supported (g is [batch, H] or [batch, H, d_k]; the pool layout must match).
  * ws may be NULL when ws_bytes is 0. */
 int gdn_decode_deltalog(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
                         const float* g, const float* beta, const gdn_deltalog_pool_t* pool,

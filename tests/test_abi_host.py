@@ -185,7 +185,7 @@ def test_deltalog_rejects_bad_arguments():
     assert call(d, bad_m) == 3
     assert call(d, big_m) == 3
     assert call(d, null_base) == 1
-    assert call(_dims(gate=1), pool) == 3
+    assert call(_dims(gate=2), pool) == 3   # rejected before any launch
     ws = ctypes.c_size_t(123)
     assert lib.gdn_deltalog_workspace_bytes(ctypes.byref(d), 512, 8, ctypes.byref(ws)) == 0
     assert ws.value == 0

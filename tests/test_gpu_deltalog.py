@@ -44,22 +44,26 @@ def test_scalar_worked_example_embedded():
     assert abs(pool.ulog[0, 0, 1, 0].item() - 3.0) < 1e-5
 
 
-@pytest.mark.parametrize("dtype,d,M,l2", [
-    (torch.float32, 16, 2, False), (torch.float32, 64, 3, False),
-    (torch.bfloat16, 128, 8, False), (torch.bfloat16, 32, 17, True),
+@pytest.mark.parametrize("dtype,d,M,l2,perkey", [
+    (torch.float32, 16, 2, False, False), (torch.float32, 64, 3, False, False),
+    (torch.bfloat16, 128, 8, False, False), (torch.bfloat16, 32, 17, True, False),
+    (torch.float32, 16, 3, False, True), (torch.float32, 128, 4, True, True),
+    (torch.bfloat16, 128, 4, False, True), (torch.bfloat16, 64, 17, False, True),
 ])
-def test_deltalog_vs_oracle_bookkeeping(dtype, d, M, l2):
+def test_deltalog_vs_oracle_bookkeeping(dtype, d, M, l2, perkey):
     """Step by step against the oracle's DeltaLog (same bf16 key log), and against the
-    oracle's dense recurrence; includes a batch where slots sit at different log lengths."""
-    say(f"case deltalog {dtype} d={d} M={M} l2={l2}")
+    oracle's dense recurrence; includes a batch where slots sit at different log lengths.
+    perkey: KDA-style per-key-channel decay (lbar and Lambda d_k wide)."""
+    say(f"case deltalog {dtype} d={d} M={M} l2={l2} perkey={perkey}")
     B, H, n_slots, steps = 6, 2, 9, 2 * M + 3
     base0 = inputs.decode_pool(6, n_slots, H, d, d)
     slots = inputs.decode_slots(7, n_slots, B)
-    stream = inputs.DecodeStream(8, B, H, d, d, dtype=dtype, prenorm=not l2)
-    pool = gdn.DeltaLogPool(base0.to(DEV), M)
+    stream = inputs.DecodeStream(8, B, H, d, d, dtype=dtype, perkey=perkey, prenorm=not l2)
+    pool = gdn.DeltaLogPool(base0.to(DEV), M, perkey=perkey)
     # stagger the log lengths: advance half the requests by some steps first
     sl = slots.long()
-    ref = oracle.DeltaLogState(base0[sl].reshape(B * H, d, d).double().numpy(), M)
+    ref = oracle.DeltaLogState(base0[sl].reshape(B * H, d, d).double().numpy(), M,
+                               perkey=perkey)
     dense = base0[sl].double().numpy()
     sd = slots.to(DEV)
     worst_o = worst_dense = 0.0
@@ -73,7 +77,7 @@ def test_deltalog_vs_oracle_bookkeeping(dtype, d, M, l2):
         # oracle on the active rows only
         idx = torch.tensor([i * H + h for i in active.tolist() for h in range(H)])
         full_o = np.zeros((B * H, d))
-        sub_state = oracle.DeltaLogState(np.zeros((len(idx), d, d)), M)
+        sub_state = oracle.DeltaLogState(np.zeros((len(idx), d, d)), M, perkey=perkey)
         for name in ("base", "lbar", "klog", "ulog", "lamlog", "len"):
             getattr(sub_state, name)[:] = getattr(ref, name)[idx.numpy()]
         f = lambda t: t.reshape(B * H, -1)[idx]
@@ -102,18 +106,28 @@ def test_deltalog_vs_oracle_bookkeeping(dtype, d, M, l2):
     assert oracle.rel_err(pool.base.cpu()[sl].reshape(B * H, d, d), ref.materialize()) <= bar
 
 
-def test_reset_clears_log_keeps_base():
-    say("case deltalog reset")
+@pytest.mark.parametrize("perkey", [False, True])
+def test_reset_clears_log_keeps_base(perkey):
+    say(f"case deltalog reset perkey={perkey}")
     d, H = 32, 2
     base0 = inputs.decode_pool(9, 4, H, d, d).to(DEV)
-    pool = gdn.DeltaLogPool(base0.clone(), 4)
+    pool = gdn.DeltaLogPool(base0.clone(), 4, perkey=perkey)
     slots = torch.tensor([1, 3], dtype=torch.int32, device=DEV)
-    q, k, v, g, b = inputs.DecodeStream(10, 2, H, d, d).next()
+    q, k, v, g, b = inputs.DecodeStream(10, 2, H, d, d, perkey=perkey).next()
     gdn.gdn_decode_deltalog(*to_dev(q, k, v, g, b), pool, slots)
     gdn.gdn_deltalog_reset(pool, slots)
     torch.cuda.synchronize()
     assert torch.all(pool.len == 0) and torch.all(pool.lbar == 0)
     assert torch.equal(pool.base, base0)
+
+
+def test_deltalog_gate_kind_must_match_pool():
+    d, H = 32, 2
+    pool = gdn.DeltaLogPool(torch.zeros((2, H, d, d), device=DEV), 4, perkey=True)
+    q, k, v, g, b = to_dev(*inputs.DecodeStream(11, 1, H, d, d).next())
+    with pytest.raises(ValueError):
+        gdn.gdn_decode_deltalog(q, k, v, g, b, pool, torch.zeros(1, dtype=torch.int32,
+                                                                  device=DEV))
 
 
 def test_deltalog_config_vs_dense_full_size():
@@ -132,6 +146,39 @@ def test_deltalog_config_vs_dense_full_size():
     sd = slots.to(DEV)
     stream = inputs.DecodeStream(0, B, H, d, d)
     rng = np.random.default_rng(1)
+    bs, hs = rng.choice(B, 48), rng.choice(H, 48)
+    S = base0[slots.long()[bs], hs].double().numpy()[:, None]
+    worst = worst_or = 0.0
+    for step in range(steps):
+        q, k, v, g, b = to_dev(*stream.next())
+        od = gdn.gdn_decode_step(q, k, v, g, b, dense, sd, scale=d ** -0.5)
+        ol = gdn.gdn_decode_deltalog(q, k, v, g, b, pool, sd, scale=d ** -0.5)
+        worst = max(worst, oracle.rel_err(ol.float().cpu(), od.float().cpu()))
+        sel = lambda t: t.cpu()[bs, hs][:, None]
+        o_ref, S = oracle.decode_step(sel(q), sel(k), sel(v), sel(g), sel(b), S, scale=d ** -0.5)
+        worst_or = max(worst_or, oracle.rel_err(ol.cpu()[bs, hs], o_ref[:, 0]))
+    gdn.gdn_deltalog_materialize(pool, sd)
+    torch.cuda.synchronize()
+    e_s = oracle.rel_err(pool.base.cpu(), dense.cpu())
+    say(f"   worst o DeltaLog vs dense {worst:.2e}; state {e_s:.2e}; vs oracle {worst_or:.2e}")
+    assert worst <= 1e-2 and e_s <= 5e-3 and worst_or <= 5e-3
+
+
+def test_kda_deltalog_vs_dense_full_size():
+    """KDA DeltaLog (per-key decay, M = 4 as the notes use for KDA) vs per-key dense decode at
+    full size: B = 512, H = 32, d = 128, 128-step rollout (43 merge cycles), identical inputs.
+    Bars as the scalar case: 5e-3 against the exact dense recurrence (sampled units, every
+    step) and for the materialised state against the GPU dense state; outputs of the two GPU
+    paths at the bf16 bar."""
+    say("case KDA deltalog B=512 vs dense, 128 steps")
+    B, H, d, M, steps = 512, 32, 128, 4, 128
+    base0 = inputs.decode_pool(2, B, H, d, d)
+    slots = inputs.decode_slots(3, B, B)
+    dense = base0.to(DEV)
+    pool = gdn.DeltaLogPool(base0.to(DEV), M, perkey=True)
+    sd = slots.to(DEV)
+    stream = inputs.DecodeStream(4, B, H, d, d, perkey=True)
+    rng = np.random.default_rng(2)
     bs, hs = rng.choice(B, 48), rng.choice(H, 48)
     S = base0[slots.long()[bs], hs].double().numpy()[:, None]
     worst = worst_or = 0.0
