@@ -7,6 +7,7 @@ mutant; a mutant that survives means a part of the oracle is not pinned by anyth
 itself.
 """
 import os
+import shutil
 import subprocess
 import sys
 
@@ -117,3 +118,35 @@ def test_pins_kill_mutant(name, tmp_path):
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode == 1 and "failed" in r.stdout, (
         f"mutant {name} survived the pins:\n{r.stdout[-2000:]}\n{r.stderr[-2000:]}")
+
+
+# Mistakes planted in the gate formula (oracle/gates.py); the pins run against a copy of the
+# oracle package that holds the mutated module.
+GATE_MUTANTS = {
+    "A_log_not_exponentiated": ("np.exp(np.asarray(A_log, dtype=np.float64))[:, None] * x",
+                                "np.asarray(A_log, dtype=np.float64)[:, None] * x"),
+    "dt_bias_dropped": ("x = fb + np.asarray(dt_bias, dtype=np.float64)", "x = fb"),
+    "sigmoid_sign": ("return 1.0 / (1.0 + np.exp(-x))", "return 1.0 / (1.0 + np.exp(x))"),
+    "A_log_per_channel": ("np.exp(np.asarray(A_log, dtype=np.float64))[:, None] * x",
+                          "np.exp(np.asarray(A_log, dtype=np.float64))[None, :] * x"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GATE_MUTANTS))
+def test_gate_pins_kill_mutant(name, tmp_path):
+    old, new = GATE_MUTANTS[name]
+    src = open(os.path.join(ROOT, "oracle", "gates.py")).read()
+    assert src.count(old) == 1
+    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle",
+                    ignore=shutil.ignore_patterns("__pycache__"))
+    (tmp_path / "oracle" / "gates.py").write_text(src.replace(old, new))
+    (tmp_path / "tests").mkdir()
+    for f in ("conftest.py", "test_oracle_pins.py"):
+        shutil.copy(os.path.join(ROOT, "tests", f), tmp_path / "tests" / f)
+    shutil.copytree(os.path.join(ROOT, "tests", "golden"), tmp_path / "tests" / "golden")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        "-k", "kda_gate", str(tmp_path / "tests" / "test_oracle_pins.py")],
+                       cwd=str(tmp_path), capture_output=True, text=True, timeout=600)
+    assert r.returncode == 1 and "failed" in r.stdout, (
+        f"gate mutant {name} survived the pins:\n{r.stdout[-2000:]}\n{r.stderr[-2000:]}")
+

@@ -500,3 +500,43 @@ def test_conv1d_silu_against_numpy_convolve():
     t, c = cu[2] + 5, 3
     z = sum(x[t - 3 + j, c] * w[c, j] for j in range(4))
     assert abs(y[t, c] - z / (1 + math.exp(-z))) < 1e-13
+
+
+# ------------------------------------------------------------------------ KDA gate formula
+def test_kda_gate_hand_values_and_broadcast():
+    """[LA-Infra] KDA实现逻辑概述: forget_log = lower_bound * sigmoid(e^{A_log} (forget_b +
+    dt_bias)), A_log per head, dt_bias per (head, channel). H = 2, d_k = 2 with A_log =
+    [0, ln 2], dt_bias = [[0, 1], [2, 3]], forget_b = 0 gives z = [[0, 1], [4, 6]]; the values
+    are -5 sigmoid(z) evaluated by hand."""
+    from oracle.gates import kda_forget_log
+    got = kda_forget_log(np.zeros((2, 2)), [[0.0, 1.0], [2.0, 3.0]], [0.0, np.log(2.0)], -5.0)
+    want = [[-2.5, -3.6552928931500244], [-4.910068950189542, -4.987636884216827]]
+    assert np.allclose(got, want, rtol=0, atol=1e-15)
+    # a leading batch axis broadcasts; forget_b shifts x per channel
+    fb = np.array([[[1.0, 0.0], [0.0, 0.0]]])
+    got = kda_forget_log(fb, np.zeros((2, 2)), [0.0, 0.0], -5.0)
+    assert got.shape == (1, 2, 2)
+    assert np.allclose(got[0, 0], [-3.6552928931500244, -2.5], rtol=0, atol=1e-15)
+
+
+def test_kda_gate_range_and_page_bound():
+    """forget_log stays in (lower_bound, 0) and z = 0 gives lower_bound / 2; with
+    lower_bound = -5 the decay cannot drop below e^{-5}, the ~0.67 % per step the page quotes."""
+    from oracle.gates import kda_forget_log, sigmoid
+    rng = np.random.default_rng(0)
+    fb = rng.normal(0, 1, (64, 4, 16))
+    fl = kda_forget_log(fb, rng.normal(0, 1, (4, 16)), rng.normal(0, 0.5, 4), -5.0)
+    assert np.all(fl < 0) and np.all(fl > -5.0)
+    # far out the sigmoid rounds to 0 or 1 in fp64: the interval closes, never overshoots
+    fl = kda_forget_log(rng.normal(0, 40, (64, 4, 16)), np.zeros((4, 16)), np.ones(4), -5.0)
+    assert np.all(fl <= 0) and np.all(fl >= -5.0)
+    assert kda_forget_log(np.array([[0.7]]), [[-0.7]], [1.3], -3.0)[0, 0] == -1.5
+    big = kda_forget_log(np.array([[60.0]]), [[0.0]], [0.0], -5.0)[0, 0]
+    assert abs(np.exp(big) - np.exp(-5.0)) < 1e-15
+    assert round(100 * np.exp(-5.0), 2) == 0.67
+    # monotone: a larger gate projection decays more
+    assert kda_forget_log(np.array([[1.0]]), [[0.0]], [0.0], -5.0)[0, 0] < \
+        kda_forget_log(np.array([[0.5]]), [[0.0]], [0.0], -5.0)[0, 0]
+    # write gate beta = sigmoid(logit): sigmoid(0) = 1/2, sigmoid(ln 3) = 3/4
+    assert sigmoid(0.0) == 0.5 and abs(sigmoid(np.log(3.0)) - 0.75) < 1e-15
+
