@@ -159,6 +159,33 @@ def bench_decode(steps, warmup, layers=4):
                 workload="dense decode B=128 H=32 d=128, 256-slot fp32 pool, 4 rotating layers")
 
 
+def bench_fused(steps, warmup, layers=4):
+    """Fused KDA decode step (conv update + in-kernel gates + L2 norm + per-key recurrence):
+    B = 128, H = 32, d = 128, width 4, bf16; four layers' pools rotate as for the dense step."""
+    B, H, d, W, n_slots = 128, 32, 128, 4, 256
+    fs = [inputs.fused_decode_step(50 + l, B, n_slots, H, d, width=W) for l in range(layers)]
+    pools = [inputs.decode_pool(60 + l, n_slots, H, d, d).to(DEV) for l in range(layers)]
+    dev = [[t.to(DEV) for t in (f.x, f.conv_w, f.conv_state, f.forget_b, f.write_logit,
+                                f.A_log, f.dt_bias)] for f in fs]
+    slots = inputs.decode_slots(0, n_slots, B).to(DEV)
+    o = torch.empty((B, H, d), dtype=torch.bfloat16, device=DEV)
+    it = [0]
+
+    def step():
+        l = it[0] % layers
+        it[0] += 1
+        x, w, cs, fb, wl, al, dt = dev[l]
+        gdn.gdn_decode_fused(x, w, cs, fb, wl, al, dt, -5.0, pools[l], slots, scale=d ** -0.5,
+                             o=o)
+
+    ms, _ = ev_time(step, steps * layers, warmup * layers)
+    byts = traffic.fused_bytes(B, H, d, W, 2)
+    return dict(ms_per_layer_step=ms, GBps=byts / (ms * 1e-3) / 1e9,
+                hbm_frac=byts / (ms * 1e-3) / traffic.HBM_PEAK_BPS, tokens_per_s=B / (ms * 1e-3),
+                workload="fused KDA decode B=128 H=32 d=128, conv width 4, bf16, in-kernel "
+                         "gates and L2 norm, 256-slot pools, 4 rotating layers")
+
+
 def bench_spec(steps, warmup, B=128, P=4):
     """Verify step of speculative decoding: B requests x P positions (3 drafts), H = 32,
     d = 128, bf16 tokens, over a B*P-slot fp32 pool (1 GiB)."""
@@ -347,6 +374,8 @@ def main():
             line["prefill_ckpt"] = bench_prefill_ckpt(args.steps, args.warmup, p["ms"])
         log("decode ...")
         line["decode"] = bench_decode(args.steps, args.warmup)
+        log("fused decode ...")
+        line["decode_fused_kda"] = bench_fused(args.steps, args.warmup)
         log("spec verify ...")
         line["spec_decode"] = bench_spec(args.steps, args.warmup)
         log("deltalog ...")

@@ -335,6 +335,92 @@ __global__ __launch_bounds__(DENSE_THREADS) void spec_decode_kernel(DecodeArgs a
     }
 }
 
+// Fused KDA decode step ([LA-Infra] "KDA实现逻辑概述", "vLLM中Decode的实现", "去掉分母引入卷积"):
+// the workgroup of (request, head) first runs the causal short convolution of the head's
+// 3 d channels (q, k, v planes) from the slot's conv state (the width - 1 previous inputs
+// before the convolution), applies SiLU and shifts the window by the new input; then forms
+// the gates in the kernel,
+//   forget_log = lower_bound * sigmoid(e^{A_log} (forget_b + dt_bias)),  beta = sigmoid(logit),
+// and runs the per-key token update on the convolved q, k, v (q, k L2-normalised). Each conv
+// channel belongs to exactly one head, so the window update has a single writer.
+template <typename T, int DK, int DV, int W>
+__global__ __launch_bounds__(DENSE_THREADS) void fused_decode_kernel(FusedDecodeArgs a) {
+    using G = DecGeom<DK, DV, DENSE_THREADS>;
+    static_assert(DK == DV && 3 * DK <= DENSE_THREADS, "one conv channel per thread");
+    __shared__ DecSmem<T, DK, DV> sm;
+    const int tid = threadIdx.x;
+    const int H = a.H;
+    const int bh = blockIdx.x;
+    const int b = bh / H, h = bh - (bh / H) * H;
+    const int slot = a.slots[b];
+    T* o = reinterpret_cast<T*>(a.o) + (size_t)bh * DV;
+    if (slot < 0 || slot >= a.n_slots) {  // inactive row: zero output, no state access
+        if (tid < DV / 4) {
+            float z[4] = {0.f, 0.f, 0.f, 0.f};
+            store4<T>(o + tid * 4, z);
+        }
+        return;
+    }
+    const size_t CH = (size_t)3 * H * DK;
+    const int plane = tid / DK, i = tid - plane * DK;
+    const size_t c = (size_t)plane * H * DK + (size_t)h * DK + i;
+    const bool conv = tid < 3 * DK;
+    T* cs = reinterpret_cast<T*>(a.conv_state) + ((size_t)slot * CH + c) * (W - 1);
+    // convolution and gate inputs first, then the state stream
+    T old[W - 1];
+    T xv = from_f32<T>(0.f);
+    float wv[W];
+    if (conv) {
+#pragma unroll
+        for (int j = 0; j < W - 1; j++) old[j] = cs[j];
+        xv = reinterpret_cast<const T*>(a.x)[(size_t)b * CH + c];
+#pragma unroll
+        for (int j = 0; j < W; j++) wv[j] = a.conv_w[c * W + j];
+    }
+    float xg = 0.f;
+    if (tid < DK) xg = a.forget_b[(size_t)bh * DK + tid] + a.dt_bias[(size_t)h * DK + tid];
+    const float logit = a.write_logit[bh];
+    const float ea = __expf(a.A_log[h]);
+    const int cg = tid % G::TPR;
+    const int r0 = tid / G::TPR;
+    float* S = a.pool + ((size_t)slot * H + h) * DK * DV;
+    f32x4 st[G::NP];
+#pragma unroll
+    for (int p = 0; p < G::NP; p++) {
+        const int r = r0 + p * G::RPP;
+        if (r < DK) st[p] = stream_load(S + (size_t)r * DV + cg * 4);
+    }
+    if (conv) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < W - 1; j++) acc += wv[j] * to_f32(old[j]);
+        acc += wv[W - 1] * to_f32(xv);
+        const float y = acc / (1.f + __expf(-acc));
+#pragma unroll
+        for (int j = 0; j + 1 < W - 1; j++) cs[j] = old[j + 1];
+        cs[W - 2] = xv;
+        float* dst = plane == 0 ? sm.q : (plane == 1 ? sm.k : sm.v);
+        dst[i] = y;
+    }
+    if (tid < DK) {
+        const float fl = a.lower_bound / (1.f + __expf(-ea * xg));
+        sm.gk[tid] = __expf(fl);
+    }
+    const float beta = 1.f / (1.f + __expf(-logit));
+    lds_barrier();
+
+    float ik, iq, kq;
+    kq_norms<DK>(sm.k, sm.q, ik, iq, kq, a.l2norm != 0);
+    const float out = token_update<DK, DV, true>(st, sm.k, sm.q, sm.v, sm.gk, 1.f, beta, ik, iq,
+                                                 kq, a.scale, sm.red_v, sm.red_q, sm.r);
+    if (tid < DV) o[tid] = from_f32<T>(out);
+#pragma unroll
+    for (int p = 0; p < G::NP; p++) {
+        const int r = r0 + p * G::RPP;
+        if (r < DK) stream_store(S + (size_t)r * DV + cg * 4, st[p]);
+    }
+}
+
 // ------------------------------------------------------------------------------ DeltaLog
 template <int DK, int DV, bool PERKEY>
 struct DlSmem {
@@ -671,6 +757,35 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     if (a.batch == 0) return hipSuccess;
     (void)hipGetLastError();  // report only errors raised by this call's launches
     return a.dtype == 1 ? dec_dispatch_dim<bf16>(a, s) : dec_dispatch_dim<float>(a, s);
+}
+
+template <typename T, int D>
+static hipError_t fused_dispatch_width(const FusedDecodeArgs& a, hipStream_t s) {
+    dim3 grid((unsigned)(a.batch * a.H)), block(DENSE_THREADS);
+    switch (a.width) {
+        case 2: hipLaunchKernelGGL((fused_decode_kernel<T, D, D, 2>), grid, block, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((fused_decode_kernel<T, D, D, 3>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((fused_decode_kernel<T, D, D, 4>), grid, block, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t fused_dispatch_dim(const FusedDecodeArgs& a, hipStream_t s) {
+    switch (a.dk) {
+        case 16: return fused_dispatch_width<T, 16>(a, s);
+        case 32: return fused_dispatch_width<T, 32>(a, s);
+        case 64: return fused_dispatch_width<T, 64>(a, s);
+        case 128: return fused_dispatch_width<T, 128>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fused_decode(const FusedDecodeArgs& a, hipStream_t s) {
+    if (a.batch == 0) return hipSuccess;
+    (void)hipGetLastError();  // report only errors raised by this call's launches
+    return a.dtype == 1 ? fused_dispatch_dim<bf16>(a, s) : fused_dispatch_dim<float>(a, s);
 }
 
 template <typename T, int D>

@@ -256,6 +256,59 @@ int gdn_decode_spec(const gdn_dims_t* dims, const void* q, const void* k, const 
                       num_accepted, batch, n_pos, o, stream, "gdn_decode_spec");
 }
 
+int gdn_decode_fused(const gdn_dims_t* dims, const void* x, const float* conv_w,
+                     int32_t conv_width, void* conv_state, const float* forget_b,
+                     const float* write_logit, const float* A_log, const float* dt_bias,
+                     float lower_bound, float* state_pool, int32_t n_slots,
+                     const int32_t* slots, int32_t batch, void* o, void* stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (dims->gate != GDN_GATE_PER_KEY)
+        return fail(GDN_ERR_UNSUPPORTED, "the fused decode step forms per-key (KDA) gates; "
+                                         "gate must be GDN_GATE_PER_KEY");
+    if (conv_width < 2 || conv_width > 4)
+        return fail(GDN_ERR_UNSUPPORTED, "conv_width must be 2, 3 or 4 (got %d)", conv_width);
+    if (!(lower_bound < 0.f) || lower_bound < -1e30f)
+        return fail(GDN_ERR_UNSUPPORTED, "lower_bound must be finite and < 0 (got %g)",
+                    (double)lower_bound);
+    if (batch < 0) return fail(GDN_ERR_SHAPE, "batch must be >= 0 (got %d)", batch);
+    if (batch == 0) return ok();
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(conv_w);
+    REQUIRE_PTR(conv_state);
+    REQUIRE_PTR(forget_b);
+    REQUIRE_PTR(write_logit);
+    REQUIRE_PTR(A_log);
+    REQUIRE_PTR(dt_bias);
+    REQUIRE_PTR(state_pool);
+    REQUIRE_PTR(slots);
+    REQUIRE_PTR(o);
+    if (n_slots < 1) return fail(GDN_ERR_SHAPE, "n_slots must be >= 1 (got %d)", n_slots);
+    gdn::FusedDecodeArgs a;
+    a.dtype = dims->dtype;
+    a.H = dims->num_heads;
+    a.dk = dims->d_k;
+    a.dv = dims->d_v;
+    a.l2norm = dims->qk_l2norm;
+    a.width = conv_width;
+    a.scale = dims->scale;
+    a.lower_bound = lower_bound;
+    a.x = x;
+    a.conv_w = conv_w;
+    a.conv_state = conv_state;
+    a.forget_b = forget_b;
+    a.write_logit = write_logit;
+    a.A_log = A_log;
+    a.dt_bias = dt_bias;
+    a.pool = state_pool;
+    a.n_slots = n_slots;
+    a.slots = slots;
+    a.batch = batch;
+    a.o = o;
+    return launch_status(gdn::launch_fused_decode(a, static_cast<hipStream_t>(stream)),
+                         "gdn_decode_fused");
+}
+
 int gdn_deltalog_workspace_bytes(const gdn_dims_t* dims, int32_t batch, int32_t M,
                                  size_t* bytes) {
     int st = check_dims(dims);

@@ -81,6 +81,26 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// Fused KDA decode step: short-convolution update from a conv-state pool, in-kernel gates,
+// then the per-key recurrence (q, k L2-normalised when l2norm is set).
+struct FusedDecodeArgs {
+    int dtype, H, dk, dv, l2norm, width;
+    float scale, lower_bound;
+    const void* x;            // [batch][3 H d_k] q|k|v before the convolution
+    const float* conv_w;      // [3 H d_k][width]
+    void* conv_state;         // [n_slots][3 H d_k][width - 1], element type of x
+    const float* forget_b;    // [batch][H][d_k]
+    const float* write_logit; // [batch][H]
+    const float* A_log;       // [H]
+    const float* dt_bias;     // [H][d_k]
+    float* pool;
+    int n_slots;
+    const int32_t* slots;
+    int batch;
+    void* o;
+};
+hipError_t launch_fused_decode(const FusedDecodeArgs& a, hipStream_t stream);
+
 struct DeltaLogArgs {
     int dtype, gate, H, dk, dv, l2norm, M;  // gate 1: lbar and Lambda are d_k wide
     float scale;

@@ -50,6 +50,8 @@ _SIGS = {
                                  _P, _P, _P, _I, _P, _P, _SZ, _P],
     "gdn_decode_step": [_DIMS, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, _P],
     "gdn_decode_spec": [_DIMS, _P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _P, _P],
+    "gdn_decode_fused": [_DIMS, _P, _P, _I, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I, _P, _I,
+                         _P, _P],
     "gdn_deltalog_workspace_bytes": [_DIMS, _I, _I, ctypes.POINTER(_SZ)],
     "gdn_decode_deltalog": [_DIMS, _P, _P, _P, _P, _P, _POOL, _I, _P, _I, _P, _P, _SZ, _P],
     "gdn_deltalog_reset": [_DIMS, _POOL, _I, _P, _I, _P],
@@ -228,6 +230,25 @@ def gdn_decode_spec(q, k, v, g, beta, state_pool, spec_slots, num_accepted, scal
         ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
         int(state_pool.shape[0]), _ptr(spec_slots), _ptr(num_accepted), int(B), int(P), _ptr(o),
         _stream(stream)))
+    return o
+
+
+def gdn_decode_fused(x, conv_w, conv_state, forget_b, write_logit, A_log, dt_bias, lower_bound,
+                     state_pool, slots, scale=1.0, qk_l2norm=True, o=None, stream=None):
+    """Fused KDA decode step. x [B, 3 H d] (q|k|v before the convolution); conv_w [3 H d, W]
+    fp32; conv_state [slots, 3 H d, W-1] (x's dtype, updated in place); forget_b [B, H, d],
+    write_logit [B, H], A_log [H], dt_bias [H, d] fp32; state_pool [slots, H, d, d] fp32;
+    slots [B] int32. Returns o [B, H, d]."""
+    B, H, dk = forget_b.shape
+    W = conv_w.shape[1]
+    if o is None:
+        o = torch.empty((B, H, dk), dtype=x.dtype, device=x.device)
+    _dev(x, conv_w, conv_state, forget_b, write_logit, A_log, dt_bias, state_pool, slots, o)
+    dims = make_dims(H, dk, dk, _dtype_code(x), True, scale, qk_l2norm)
+    _check("gdn_decode_fused", lib().gdn_decode_fused(
+        ctypes.byref(dims), _ptr(x), _ptr(conv_w), int(W), _ptr(conv_state), _ptr(forget_b),
+        _ptr(write_logit), _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(state_pool),
+        int(state_pool.shape[0]), _ptr(slots), int(B), _ptr(o), _stream(stream)))
     return o
 
 

@@ -193,6 +193,38 @@ def spec_slot_table(seed: int, n_slots: int, batch: int, n_pos: int):
 
 
 @dataclass
+class FusedDecodeInputs:
+    x: torch.Tensor            # [B, 3 H d] dtype, q|k|v before the convolution
+    conv_w: torch.Tensor       # [3 H d, W] fp32
+    conv_state: torch.Tensor   # [n_slots, 3 H d, W - 1] dtype
+    forget_b: torch.Tensor     # [B, H, d] fp32
+    write_logit: torch.Tensor  # [B, H] fp32
+    A_log: torch.Tensor        # [H] fp32
+    dt_bias: torch.Tensor      # [H, d] fp32
+    lower_bound: float
+
+
+def fused_decode_step(seed: int, batch: int, n_slots: int, H: int, d: int, width: int = 4,
+                      dtype=BF16) -> FusedDecodeInputs:
+    """One fused KDA decode step: raw q|k|v ~ randn, conv weights randn/2 and a conv-state
+    pool ~ randn (all as the KDA prefill recipe), gate projection forget_b ~ randn, write
+    logits ~ randn, A_log = log(uniform(1, 16)) per head, dt_bias ~ randn/2 per (head,
+    channel), lower_bound -5 (the page's value). No trained weights: all synthetic."""
+    gen = _gen(seed)
+    CH = 3 * H * d
+    x = torch.randn(batch, CH, generator=gen).to(dtype)
+    w = torch.randn(CH, width, generator=gen) / 2
+    cs = torch.randn(n_slots, CH, width - 1, generator=gen).to(dtype)
+    fb = torch.randn(batch, H, d, generator=gen)
+    wl = torch.randn(batch, H, generator=gen)
+    A_log = torch.log(1.0 + 15.0 * torch.rand(H, generator=gen))
+    dt = torch.randn(H, d, generator=gen) / 2
+    return FusedDecodeInputs(x=x.contiguous(), conv_w=w.contiguous(), conv_state=cs.contiguous(),
+                             forget_b=fb.contiguous(), write_logit=wl.contiguous(),
+                             A_log=A_log.contiguous(), dt_bias=dt.contiguous(), lower_bound=-5.0)
+
+
+@dataclass
 class KdaVarlenInputs:
     x: torch.Tensor           # [T, 3*H*d] bf16, raw fused q|k|v projection output
     conv_w: torch.Tensor      # [3*H*d, 4] fp32

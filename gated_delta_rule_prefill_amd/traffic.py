@@ -99,3 +99,13 @@ def spec_bytes(B: int, n_pos: int, H: int, dk: int, dv: int, e: int, perkey: boo
     per_tok = (2 * dk + 2 * dv) * e + 4 * (dk if perkey else 1) + 4
     return B * H * (state * (1 + n_pos) + n_pos * per_tok) + 4 * B * n_pos + 4 * B
 
+
+def fused_bytes(B: int, H: int, d: int, width: int, e: int) -> int:
+    """Fused KDA decode step: read + write the fp32 state, read + write the conv window
+    (width - 1 inputs per q/k/v channel), read the new inputs, conv weights, gate inputs and
+    parameters, write o, read the slot map."""
+    CH = 3 * H * d
+    return int(2 * 4 * B * H * d * d + 2 * B * CH * (width - 1) * e + B * CH * e
+               + CH * width * 4 + 4 * B * H * d + 4 * B * H + 4 * H + 4 * H * d
+               + B * H * d * e + 4 * B)
+

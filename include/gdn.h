@@ -222,6 +222,38 @@ int gdn_decode_spec(const gdn_dims_t* dims, const void* q, const void* k, const 
                     const int32_t* spec_slots, const int32_t* num_accepted, int32_t batch,
                     int32_t n_pos, void* o, void* stream);
 
+/* Fused KDA decode step: short-convolution update, in-kernel gates, L2 norm and the per-key
+ * recurrence in one launch ([LA-Infra] "KDA实现逻辑概述" gate formulas and step list;
+ * "vLLM中Decode的实现": one convolution over the concatenated q|k|v channels reading and
+ * writing a conv-state pool, gates formed inside the decode kernel, q/k L2 norm in the
+ * kernel; "去掉分母引入卷积": the conv state keeps the conv_width - 1 most recent inputs
+ * before the convolution, [slots, 3 H d, conv_width - 1], and the output is not stored).
+ * Per request b (slot s = slots[b]), head h, key channel c, with W = conv_width:
+ *   for each of the 3 d channels ch of head h in the q, k, v planes:
+ *     y[ch] = SiLU(sum_{j<W-1} conv_state[s, ch, j] w[ch, j] + x[b, ch] w[ch, W-1]);
+ *     conv_state[s, ch, :] <- (conv_state[s, ch, 1:], x[b, ch])   (column 0 is the oldest)
+ *   forget_log[c] = lower_bound * sigmoid(e^{A_log[h]} (forget_b[b, h, c] + dt_bias[h, c]))
+ *   beta          = sigmoid(write_logit[b, h])
+ *   then gdn_decode_step with the per-key gate g = forget_log on (q, k, v) = y of the three
+ *   planes (q, k L2-normalised when dims.qk_l2norm = 1, as the page's KDA does).
+ *   dims         gate must be GDN_GATE_PER_KEY (GDN_ERR_UNSUPPORTED otherwise)
+ *   x            [batch, 3 H d_k] dtype: q | k | v channels before the convolution
+ *   conv_w       [3 H d_k, conv_width] fp32 (column conv_width - 1 weighs the current input)
+ *   conv_width   2, 3 or 4
+ *   conv_state   [n_slots, 3 H d_k, conv_width - 1] dtype, read and updated in place
+ *   forget_b     [batch, H, d_k] fp32;  write_logit [batch, H] fp32
+ *   A_log        [H] fp32;  dt_bias [H, d_k] fp32;  lower_bound < 0 (finite; e.g. -5)
+ *   state_pool   [n_slots, H, d_k, d_v] fp32;  slots [batch] int32 (device)
+ *   o            [batch, H, d_v] dtype
+ * Both pools are addressed by the same slot. A slot outside [0, n_slots) marks an inactive
+ * row: o is zeroed and neither pool is touched. Valid slots must be distinct. batch == 0 is
+ * a valid no-op. */
+int gdn_decode_fused(const gdn_dims_t* dims, const void* x, const float* conv_w,
+                     int32_t conv_width, void* conv_state, const float* forget_b,
+                     const float* write_logit, const float* A_log, const float* dt_bias,
+                     float lower_bound, float* state_pool, int32_t n_slots,
+                     const int32_t* slots, int32_t batch, void* o, void* stream);
+
 /* ----------------------------------------------------------------------------- DeltaLog */
 
 /* DeltaLog state pool ([DeltaLog] §2.1 symbol table). All arrays are device memory:

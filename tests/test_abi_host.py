@@ -23,6 +23,7 @@ def test_header_declares_the_abi():
     names = _declared()
     for n in ("gdn_prefill_chunked", "gdn_prefill_chunked_ckpt",
               "gdn_prefill_workspace_bytes", "gdn_decode_step", "gdn_decode_spec",
+              "gdn_decode_fused",
               "gdn_decode_deltalog", "gdn_deltalog_workspace_bytes", "gdn_deltalog_reset",
               "gdn_deltalog_materialize", "gdn_conv1d_silu", "gdn_status_string",
               "gdn_last_error", "gdn_abi_version"):
@@ -168,6 +169,31 @@ def test_decode_spec_rejects_bad_arguments(kw, status):
 
 def test_decode_spec_zero_batch_is_a_noop():
     assert _spec(_dims(), batch=0, q=None, num_accepted=None) == 0
+
+
+def _fused(dims, width=4, lb=-5.0, batch=8, **kw):
+    a = dict(x=FAKE, w=FAKE, cs=FAKE, fb=FAKE, wl=FAKE, al=FAKE, dt=FAKE, pool=FAKE, n_slots=16,
+             slots=FAKE, o=FAKE)
+    a.update(kw)
+    return gdn.load().gdn_decode_fused(
+        ctypes.byref(dims), a["x"], a["w"], width, a["cs"], a["fb"], a["wl"], a["al"], a["dt"],
+        lb, a["pool"], a["n_slots"], a["slots"], batch, a["o"], None)
+
+
+@pytest.mark.parametrize("dims,kw,status", [
+    (_dims(gate=0), {}, 3), (_dims(gate=1), dict(width=5), 3), (_dims(gate=1), dict(width=1), 3),
+    (_dims(gate=1), dict(lb=0.0), 3), (_dims(gate=1), dict(lb=float("nan")), 3),
+    (_dims(gate=1), dict(lb=float("-inf")), 3), (_dims(gate=1), dict(cs=None), 1),
+    (_dims(gate=1), dict(dt=FAKE + 4), 4), (_dims(gate=1), dict(batch=-2), 2),
+    (_dims(gate=1), dict(n_slots=0), 2),
+])
+def test_decode_fused_rejects_bad_arguments(dims, kw, status):
+    assert _fused(dims, **kw) == status
+    assert gdn.gdn_last_error() != ""
+
+
+def test_decode_fused_zero_batch_is_a_noop():
+    assert _fused(_dims(gate=1), batch=0, x=None) == 0
 
 
 def test_deltalog_rejects_bad_arguments():
