@@ -55,6 +55,47 @@ struct PfCfg {
 struct ChunkLoc {
     int seq, tok0, len;
 };
+
+// Up to one wave's worth of sequences, every wave forms the first-chunk table itself: lane n
+// holds the exclusive and inclusive prefix sums of ceil(len_s / C) at sequence n (the same
+// table the separate seq_first pass writes for longer lists), so no extra launch runs.
+constexpr int SEQ_INLINE_MAX = WAVE;
+struct WaveSeqTable {
+    int excl, incl;
+};
+__device__ __forceinline__ WaveSeqTable wave_seq_table(const int32_t* cu, int n_seqs, int C) {
+    const int l = lane_id();
+    int cnt = 0;
+    if (l < n_seqs) cnt = (max(0, cu[l + 1] - cu[l]) + C - 1) / C;
+    int x = cnt;
+#pragma unroll
+    for (int off = 1; off < WAVE; off <<= 1) {
+        const int y = __shfl_up(x, off, WAVE);
+        if (l >= off) x += y;
+    }
+    return {x - cnt, x};
+}
+__device__ __forceinline__ ChunkLoc locate_chunk_inline(int c, const int32_t* cu, int n_seqs,
+                                                        int C, int total_tokens) {
+    ChunkLoc r;
+    r.seq = -1;
+    r.tok0 = 0;
+    r.len = 0;
+    const WaveSeqTable t = wave_seq_table(cu, n_seqs, C);
+    // the one non-empty sequence whose chunk range holds c (none past the last chunk)
+    const uint64_t m = __ballot(lane_id() < n_seqs && t.excl <= c && c < t.incl);
+    if (m == 0) return r;
+    const int n = __builtin_ctzll(m);
+    const int first = __builtin_amdgcn_readlane(t.excl, n);
+    r.tok0 = cu[n] + (c - first) * C;
+    r.len = min(C, min(cu[n + 1], total_tokens) - r.tok0);
+    if (r.tok0 < 0 || r.len <= 0) {  // inconsistent cu_seqlens: never index outside q/k/v
+        r.len = 0;
+        return r;
+    }
+    r.seq = n;
+    return r;
+}
 __device__ __forceinline__ ChunkLoc locate_chunk(int c, const int32_t* seq_first,
                                                  const int32_t* cu, int n_seqs, int C,
                                                  int total_tokens) {
@@ -199,8 +240,10 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
     const int H = a.H;
     const int c = blockIdx.x / H;
     const int h = blockIdx.x - c * H;
-    const ChunkLoc loc = locate_chunk(c, a.ws.seq_first, a.cu_seqlens, a.n_seqs, C,
-                                      a.total_tokens);
+    const ChunkLoc loc =
+        a.n_seqs <= SEQ_INLINE_MAX
+            ? locate_chunk_inline(c, a.cu_seqlens, a.n_seqs, C, a.total_tokens)
+            : locate_chunk(c, a.ws.seq_first, a.cu_seqlens, a.n_seqs, C, a.total_tokens);
     if (loc.seq < 0) return;
     const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
     const int g4 = lane >> 4, r16 = lane & 15;
@@ -772,8 +815,17 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
     const int kq = g * KPL;
     const int vcol0 = vt * BV;
     // clamps keep inconsistent cu_seqlens inside the workspace and the token range
-    const int c_begin = a.ws.seq_first[n];
-    const int c_end = (int)min((int64_t)a.ws.seq_first[n + 1], a.ws.max_chunks);
+    int c_first, c_last1;
+    if (a.n_seqs <= SEQ_INLINE_MAX) {
+        const WaveSeqTable t = wave_seq_table(a.cu_seqlens, a.n_seqs, C);
+        c_first = __builtin_amdgcn_readlane(t.excl, n);
+        c_last1 = __builtin_amdgcn_readlane(t.incl, n);
+    } else {
+        c_first = a.ws.seq_first[n];
+        c_last1 = a.ws.seq_first[n + 1];
+    }
+    const int c_begin = c_first;
+    const int c_end = (int)min((int64_t)c_last1, a.ws.max_chunks);
     const int t_begin = a.cu_seqlens[n], t_end = min(a.cu_seqlens[n + 1], a.total_tokens);
     const int slot = a.slots[n];
     const bool valid = slot >= 0 && slot < a.n_slots;
@@ -1015,8 +1067,9 @@ hipError_t prefill_launch_cfg(const PrefillArgs& a, hipStream_t s) {
         (void)hipGetLastError();
         return e;
     }
-    hipLaunchKernelGGL(seq_first_kernel, dim3(1), dim3(256), 0, s, a.cu_seqlens, a.n_seqs,
-                       C, a.ws.seq_first);
+    if (a.n_seqs > SEQ_INLINE_MAX)  // shorter lists: each wave forms the table itself
+        hipLaunchKernelGGL(seq_first_kernel, dim3(1), dim3(256), 0, s, a.cu_seqlens, a.n_seqs,
+                           C, a.ws.seq_first);
     const int64_t nchunk = a.ws.max_chunks;
     if (nchunk > 0)
         hipLaunchKernelGGL(prep, dim3((unsigned)(nchunk * a.H)), dim3(PF_THREADS), smem, s, a);

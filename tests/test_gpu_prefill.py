@@ -77,6 +77,19 @@ def test_many_sequences_wide_value_tiles(nseq, dtype, perkey):
     _check(x, o, pool, o_ref, s_ref)
 
 
+@pytest.mark.parametrize("nseq", [65, 150])
+def test_more_sequences_than_one_wave(nseq):
+    """Past 64 sequences the per-sequence first-chunk table comes from its own pass instead
+    of being formed inside each wave: ragged lengths (empty ones included), H = 2, d = 32."""
+    say(f"case prefill {nseq} sequences")
+    lengths = torch.randint(0, 100, (nseq,), generator=torch.Generator().manual_seed(22)).tolist()
+    lengths[3] = 0
+    x = inputs.random_prefill(23, lengths, H=2, dk=32, dv=32, chunk=32, with_init=True)
+    o, pool = run_prefill(x)
+    o_ref, s_ref = oracle_prefill(x)
+    _check(x, o, pool, o_ref, s_ref)
+
+
 @pytest.mark.parametrize("perkey", [False, True])
 def test_chunk_size_invariance(perkey):
     """The chunk size is an execution choice: C = 16, 32, 64 give the same result."""
