@@ -176,10 +176,15 @@ struct PrepSmem {
             float gseg[PERKEY ? PF_THREADS / DK : 1][PERKEY ? DK : 1];    // segment totals
         } a;
         struct {                      // from barrier #2 on
-            alignas(16) float ar[C][C + 1];  // A (strictly lower), then R = (I + A)^{-1} in
-                                             // place; the strictly upper part is merge scratch
+            union {
+                alignas(16) float ar[C][C + 1];  // A (strictly lower), then R = (I + A)^{-1}
+                                                 // in place; the strictly upper part is
+                                                 // merge scratch
+                alignas(16) T va[PERKEY ? 1 : DV][F::LDC];  // scalar gate: (diag(beta) V)^T,
+                                                            // written once R is complete
+            };
             alignas(16) T rs[C][F::LDC];     // R as an MFMA operand
-            alignas(16) T vt[DV][F::LDC];    // (diag(beta) V)^T
+            alignas(16) T vt[PERKEY ? DV : 1][F::LDC];  // per-key gate: (diag(beta) V)^T
         } b;
     } u;
 };
@@ -226,8 +231,12 @@ template <> struct Ident<float> {
     }
 };
 
+// Scalar gate: V^T shares its LDS with A/R (46.6 KiB at d = 128, C = 64) and the register
+// budget allows three waves per SIMD, so three workgroups share a CU and hide more of the
+// load latency of each unit's q, k, v.
 template <typename T, int DK, int DV, int C, bool PERKEY>
-__global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(PF_THREADS)
+__attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(PrefillArgs a) {
     using F = PfCfg<T, DK, DV, C>;
     using MM = typename F::MM;
     using frag = typename MM::frag;
@@ -236,6 +245,7 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
     constexpr int NV = ((DV + KB - 1) / KB);           // row fragments over d_v
     extern __shared__ __align__(16) unsigned char smem_raw[];
     auto& sm = *reinterpret_cast<PrepSmem<T, DK, DV, C, PERKEY>*>(smem_raw);
+    T (*const vt)[F::LDC] = PERKEY ? sm.u.b.vt : sm.u.b.va;
 
     const int H = a.H;
     const int c = blockIdx.x / H;
@@ -552,26 +562,30 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
             }
         }
     }
-    if (own) {
-        // (diag(beta) V)^T: lane (g4, n) gets V[16w + 4 g4 + e][16 vb + n]
-        const int t0 = w * 16 + g4 * 4;
+    // (diag(beta) V)^T: lane (g4, n) gets V[16w + 4 g4 + e][16 vb + n], plus zero padding
+    // tokens; per-key gate here, scalar gate after the merges (over A/R)
+    auto store_vt = [&]() {
+        if (own) {
+            const int t0 = w * 16 + g4 * 4;
 #pragma unroll
-        for (int vb = 0; vb < DV / 16; vb++) {
-            const f32x4 vt4 = Ident<T>::template transpose<NV>(vf, vb, idf);
-            float vv[4];
+            for (int vb = 0; vb < DV / 16; vb++) {
+                const f32x4 vt4 = Ident<T>::template transpose<NV>(vf, vb, idf);
+                float vv[4];
 #pragma unroll
-            for (int e = 0; e < 4; e++) vv[e] = sm.bs[t0 + e] * vt4[e];
-            store4<T>(&sm.u.b.vt[vb * 16 + r16][t0], vv);
+                for (int e = 0; e < 4; e++) vv[e] = sm.bs[t0 + e] * vt4[e];
+                store4<T>(&vt[vb * 16 + r16][t0], vv);
+            }
         }
-    }
-    // zeros: V^T padding tokens, R above the diagonal blocks and in the padding columns
-    if constexpr (CP > C) {
-        for (int idx = tid; idx < DV * ((CP - C) / 4); idx += PF_THREADS) {
-            const int ch = idx / ((CP - C) / 4), t0 = C + (idx % ((CP - C) / 4)) * 4;
-            float z[4] = {0.f, 0.f, 0.f, 0.f};
-            store4<T>(&sm.u.b.vt[ch][t0], z);
+        if constexpr (CP > C) {
+            for (int idx = tid; idx < DV * ((CP - C) / 4); idx += PF_THREADS) {
+                const int ch = idx / ((CP - C) / 4), t0 = C + (idx % ((CP - C) / 4)) * 4;
+                float z[4] = {0.f, 0.f, 0.f, 0.f};
+                store4<T>(&vt[ch][t0], z);
+            }
         }
-    }
+    };
+    if constexpr (PERKEY) store_vt();
+    // zeros: R above the diagonal blocks and in the padding columns
     for (int idx = tid; idx < C * (CP / 4); idx += PF_THREADS) {
         const int i = idx / (CP / 4), j0 = (idx % (CP / 4)) * 4;
         if (j0 / 16 > i / 16 || j0 >= C) {
@@ -637,6 +651,10 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
         }
     }
     lds_barrier();  // #6: R complete
+    if constexpr (!PERKEY) {
+        store_vt();     // A/R is dead: V^T goes over it
+        lds_barrier();  // #7
+    }
 
     // ---------------------------------------- P4: -W (fragment-major) and U (scan order)
     {
@@ -674,7 +692,7 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_prep_kernel(PrefillArgs a)
 #pragma unroll
                 for (int kb = 0; kb < CP / KB; kb++) {
                     auto fa = MM::load(&sm.u.b.rs[mb * 16 + r16][kb * KB + kq]);
-                    auto fb = MM::load(&sm.u.b.vt[nb * 16 + r16][kb * KB + kq]);
+                    auto fb = MM::load(&vt[nb * 16 + r16][kb * KB + kq]);
                     acc = MM::mma(fa, fb, acc);
                 }
                 // lane: U[i = mb*16 + 4*g4 + e][v = nb*16 + r16], scan accumulator order
