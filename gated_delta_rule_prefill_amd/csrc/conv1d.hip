@@ -99,7 +99,18 @@ __global__ __launch_bounds__(CONV_THREADS) void conv1d_silu_kernel(ConvArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < 8; i++) acc[i] = acc[i] / (1.f + __expf(-acc[i]));
-        store8<T>(ybase + (size_t)t * pc, acc);
+        T* dst = ybase + (size_t)t * pc;
+        if constexpr (sizeof(T) == 2) {  // output rows are streamed: non-temporal stores
+            bf16x8 v;
+#pragma unroll
+            for (int i = 0; i < 8; i++) v[i] = (bf16)acc[i];
+            __builtin_nontemporal_store(v, reinterpret_cast<bf16x8*>(dst));
+        } else {
+            __builtin_nontemporal_store(f32x4{acc[0], acc[1], acc[2], acc[3]},
+                                        reinterpret_cast<f32x4*>(dst));
+            __builtin_nontemporal_store(f32x4{acc[4], acc[5], acc[6], acc[7]},
+                                        reinterpret_cast<f32x4*>(dst + 4));
+        }
     }
 }
 
