@@ -1050,8 +1050,14 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
         if (c < c_end) step(op0, op1, c);
     };
     if (c_begin < c_end) {
-        if (w < NB) run(std::integral_constant<bool, true>());
-        else run(std::integral_constant<bool, false>());
+        if (w < NB) {
+            // an E wave shares its SIMD with an O wave; issuing its instructions first keeps
+            // the state chain, which every chunk waits on, ahead of the output work
+            __builtin_amdgcn_s_setprio(1);
+            run(std::integral_constant<bool, true>());
+        } else {
+            run(std::integral_constant<bool, false>());
+        }
     }
     if (valid && ewave) store_state(S);
 }
