@@ -166,6 +166,40 @@ def test_slots_untouched_noslot_and_empty_sequences():
         assert torch.equal(after[untouched], pool[untouched])
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_degenerate_no_write_no_decay(dtype):
+    """beta = 0 and g = 0: nothing is written and nothing decays, so the state stays exactly
+    the initial state and every output is scale * S_0^T q (the beta = 0 closed form)."""
+    say(f"case degenerate beta=0 g=0 {dtype}")
+    x = inputs.random_prefill(24, [200, 64, 1], H=2, dk=64, dv=64, dtype=dtype, with_init=True)
+    x.beta = torch.zeros_like(x.beta)
+    x.g = torch.zeros_like(x.g)
+    o, pool = run_prefill(x)
+    assert torch.equal(pool, x.init_states.float())
+    o_ref, s_ref = oracle_prefill(x)
+    _check(x, o, pool, o_ref, s_ref)
+
+
+def test_zero_queries_give_zero_outputs():
+    say("case zero queries")
+    x = inputs.random_prefill(25, [150, 33], H=2, dk=128, dv=128, with_init=True)
+    x.q = torch.zeros_like(x.q)
+    o, pool = run_prefill(x)
+    assert torch.all(o == 0)
+    o_ref, s_ref = oracle_prefill(x)
+    assert oracle.rel_err(pool, s_ref) <= 1e-2
+
+
+def test_long_sequence_many_chunks():
+    """One 65536-token sequence (1024 chunks of 64), H = 2, d = 64, bf16, with an initial
+    state: outputs and final state against the oracle."""
+    say("case long sequence T=65536")
+    x = inputs.random_prefill(26, [65536], H=2, dk=64, dv=64, with_init=True)
+    o, pool = run_prefill(x)
+    o_ref, s_ref = oracle_prefill(x)
+    _check(x, o, pool, o_ref, s_ref)
+
+
 def test_deterministic():
     say("case determinism")
     x = inputs.random_prefill(17, [500, 300], H=4, dk=128, dv=128, perkey=True)
