@@ -15,7 +15,7 @@ LIB = os.path.join(HERE, "libgdn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["gdn_api.cpp", "decode.hip", "conv1d.hip", "prefill.hip", "prefill_bf16.hip",
-           "prefill_f32.hip"]
+           "prefill_f32.hip", "prefill_conv_bf16.hip", "prefill_conv_f32.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"),
           "-I", CSRC]

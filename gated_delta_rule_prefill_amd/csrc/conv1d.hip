@@ -95,10 +95,10 @@ __global__ __launch_bounds__(CONV_THREADS) void conv1d_silu_kernel(ConvArgs a) {
             const int src = t - (W - 1) + j;
             const bool keep = src >= start;  // zero history before the sequence start
 #pragma unroll
-            for (int i = 0; i < 8; i++) acc[i] += keep ? wv[i][j] * xr[tt + j][i] : 0.f;
+            for (int i = 0; i < 8; i++) acc[i] = fmaf(wv[i][j], keep ? xr[tt + j][i] : 0.f, acc[i]);
         }
 #pragma unroll
-        for (int i = 0; i < 8; i++) acc[i] = acc[i] / (1.f + __expf(-acc[i]));
+        for (int i = 0; i < 8; i++) acc[i] = silu_f32(acc[i]);
         T* dst = ybase + (size_t)t * pc;
         if constexpr (sizeof(T) == 2) {  // output rows are streamed: non-temporal stores
             bf16x8 v;
@@ -131,6 +131,47 @@ hipError_t launch_conv1d(const ConvArgs& a, hipStream_t s) {
     if (a.total_tokens == 0 || a.n_seqs == 0) return hipSuccess;
     (void)hipGetLastError();  // report only errors raised by this call's launches
     return a.dtype == 1 ? conv_launch<bf16>(a, s) : conv_launch<float>(a, s);
+}
+
+// One thread per (sequence, channel): the new history is the last W-1 rows of the
+// sequence's raw projection, where a row before the sequence start is the old history's
+// entry for it (zero without one). Row r of the new history holds token end-(W-1)+r, so
+// column 0 stays the oldest, as the decode step expects.
+template <typename T>
+__global__ __launch_bounds__(256) void conv_state_update_kernel(PrefillArgs a) {
+    const int XC = 3 * a.H * a.dk;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)a.n_seqs * XC) return;
+    const int n = (int)(idx / XC), ch = (int)(idx - (int64_t)n * XC);
+    const int slot = a.slots[n];
+    if (slot < 0 || slot >= a.n_slots) return;
+    const int W = a.conv_width;
+    const int s0 = a.cu_seqlens[n], s1 = a.cu_seqlens[n + 1];
+    const bool hist = a.has_init != nullptr && a.has_init[n] != 0;
+    T* cs = reinterpret_cast<T*>(a.conv_state) + ((size_t)slot * XC + ch) * (W - 1);
+    const T* x = reinterpret_cast<const T*>(a.x);
+    T old[3], nw[3];
+#pragma unroll
+    for (int j = 0; j < 3; j++) old[j] = (hist && j < W - 1) ? cs[j] : from_f32<T>(0.f);
+    const int len = s1 - s0;
+#pragma unroll
+    for (int j = 0; j < 3; j++) {
+        const int r = s1 - (W - 1) + j;
+        if (r >= s0) nw[j] = x[(size_t)r * XC + ch];
+        else nw[j] = j + len < W - 1 ? old[j + len] : from_f32<T>(0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < 3; j++)
+        if (j < W - 1) cs[j] = nw[j];
+}
+
+hipError_t launch_conv_state_update(const PrefillArgs& a, hipStream_t s) {
+    const int64_t work = (int64_t)a.n_seqs * 3 * a.H * a.dk;
+    if (work == 0) return hipSuccess;
+    const dim3 grid((unsigned)((work + 255) / 256)), block(256);
+    if (a.dtype == 1) hipLaunchKernelGGL(conv_state_update_kernel<bf16>, grid, block, 0, s, a);
+    else hipLaunchKernelGGL(conv_state_update_kernel<float>, grid, block, 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace gdn

@@ -395,7 +395,7 @@ __global__ __launch_bounds__(DENSE_THREADS) void fused_decode_kernel(FusedDecode
 #pragma unroll
         for (int j = 0; j < W - 1; j++) acc += wv[j] * to_f32(old[j]);
         acc += wv[W - 1] * to_f32(xv);
-        const float y = acc / (1.f + __expf(-acc));
+        const float y = silu_f32(acc);
 #pragma unroll
         for (int j = 0; j + 1 < W - 1; j++) cs[j] = old[j + 1];
         cs[W - 2] = xv;

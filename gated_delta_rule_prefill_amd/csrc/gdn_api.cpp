@@ -90,15 +90,27 @@ int deltalog_pool_checks(const gdn_deltalog_pool_t* pool) {
     return GDN_OK;
 }
 
-// Shared by gdn_prefill_chunked (no checkpoints) and gdn_prefill_chunked_ckpt.
+// Raw projection and short-convolution operands of the conv-fused prefill.
+struct ConvIn {
+    const void* x;
+    const float* w;
+    int32_t width;
+    void* state;
+};
+
+// Shared by gdn_prefill_chunked (no checkpoints), gdn_prefill_chunked_ckpt and, with conv
+// set (q, k, v then unused), gdn_prefill_chunked_conv.
 int prefill_run(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
                 const float* g, const float* beta, const int32_t* cu_seqlens, int32_t n_seqs,
                 int32_t total_tokens, int32_t chunk, float* state_pool, int32_t n_slots,
                 const int32_t* slots, const int32_t* has_init, const int32_t* ckpt_cu,
                 const int32_t* ckpt_pos, const int32_t* ckpt_slots, int32_t n_ckpt, void* o,
-                void* workspace, size_t ws_bytes, void* stream, const char* what) {
+                void* workspace, size_t ws_bytes, void* stream, const char* what,
+                const ConvIn* conv = nullptr) {
     int st = prefill_common_checks(dims, n_seqs, total_tokens, chunk);
     if (st) return st;
+    if (conv != nullptr && (conv->width < 2 || conv->width > 4))
+        return fail(GDN_ERR_UNSUPPORTED, "conv_width must be 2, 3 or 4 (got %d)", conv->width);
     if (n_seqs == 0) return ok();
     REQUIRE_PTR(cu_seqlens);
     REQUIRE_PTR(slots);
@@ -111,10 +123,20 @@ int prefill_run(const gdn_dims_t* dims, const void* q, const void* k, const void
         REQUIRE_PTR(ckpt_pos);
         REQUIRE_PTR(ckpt_slots);
     }
+    if (conv != nullptr) {
+        const void* x = conv->x;
+        const float* conv_w = conv->w;
+        void* conv_state = conv->state;
+        if (total_tokens > 0) REQUIRE_PTR(x);
+        REQUIRE_PTR(conv_w);
+        OPT_PTR(conv_state);
+    }
     if (total_tokens > 0) {
-        REQUIRE_PTR(q);
-        REQUIRE_PTR(k);
-        REQUIRE_PTR(v);
+        if (conv == nullptr) {
+            REQUIRE_PTR(q);
+            REQUIRE_PTR(k);
+            REQUIRE_PTR(v);
+        }
         REQUIRE_PTR(g);
         REQUIRE_PTR(beta);
         REQUIRE_PTR(o);
@@ -153,6 +175,10 @@ int prefill_run(const gdn_dims_t* dims, const void* q, const void* k, const void
     a.ckpt_pos = n_ckpt > 0 ? ckpt_pos : nullptr;
     a.ckpt_slots = n_ckpt > 0 ? ckpt_slots : nullptr;
     a.n_ckpt = n_ckpt;
+    a.x = conv != nullptr ? conv->x : nullptr;
+    a.conv_w = conv != nullptr ? conv->w : nullptr;
+    a.conv_state = conv != nullptr ? conv->state : nullptr;
+    a.conv_width = conv != nullptr ? conv->width : 0;
     a.ws = ws;
     return launch_status(gdn::launch_prefill(a, static_cast<hipStream_t>(stream)), what);
 }
@@ -236,6 +262,19 @@ int gdn_prefill_chunked_ckpt(const gdn_dims_t* dims, const void* q, const void* 
     return prefill_run(dims, q, k, v, g, beta, cu_seqlens, n_seqs, total_tokens, chunk,
                        state_pool, n_slots, slots, has_init, ckpt_cu, ckpt_pos, ckpt_slots,
                        n_ckpt, o, workspace, ws_bytes, stream, "gdn_prefill_chunked_ckpt");
+}
+
+int gdn_prefill_chunked_conv(const gdn_dims_t* dims, const void* x, const float* conv_w,
+                             int32_t conv_width, void* conv_state, const float* g,
+                             const float* beta, const int32_t* cu_seqlens, int32_t n_seqs,
+                             int32_t total_tokens, int32_t chunk, float* state_pool,
+                             int32_t n_slots, const int32_t* slots, const int32_t* has_init,
+                             void* o, void* workspace, size_t ws_bytes, void* stream) {
+    const ConvIn conv{x, conv_w, conv_width, conv_state};
+    return prefill_run(dims, nullptr, nullptr, nullptr, g, beta, cu_seqlens, n_seqs,
+                       total_tokens, chunk, state_pool, n_slots, slots, has_init, nullptr,
+                       nullptr, nullptr, 0, o, workspace, ws_bytes, stream,
+                       "gdn_prefill_chunked_conv", &conv);
 }
 
 int gdn_decode_step(const gdn_dims_t* dims, const void* q, const void* k, const void* v,

@@ -84,6 +84,34 @@ __device__ __forceinline__ int wave_id() { return (int)(threadIdx.x / WAVE); }
 // arithmetic that follows.
 __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
 
+// SiLU in fp32 after the short convolution: x * 1 / (1 + 2^(-x log2 e)) on the hardware
+// exp2 and reciprocal (about 1 ulp each; an overflowing exponential gives 1/inf = 0, so the
+// result tends to -0 for very negative x and to x for large x). Every convolution kernel
+// calls this, so the standalone convolution and the ones fused into the prefill and the
+// decode step agree bit for bit.
+__device__ __forceinline__ float silu_f32(float x) {
+    const float e = __builtin_amdgcn_exp2f(x * -1.4426950408889634f);
+    return x * __builtin_amdgcn_rcpf(1.f + e);
+}
+
+// Rotation inside each 16-lane row of the wave (DPP row_ror:D): lane l receives the value
+// of lane (l & ~15) | ((l - D) & 15).
+// Every lane has a source in a rotation, so no fallback value is needed.
+template <int D>
+__device__ __forceinline__ float row_ror(float v) {
+    static_assert(D >= 1 && D <= 15, "row_ror distance");
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 + D, 0xF, 0xF, true));
+}
+template <int D>
+__device__ __forceinline__ bf16x8 row_ror(bf16x8 v) {
+    static_assert(D >= 1 && D <= 15, "row_ror distance");
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    i32x4 t = __builtin_bit_cast(i32x4, v);
+#pragma unroll
+    for (int i = 0; i < 4; i++) t[i] = __builtin_amdgcn_mov_dpp(t[i], 0x120 + D, 0xF, 0xF, true);
+    return __builtin_bit_cast(bf16x8, t);
+}
+
 // Sum across lanes that share (lane % width) ... reduction over the `width`-lane groups
 // formed by xor distances 1..width/2.
 template <int WIDTH>

@@ -47,6 +47,14 @@ struct PrefillArgs {
     // tokens of the sequence, stored in pool slot ckpt_slots[i]
     const int32_t *ckpt_cu, *ckpt_pos, *ckpt_slots;
     int n_ckpt;
+    // fused short convolution (conv_width == 0: q, k, v are given). x is the raw q|k|v
+    // projection [T, 3 H d], conv_w [3 H d, conv_width] fp32; conv_state [n_slots, 3 H d,
+    // conv_width - 1] in the element type holds the history of the slot's sequence (null:
+    // zero history, nothing stored)
+    const void* x;
+    const float* conv_w;
+    void* conv_state;
+    int conv_width;
     PrefillWs ws;
 };
 
@@ -129,5 +137,9 @@ struct ConvArgs {
     void* y;
 };
 hipError_t launch_conv1d(const ConvArgs& a, hipStream_t stream);
+
+// After a conv-fused prefill: conv_state[slots[n]] <- the last width-1 rows of sequence n's
+// raw projection, taking the rows before its start from the old history (has_init) or zero.
+hipError_t launch_conv_state_update(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace gdn

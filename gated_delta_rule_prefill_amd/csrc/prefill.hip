@@ -7,6 +7,10 @@ namespace gdn {
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_scan_bf16(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_scan_f32(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_conv_prep_bf16(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_conv_prep_f32(const PrefillArgs& a, hipStream_t s);
 
 // seq_first[n] = sum_{s < n} ceil(len_s / C), n = 0..n_seqs (one workgroup, tiled scan).
 __global__ __launch_bounds__(256) void seq_first_kernel(const int32_t* cu, int n_seqs, int C,
@@ -80,7 +84,14 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     // empty sequence list is a no-op
     if (a.n_seqs == 0) return hipSuccess;
     (void)hipGetLastError();  // report only errors raised by this call's launches
-    return a.dtype == 1 ? launch_prefill_bf16(a, s) : launch_prefill_f32(a, s);
+    const bool b16 = a.dtype == 1;
+    if (a.conv_width == 0) return b16 ? launch_prefill_bf16(a, s) : launch_prefill_f32(a, s);
+    // conv-fused: prep forms q, k, v from x; the conv history is advanced only after every
+    // prep workgroup has read the old one (same stream, next launch)
+    hipError_t e = b16 ? launch_prefill_conv_prep_bf16(a, s) : launch_prefill_conv_prep_f32(a, s);
+    if (e == hipSuccess) e = b16 ? launch_prefill_scan_bf16(a, s) : launch_prefill_scan_f32(a, s);
+    if (e == hipSuccess && a.conv_state != nullptr) e = launch_conv_state_update(a, s);
+    return e;
 }
 
 }  // namespace gdn

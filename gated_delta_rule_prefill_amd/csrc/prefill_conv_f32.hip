@@ -1,0 +1,8 @@
+// fp32 instantiations of the prefill prep with the short convolution fused into its
+// loads (the scan that follows is the one of the plain prefill).
+#include "prefill_impl.h"
+namespace gdn {
+hipError_t launch_prefill_conv_prep_f32(const PrefillArgs& a, hipStream_t s) {
+    return prefill_conv_prep_typed<float>(a, s);
+}
+}  // namespace gdn

@@ -234,7 +234,14 @@ template <> struct Ident<float> {
 // Scalar gate: V^T shares its LDS with A/R (46.6 KiB at d = 128, C = 64) and the register
 // budget allows three waves per SIMD, so three workgroups share a CU and hide more of the
 // load latency of each unit's q, k, v.
-template <typename T, int DK, int DV, int C, bool PERKEY>
+//
+// CONV: q, k and v are formed on load from the raw projection x by the causal short
+// convolution and SiLU ([LA-Infra] "去掉分母引入卷积"): each lane loads its own row of x and
+// the conv taps on earlier rows reach it through a rotation inside its 16-lane row group;
+// lanes 13..15 also load the three rows before the block (from the previous block, the
+// previous chunk, or the sequence's conv history). The weights of the head's channels sit
+// in LDS for the duration of P0.
+template <typename T, int DK, int DV, int C, bool PERKEY, bool CONV>
 __global__ __launch_bounds__(PF_THREADS)
 __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(PrefillArgs a) {
     using F = PfCfg<T, DK, DV, C>;
@@ -264,7 +271,71 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
 
     // ------------------------------------------------------------------------ P0 loads
     frag kf[NK], qf[NK], vf[NV];
-    {
+    // conv-fused: weights (registers, then LDS), own rows and halo rows of x
+    constexpr int NWL = CONV ? (3 * DK * 4 + PF_THREADS - 1) / PF_THREADS : 1;
+    float wreg[NWL];
+    frag xh[CONV ? 2 * NK + NV : 1];
+    static_assert(!CONV || DK == DV, "the fused convolution assumes d_k == d_v");
+    static_assert(!CONV || F::LDC * sizeof(T) >= 48, "conv weights do not fit the K_in^T area");
+    if constexpr (CONV) {
+        const int W = a.conv_width;
+        // tap d (token t - d) of channel ch of plane p at [(p DK + ch) 4 + d]; taps >= W are 0
+#pragma unroll
+        for (int k = 0; k < NWL; k++) {
+            const int i = tid + k * PF_THREADS;
+            const int p = i / (DK * 4), ch = (i >> 2) % DK, d = i & 3;
+            wreg[k] = (i < 3 * DK * 4 && d < W)
+                          ? a.conv_w[((size_t)(p * H + h) * DK + ch) * W + (W - 1 - d)]
+                          : 0.f;
+        }
+        sched_fence();
+        const size_t XC = (size_t)3 * H * DK;
+        const T* xb = reinterpret_cast<const T*>(a.x);
+        const int ss = a.cu_seqlens[loc.seq];
+        const int hrow = loc.tok0 + w * 16 + r16 - 16;  // halo row of lanes 13..15
+        const bool hlane = own && r16 >= 13;
+        // a row past the chunk's last token feeds only padding rows: never loaded
+        const bool hin = hlane && hrow >= ss && hrow < loc.tok0 + loc.len;
+        const T* xo = xb + (size_t)(loc.tok0 + row) * XC + (size_t)h * DK;
+        const T* xhp = xb + (size_t)(hin ? hrow : 0) * XC + (size_t)h * DK;
+#pragma unroll
+        for (int f = 0; f < 2 * NK + NV; f++) {
+            const int p = f < NK ? 0 : (f < 2 * NK ? 1 : 2);
+            const int kb = f - p * NK;
+            const int c0 = kb * KB + g4 * KPL;
+            const size_t po = (size_t)p * H * DK + c0;
+            frag xv = MM::zero(), hv = MM::zero();
+            if (rvalid && c0 < DK) xv = MM::load(xo + po);
+            if (hin && c0 < DK) hv = MM::load(xhp + po);
+            if (p == 0) qf[kb] = xv;
+            else if (p == 1) kf[kb] = xv;
+            else vf[kb] = xv;
+            xh[f] = hv;
+        }
+        // rows before the sequence start: the slot's conv history, if it has one
+        const int slot = a.slots[loc.seq];
+        const bool hist = a.conv_state != nullptr && 0 <= slot && slot < a.n_slots &&
+                          a.has_init != nullptr && a.has_init[loc.seq] != 0;
+        const int m = ss - hrow;  // 1..W-1 for a history row
+        if (hist && hlane && m >= 1 && m <= W - 1) {
+            const T* cs = reinterpret_cast<const T*>(a.conv_state) +
+                          ((size_t)slot * XC + (size_t)h * DK) * (W - 1) + (W - 1 - m);
+#pragma unroll
+            for (int f = 0; f < 2 * NK + NV; f++) {
+                const int p = f < NK ? 0 : (f < 2 * NK ? 1 : 2);
+                const int c0 = (f - p * NK) * KB + g4 * KPL;
+                if (c0 < DK) {
+                    const T* src = cs + ((size_t)p * H * DK + c0) * (W - 1);
+                    if constexpr (KPL == 1) xh[f] = src[0];
+                    else {
+#pragma unroll
+                        for (int e = 0; e < KPL; e++) xh[f][e] = src[(size_t)e * (W - 1)];
+                    }
+                }
+            }
+        }
+        sched_fence();
+    } else {
         const size_t tk = ((size_t)(loc.tok0 + row) * H + h);
         const T* kg = reinterpret_cast<const T*>(a.k) + tk * DK;
         const T* qg = reinterpret_cast<const T*>(a.q) + tk * DK;
@@ -302,6 +373,51 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
         gsc = (lane < loc.len && lane < C) ? a.g[(size_t)(loc.tok0 + lane) * H + h] : 0.f;
     if (tid < C && tid < loc.len) bval = a.beta[(size_t)(loc.tok0 + tid) * H + h];
 
+    if constexpr (CONV) {
+        float* wl = reinterpret_cast<float*>(&sm.kint[0][0]);  // K_in^T is written after #1
+#pragma unroll
+        for (int k = 0; k < NWL; k++) {
+            const int i = tid + k * PF_THREADS;
+            if (i < 3 * DK * 4) wl[i] = wreg[k];
+        }
+        lds_barrier();  // #0: conv weights in LDS
+#pragma unroll
+        for (int f = 0; f < 2 * NK + NV; f++) {
+            if (!own) break;
+            const int p = f < NK ? 0 : (f < 2 * NK ? 1 : 2);
+            const int kb = f - p * NK;
+            const int c0 = kb * KB + g4 * KPL;
+            frag& xf = p == 0 ? qf[kb] : (p == 1 ? kf[kb] : vf[kb]);
+            if (c0 >= DK) continue;  // zero padding columns stay zero
+            // x at t - d (d = 1..3) arrives by rotating the row group by d: lane s sends to
+            // lane (s + d) mod 16, its own row if that lane follows it, else (wrapping
+            // around, s >= 16 - d) the halo row that lane needs
+            const frag x1 = row_ror<1>(r16 >= 15 ? xh[f] : xf);
+            const frag x2 = row_ror<2>(r16 >= 14 ? xh[f] : xf);
+            const frag x3 = row_ror<3>(r16 >= 13 ? xh[f] : xf);
+            frag out;
+#pragma unroll
+            for (int e = 0; e < KPL; e++) {
+                const f32x4 wt = *reinterpret_cast<const f32x4*>(wl + (p * DK + c0 + e) * 4);
+                auto el = [&](const frag& v) {
+                    if constexpr (KPL == 1) return to_f32(v);
+                    else return to_f32(v[e]);
+                };
+                // oldest tap first, as the standalone convolution accumulates; the taps a
+                // narrower convolution lacks have weight 0 and add exactly +0 to the zero
+                // accumulator (finite inputs)
+                float acc = fmaf(wt[3], el(x3), 0.f);
+                acc = fmaf(wt[2], el(x2), acc);
+                acc = fmaf(wt[1], el(x1), acc);
+                acc = fmaf(wt[0], el(xf), acc);
+                const T y = from_f32<T>(silu_f32(acc));
+                if constexpr (KPL == 1) out = y;
+                else out[e] = y;
+            }
+            xf = rvalid ? out : MM::zero();  // rows past the chunk stay zero
+        }
+    }
+
     // L2 norm of q and k rows: a row lives in the 4 lane groups sharing r16
     if (a.l2norm) {
         float sk = 0.f, sq = 0.f;
@@ -312,8 +428,9 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
                 float x, y;
                 if constexpr (KPL == 1) { x = to_f32(kf[kb]); y = to_f32(qf[kb]); }
                 else { x = to_f32(kf[kb][e]); y = to_f32(qf[kb][e]); }
-                sk += x * x;
-                sq += y * y;
+                // explicit FMAs: every instantiation rounds the same way
+                sk = fmaf(x, x, sk);
+                sq = fmaf(y, y, sq);
             }
         }
         sk += __shfl_xor(sk, 16, WAVE);
@@ -1078,11 +1195,11 @@ void scan_launch(const PrefillArgs& a, int nvb, unsigned grid, hipStream_t s) {
     }
 }
 
-template <typename T, int D, int C, bool PERKEY>
-hipError_t prefill_launch_cfg(const PrefillArgs& a, hipStream_t s) {
+template <typename T, int D, int C, bool PERKEY, bool CONV>
+hipError_t prefill_prep_cfg(const PrefillArgs& a, hipStream_t s) {
     const size_t smem = sizeof(PrepSmem<T, D, D, C, PERKEY>);
     static_assert(sizeof(PrepSmem<T, D, D, C, PERKEY>) <= 160 * 1024, "prep LDS over 160 KiB");
-    auto prep = prefill_prep_kernel<T, D, D, C, PERKEY>;
+    auto prep = prefill_prep_kernel<T, D, D, C, PERKEY, CONV>;
     // dynamic LDS above 64 KiB must be allowed explicitly (idempotent, no library state);
     // done before the first launch so a refusal launches nothing
     hipError_t e = hipFuncSetAttribute((const void*)prep,
@@ -1097,6 +1214,11 @@ hipError_t prefill_launch_cfg(const PrefillArgs& a, hipStream_t s) {
     const int64_t nchunk = a.ws.max_chunks;
     if (nchunk > 0)
         hipLaunchKernelGGL(prep, dim3((unsigned)(nchunk * a.H)), dim3(PF_THREADS), smem, s, a);
+    return hipGetLastError();
+}
+
+template <typename T, int D, int C, bool PERKEY>
+hipError_t prefill_scan_cfg(const PrefillArgs& a, hipStream_t s) {
     // The value width per workgroup (NVB 16-column tiles) is the widest that still leaves
     // at least one workgroup per CU: wider tiles share each chunk's operand stream over more
     // columns (fewer bytes per column), narrower ones run more sequential chains at once.
@@ -1116,31 +1238,50 @@ hipError_t prefill_launch_cfg(const PrefillArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename T, int D, int C>
-hipError_t prefill_launch_gate(const PrefillArgs& a, hipStream_t s) {
-    return a.gate == 1 ? prefill_launch_cfg<T, D, C, true>(a, s)
-                       : prefill_launch_cfg<T, D, C, false>(a, s);
-}
-
-template <typename T, int D>
-hipError_t prefill_launch_chunk(const PrefillArgs& a, hipStream_t s) {
-    switch (a.chunk) {
-        case 16: return prefill_launch_gate<T, D, 16>(a, s);
-        case 32: return prefill_launch_gate<T, D, 32>(a, s);
-        case 64: return prefill_launch_gate<T, D, 64>(a, s);
+// Calls fn(D, C, PERKEY), each an integral constant, for the call's head dim, chunk size
+// and gate kind.
+template <typename Fn>
+hipError_t prefill_dispatch(const PrefillArgs& a, Fn&& fn) {
+    using std::integral_constant;
+    auto gate = [&](auto D, auto C) {
+        return a.gate == 1 ? fn(D, C, std::true_type{}) : fn(D, C, std::false_type{});
+    };
+    auto chunk = [&](auto D) {
+        switch (a.chunk) {
+            case 16: return gate(D, integral_constant<int, 16>{});
+            case 32: return gate(D, integral_constant<int, 32>{});
+            case 64: return gate(D, integral_constant<int, 64>{});
+        }
+        return hipErrorInvalidValue;
+    };
+    switch (a.dk) {
+        case 16: return chunk(integral_constant<int, 16>{});
+        case 32: return chunk(integral_constant<int, 32>{});
+        case 64: return chunk(integral_constant<int, 64>{});
+        case 128: return chunk(integral_constant<int, 128>{});
     }
     return hipErrorInvalidValue;
 }
 
+// prep (q, k, v given) followed by the scan
 template <typename T>
 hipError_t prefill_launch_typed(const PrefillArgs& a, hipStream_t s) {
-    switch (a.dk) {
-        case 16: return prefill_launch_chunk<T, 16>(a, s);
-        case 32: return prefill_launch_chunk<T, 32>(a, s);
-        case 64: return prefill_launch_chunk<T, 64>(a, s);
-        case 128: return prefill_launch_chunk<T, 128>(a, s);
-    }
-    return hipErrorInvalidValue;
+    return prefill_dispatch(a, [&](auto D, auto C, auto PK) {
+        hipError_t e = prefill_prep_cfg<T, D, C, PK, false>(a, s);
+        return e != hipSuccess ? e : prefill_scan_cfg<T, D, C, PK>(a, s);
+    });
+}
+template <typename T>
+hipError_t prefill_scan_typed(const PrefillArgs& a, hipStream_t s) {
+    return prefill_dispatch(a, [&](auto D, auto C, auto PK) {
+        return prefill_scan_cfg<T, D, C, PK>(a, s);
+    });
+}
+template <typename T>
+hipError_t prefill_conv_prep_typed(const PrefillArgs& a, hipStream_t s) {
+    return prefill_dispatch(a, [&](auto D, auto C, auto PK) {
+        return prefill_prep_cfg<T, D, C, PK, true>(a, s);
+    });
 }
 
 }  // namespace gdn

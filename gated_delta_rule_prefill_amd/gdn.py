@@ -48,6 +48,8 @@ _SIGS = {
                             _SZ, _P],
     "gdn_prefill_chunked_ckpt": [_DIMS, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _I, _P, _P,
                                  _P, _P, _P, _I, _P, _P, _SZ, _P],
+    "gdn_prefill_chunked_conv": [_DIMS, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _P, _I, _P,
+                                 _P, _P, _P, _SZ, _P],
     "gdn_decode_step": [_DIMS, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, _P],
     "gdn_decode_spec": [_DIMS, _P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _P, _P],
     "gdn_decode_fused": [_DIMS, _P, _P, _I, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I, _P, _I,
@@ -193,6 +195,35 @@ def gdn_prefill_chunked_ckpt(q, k, v, g, beta, cu_seqlens, chunk, state_pool, sl
         int(n), int(T), int(chunk), _ptr(state_pool), int(state_pool.shape[0]), _ptr(slots),
         _ptr(has_init), _ptr(ckpt_cu), _ptr(ckpt_pos), _ptr(ckpt_slots), int(ckpt_pos.numel()),
         _ptr(o), _ptr(workspace), int(workspace.numel()), _stream(stream)))
+    return o
+
+
+def gdn_prefill_chunked_conv(x, conv_w, g, beta, cu_seqlens, chunk, state_pool, slots,
+                             conv_state=None, has_init=None, scale=1.0, qk_l2norm=False,
+                             o=None, workspace=None, stream=None):
+    """Chunked prefill with the short convolution and SiLU fused into its loads.
+    x [T, 3 H d] raw q|k|v projection; conv_w [3 H d, W] fp32; conv_state [slots, 3 H d, W-1]
+    (x's dtype) or None: read as the history of sequences with has_init and overwritten with
+    each sequence's last W-1 rows. g [T,H] or [T,H,d]; other arguments as
+    gdn_prefill_chunked. Returns o [T, H, d]."""
+    T = x.shape[0]
+    H = beta.shape[1]
+    d = x.shape[1] // (3 * H)
+    W = conv_w.shape[1]
+    n = cu_seqlens.numel() - 1
+    perkey = g.dim() == 3
+    if o is None:
+        o = torch.empty((T, H, d), dtype=x.dtype, device=x.device)
+    need = gdn_prefill_workspace_bytes(H, d, d, _dtype_code(x), perkey, n, T, chunk)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _dev(x, conv_w, conv_state, g, beta, cu_seqlens, state_pool, slots, has_init, o, workspace)
+    dims = make_dims(H, d, d, _dtype_code(x), perkey, scale, qk_l2norm)
+    _check("gdn_prefill_chunked_conv", lib().gdn_prefill_chunked_conv(
+        ctypes.byref(dims), _ptr(x), _ptr(conv_w), int(W), _ptr(conv_state), _ptr(g),
+        _ptr(beta), _ptr(cu_seqlens), int(n), int(T), int(chunk), _ptr(state_pool),
+        int(state_pool.shape[0]), _ptr(slots), _ptr(has_init), _ptr(o), _ptr(workspace),
+        int(workspace.numel()), _stream(stream)))
     return o
 
 

@@ -225,6 +225,45 @@ def fused_decode_step(seed: int, batch: int, n_slots: int, H: int, d: int, width
 
 
 @dataclass
+class ConvPrefillInputs:
+    x: torch.Tensor           # [T, 3 H d] dtype, q|k|v before the convolution
+    conv_w: torch.Tensor      # [3 H d, W] fp32
+    g: torch.Tensor           # [T, H] or [T, H, d] fp32
+    beta: torch.Tensor        # [T, H] fp32
+    cu_seqlens: torch.Tensor  # [n + 1] int32
+    conv_hist: torch.Tensor   # [n, 3 H d, W - 1] dtype, conv history per sequence
+    init_states: torch.Tensor  # [n, H, d, d] fp32
+    H: int
+    d: int
+    scale: float
+    qk_l2norm: bool
+
+
+def conv_prefill(seed: int, lengths, H: int, d: int, width: int = 4, dtype=BF16,
+                 perkey: bool = True, gate_shift: float = 3.0) -> ConvPrefillInputs:
+    """Packed varlen inputs of the conv-fused prefill, as the KDA recipe: raw q|k|v ~ randn,
+    conv weights randn/2, gates logsigmoid(randn + gate_shift) (per key or per head), beta =
+    sigmoid(randn), conv histories ~ randn and initial states ~ randn/sqrt(d); q and k are
+    L2-normalised in the kernel after the convolution."""
+    gen = _gen(seed)
+    lengths = [int(x) for x in lengths]
+    T, n, CH = sum(lengths), len(lengths), 3 * H * d
+    x = torch.randn(T, CH, generator=gen).to(dtype)
+    w = torch.randn(CH, width, generator=gen) / 2
+    a = torch.randn(*((T, H, d) if perkey else (T, H)), generator=gen)
+    b = torch.randn(T, H, generator=gen)
+    hist = torch.randn(n, CH, width - 1, generator=gen).to(dtype)
+    init = torch.randn(n, H, d, d, generator=gen) / d ** 0.5
+    cu = torch.zeros(n + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    return ConvPrefillInputs(
+        x=x.contiguous(), conv_w=w.contiguous(),
+        g=torch.nn.functional.logsigmoid(a + gate_shift).contiguous(),
+        beta=beta_from_normal(b).contiguous(), cu_seqlens=cu, conv_hist=hist.contiguous(),
+        init_states=init.contiguous(), H=H, d=d, scale=1.0 / d ** 0.5, qk_l2norm=True)
+
+
+@dataclass
 class KdaVarlenInputs:
     x: torch.Tensor           # [T, 3*H*d] bf16, raw fused q|k|v projection output
     conv_w: torch.Tensor      # [3*H*d, 4] fp32

@@ -168,6 +168,35 @@ int gdn_prefill_chunked_ckpt(const gdn_dims_t* dims, const void* q, const void* 
                              const int32_t* ckpt_slots, int32_t n_ckpt, void* o,
                              void* workspace, size_t ws_bytes, void* stream);
 
+/* Chunked prefill that takes the raw q|k|v projection and applies the causal short
+ * convolution and SiLU ([LA-Infra] "去掉分母引入卷积") while loading it, so q, k and v never
+ * go to memory; everything after is gdn_prefill_chunked. For sequence n, head h, channel c
+ * of plane p (q, k, v), token t of the sequence and W = conv_width:
+ *   q|k|v[t, h, c] = SiLU(sum_{j<W} w[ch, j] x[t - (W-1) + j, ch]),  ch = p H d + h d + c,
+ * accumulated in fp32 from the oldest tap and rounded to dtype, bit-identical to
+ * gdn_conv1d_silu(planes = 3) followed by gdn_prefill_chunked on its three planes. A token
+ * before the sequence start is the slot's conv history conv_state[slot, ch, W-1-m] (m tokens
+ * before the start, m <= W-1) when conv_state is given and has_init[n] is nonzero, else 0.
+ * After the call, conv_state[slot] (when given, for valid slots) holds the last W-1 inputs
+ * of the sequence before the convolution, column 0 the oldest, taking inputs from before
+ * the start from the old history or zero: the layout gdn_decode_fused reads and advances,
+ * so a prefill followed by fused decode steps continues the sequence ([LA-Infra]
+ * "vLLM中Decode的实现": one conv-state pool over the concatenated channels).
+ *   x            [total_tokens, 3 H d_k] dtype (device), 16-byte aligned
+ *   conv_w       [3 H d_k, conv_width] fp32 (device); conv_width 2, 3 or 4
+ *   conv_state   [n_slots, 3 H d_k, conv_width - 1] dtype (device) or NULL (zero history,
+ *                nothing stored); addressed by the same slot as state_pool
+ *   g, beta, cu_seqlens, chunk, state_pool, slots, has_init, o, workspace: as
+ *   gdn_prefill_chunked, whose workspace query applies (d_k == d_v). q, k and v are not
+ *   passed. With zero tokens the conv states still advance (unchanged with history, zeroed
+ *   without). */
+int gdn_prefill_chunked_conv(const gdn_dims_t* dims, const void* x, const float* conv_w,
+                             int32_t conv_width, void* conv_state, const float* g,
+                             const float* beta, const int32_t* cu_seqlens, int32_t n_seqs,
+                             int32_t total_tokens, int32_t chunk, float* state_pool,
+                             int32_t n_slots, const int32_t* slots, const int32_t* has_init,
+                             void* o, void* workspace, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------------- decode */
 
 /* One recurrent step for a batch of requests, one token each, states read and written in

@@ -21,7 +21,7 @@ def _declared():
 
 def test_header_declares_the_abi():
     names = _declared()
-    for n in ("gdn_prefill_chunked", "gdn_prefill_chunked_ckpt",
+    for n in ("gdn_prefill_chunked", "gdn_prefill_chunked_ckpt", "gdn_prefill_chunked_conv",
               "gdn_prefill_workspace_bytes", "gdn_decode_step", "gdn_decode_spec",
               "gdn_decode_fused",
               "gdn_decode_deltalog", "gdn_deltalog_workspace_bytes", "gdn_deltalog_reset",
@@ -169,6 +169,30 @@ def test_decode_spec_rejects_bad_arguments(kw, status):
 
 def test_decode_spec_zero_batch_is_a_noop():
     assert _spec(_dims(), batch=0, q=None, num_accepted=None) == 0
+
+
+def _prefill_conv(dims, width=4, ws_bytes=1 << 40, **kw):
+    a = dict(x=FAKE, w=FAKE, cs=None, g=FAKE, beta=FAKE, cu=FAKE, n=2, T=100, chunk=64,
+             pool=FAKE, n_slots=4, slots=FAKE, has_init=None, o=FAKE, ws=FAKE)
+    a.update(kw)
+    return gdn.load().gdn_prefill_chunked_conv(
+        ctypes.byref(dims), a["x"], a["w"], width, a["cs"], a["g"], a["beta"], a["cu"], a["n"],
+        a["T"], a["chunk"], a["pool"], a["n_slots"], a["slots"], a["has_init"], a["o"], a["ws"],
+        ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(width=1), 3), (dict(width=5), 3), (dict(x=None), 1), (dict(w=None), 1),
+    (dict(x=FAKE + 2), 4), (dict(cs=FAKE + 8), 4), (dict(g=None), 1), (dict(chunk=48), 3),
+    (dict(n_slots=0), 2), (dict(ws_bytes=16), 5),
+])
+def test_prefill_conv_rejects_bad_arguments(kw, status):
+    assert _prefill_conv(_dims(gate=1), **kw) == status
+    assert gdn.gdn_last_error() != ""
+
+
+def test_prefill_conv_zero_sequences_is_a_noop():
+    assert _prefill_conv(_dims(), n=0, x=None, ws=None) == 0
 
 
 def _fused(dims, width=4, lb=-5.0, batch=8, **kw):
