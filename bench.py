@@ -249,7 +249,7 @@ def bench_deltalog(cycles=4, warm_cycles=1, M=8, perkey=False):
                          + (", per-key (KDA) decay" if perkey else ""))
 
 
-def bench_kda(steps=3, warmup=1):
+def bench_kda(steps=5, warmup=3, rounds=3):
     x = inputs.kda_varlen_config(0)
     T = x.x.shape[0]
     xd, wd, cud, g, b = (t.to(DEV) for t in (x.x, x.conv_w, x.cu_seqlens, x.g, x.beta))
@@ -271,8 +271,13 @@ def bench_kda(steps=3, warmup=1):
         gdn.gdn_prefill_chunked_conv(xd, wd, g, b, cud, x.chunk, pool, slots, scale=x.scale,
                                      qk_l2norm=True, o=o, workspace=ws)
 
-    ms, _ = ev_time(fused, steps, warmup)
-    ms_two, _ = ev_time(two_launch, steps, warmup)
+    # alternate the two variants so both see the same clock and thermal state; the median
+    # round of each is reported, every round alongside
+    f_ms, t_ms = [], []
+    for r in range(rounds):
+        f_ms.append(ev_time(fused, steps, warmup if r == 0 else 1)[0])
+        t_ms.append(ev_time(two_launch, steps, warmup if r == 0 else 1)[0])
+    ms, ms_two = sorted(f_ms)[rounds // 2], sorted(t_ms)[rounds // 2]
     lengths = (x.cu_seqlens[1:] - x.cu_seqlens[:-1]).tolist()
     # the raw projection is read once in place of q, k, v
     byts = traffic.prefill_bytes(T, H, d, d, 2, True, 8, False)
@@ -280,6 +285,7 @@ def bench_kda(steps=3, warmup=1):
                 GBps=byts / (ms * 1e-3) / 1e9, hbm_frac=byts / (ms * 1e-3) / traffic.HBM_PEAK_BPS,
                 flops=traffic.prefill_flops(lengths, H, d, d, x.chunk),
                 ms_conv_then_prefill=ms_two,
+                ms_rounds=[round(x, 4) for x in f_ms], ms_conv_then_prefill_rounds=[round(x, 4) for x in t_ms],
                 workload=f"KDA varlen prefill, 8 seqs (T_total={T}), H=32, d=128, conv+SiLU "
                          "fused into the prefill, per-key gates, in-kernel L2 norm")
 
