@@ -7,6 +7,10 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <initializer_list>
+#include <utility>
+#include <vector>
+
 #include "../../include/gdn.h"
 #include "gdn_launch.h"
 
@@ -59,6 +63,44 @@ int check_dims(const gdn_dims_t* d) {
         if ((p) != nullptr && !aligned16(p))                                         \
             return fail(GDN_ERR_ALIGN, "%s is not 16-byte aligned", #p);             \
     } while (0)
+
+// Debug builds (GDN_DEBUG_CHECKS) also verify what the kernels assume but the host cannot
+// see without reading device memory: the valid slot indices of one call are distinct. The
+// check copies the slot arrays to the host, which synchronises `stream`; release builds
+// skip it. A repeated slot returns GDN_ERR_SHAPE before any launch.
+#ifdef GDN_DEBUG_CHECKS
+int debug_distinct_slots(std::initializer_list<std::pair<const int32_t*, int64_t>> lists,
+                         int32_t n_slots, void* stream, const char* what) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::vector<char> seen((size_t)n_slots, 0);
+    for (const auto& l : lists) {
+        if (l.first == nullptr || l.second <= 0) continue;
+        std::vector<int32_t> h((size_t)l.second);
+        if (hipMemcpyAsync(h.data(), l.first, sizeof(int32_t) * h.size(), hipMemcpyDeviceToHost,
+                           s) != hipSuccess ||
+            hipStreamSynchronize(s) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(GDN_ERR_LAUNCH, "%s: debug check could not read the slot indices", what);
+        }
+        for (int32_t v : h) {
+            if (v < 0 || v >= n_slots) continue;
+            if (seen[(size_t)v]) return fail(GDN_ERR_SHAPE, "%s: slot %d used twice", what, v);
+            seen[(size_t)v] = 1;
+        }
+    }
+    return GDN_OK;
+}
+#define DEBUG_DISTINCT_SLOTS(lists, n_slots, what)                                  \
+    do {                                                                            \
+        int st_ = debug_distinct_slots(lists, n_slots, stream, what);               \
+        if (st_) return st_;                                                        \
+    } while (0)
+#else
+#define DEBUG_DISTINCT_SLOTS(lists, n_slots, what) \
+    do {                                           \
+    } while (0)
+#endif
+#define SLOT_LISTS(...) (std::initializer_list<std::pair<const int32_t*, int64_t>>{__VA_ARGS__})
 
 int launch_status(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
@@ -180,6 +222,8 @@ int prefill_run(const gdn_dims_t* dims, const void* q, const void* k, const void
     a.conv_state = conv != nullptr ? conv->state : nullptr;
     a.conv_width = conv != nullptr ? conv->width : 0;
     a.ws = ws;
+    DEBUG_DISTINCT_SLOTS(SLOT_LISTS({slots, n_seqs}, {a.ckpt_slots, (int64_t)n_ckpt}), n_slots,
+                         what);
     return launch_status(gdn::launch_prefill(a, static_cast<hipStream_t>(stream)), what);
 }
 
@@ -223,6 +267,7 @@ int decode_run(const gdn_dims_t* dims, const void* q, const void* k, const void*
     a.o = o;
     a.num_accepted = spec ? num_accepted : nullptr;
     a.n_pos = n_pos;
+    DEBUG_DISTINCT_SLOTS(SLOT_LISTS({slots, (int64_t)batch * (spec ? n_pos : 1)}), n_slots, what);
     return launch_status(gdn::launch_decode(a, static_cast<hipStream_t>(stream)), what);
 }
 
@@ -344,6 +389,7 @@ int gdn_decode_fused(const gdn_dims_t* dims, const void* x, const float* conv_w,
     a.slots = slots;
     a.batch = batch;
     a.o = o;
+    DEBUG_DISTINCT_SLOTS(SLOT_LISTS({slots, batch}), n_slots, "gdn_decode_fused");
     return launch_status(gdn::launch_fused_decode(a, static_cast<hipStream_t>(stream)),
                          "gdn_decode_fused");
 }
@@ -409,6 +455,7 @@ int gdn_decode_deltalog(const gdn_dims_t* dims, const void* q, const void* k, co
     a.g = g;
     a.beta = beta;
     a.o = o;
+    DEBUG_DISTINCT_SLOTS(SLOT_LISTS({slots, batch}), n_slots, "gdn_decode_deltalog");
     return launch_status(gdn::launch_deltalog(a, static_cast<hipStream_t>(stream)),
                          "gdn_decode_deltalog");
 }
@@ -425,6 +472,7 @@ static int deltalog_maint(const gdn_dims_t* dims, const gdn_deltalog_pool_t* poo
     REQUIRE_PTR(slots);
     if (n_slots < 1) return fail(GDN_ERR_SHAPE, "n_slots must be >= 1 (got %d)", n_slots);
     gdn::DeltaLogArgs a = dl_args(dims, pool, n_slots, slots, n);
+    DEBUG_DISTINCT_SLOTS(SLOT_LISTS({slots, n}), n_slots, what);
     return launch_status(gdn::launch_deltalog_maint(a, mode, static_cast<hipStream_t>(stream)),
                          what);
 }

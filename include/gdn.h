@@ -41,6 +41,10 @@
  *     before any launch; a call that returns an error has launched nothing and changed no
  *     memory. gdn_last_error() returns a thread-local description of the last failure.
  *     No C++ exception crosses this boundary.
+ *   - Debug build (libgdn_debug.so, same kernels): every entry point that takes slot indices
+ *     first copies them to the host, synchronising `stream`, and returns GDN_ERR_SHAPE if a
+ *     valid slot appears twice in the call. The release library does not read device
+ *     arguments on the host, so there a repeated slot is undefined behaviour.
  */
 #ifndef GDN_H_
 #define GDN_H_

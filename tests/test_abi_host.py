@@ -37,6 +37,15 @@ def test_library_exports_every_declared_symbol():
     assert gdn.gdn_abi_version() == 1
 
 
+def test_debug_library_exports_every_declared_symbol():
+    """libgdn_debug.so (C-ABI layer with GDN_DEBUG_CHECKS, same kernels) is built beside
+    libgdn.so and exports the same symbols."""
+    path = os.path.join(os.path.dirname(gdn.LIB_PATH), "libgdn_debug.so")
+    lib = ctypes.CDLL(path)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
 def test_binding_uses_the_c_names():
     for name in _declared():
         assert hasattr(gdn, name), name
