@@ -256,6 +256,11 @@ template <int DK, int DV, bool PERKEY>
 constexpr size_t spec_dyn_bytes(int P) {
     return (size_t)P * ((PERKEY ? 3 : 2) * DK + DV + 2) * sizeof(float);
 }
+// the largest call (d = 128, per-key gate, the most positions the ABI accepts) stays within
+// the 64 KiB a launch gets without raising its LDS limit
+static_assert(spec_dyn_bytes<128, 128, true>(SPEC_MAX_POS) + sizeof(SpecSmem<128, 128>) <=
+                  64 * 1024,
+              "spec-decode LDS at the maximum position count");
 
 template <typename T, int DK, int DV, bool PERKEY>
 __global__ __launch_bounds__(DENSE_THREADS) void spec_decode_kernel(DecodeArgs a) {
