@@ -106,3 +106,43 @@ def test_deltalog_cycle_graph_replays_match_eager():
         assert torch.equal(o, ref_o), r
         for name in ("base", "lbar", "klog", "ulog", "lamlog", "len"):
             assert torch.equal(getattr(pool, name), getattr(ref, name)), (r, name)
+
+
+def test_conv_prefill_graph_replays_match_eager():
+    """The conv-fused prefill with a conv-state pool (prep, scan and the conv-state update in
+    one capture), continuing sequences from their histories and states."""
+    say("case graph: conv-fused prefill")
+    lengths, H, d, W = [300, 2, 128], 2, 64, 4
+    n = len(lengths)
+    x = inputs.conv_prefill(75, lengths, H, d, width=W)
+    X, w, g_, b, cu = to_dev(x.x, x.conv_w, x.g, x.beta, x.cu_seqlens)
+    pool = x.init_states.clone().to(DEV)
+    cs = x.conv_hist.clone().to(DEV)
+    slots = torch.arange(n, dtype=torch.int32, device=DEV)
+    hi = torch.ones(n, dtype=torch.int32, device=DEV)
+    T = x.x.shape[0]
+    ws = torch.empty(gdn.gdn_prefill_workspace_bytes(H, d, d, x.x.dtype, True, n, T, 64),
+                     dtype=torch.uint8, device=DEV)
+    o = torch.empty((T, H, d), dtype=x.x.dtype, device=DEV)
+    kw = dict(has_init=hi, scale=x.scale, qk_l2norm=True)
+    gdn.gdn_prefill_chunked_conv(X, w, g_, b, cu, 64, pool.clone(), slots, conv_state=cs.clone(),
+                                 o=o, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        gdn.gdn_prefill_chunked_conv(X, w, g_, b, cu, 64, pool, slots, conv_state=cs, o=o,
+                                     workspace=ws, **kw)
+    for r in _replays():
+        y = inputs.conv_prefill(76 + r, lengths, H, d, width=W)
+        for s_, n_ in zip((X, g_, b), to_dev(y.x, y.g, y.beta)):
+            s_.copy_(n_)
+        pool.copy_(y.init_states.to(DEV))
+        cs.copy_(y.conv_hist.to(DEV))
+        ref_pool, ref_cs = pool.clone(), cs.clone()
+        ref_o = gdn.gdn_prefill_chunked_conv(X.clone(), w, g_.clone(), b.clone(), cu, 64,
+                                             ref_pool, slots, conv_state=ref_cs, **kw)
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(pool, ref_pool), r
+        assert torch.equal(cs, ref_cs), r
