@@ -156,8 +156,11 @@ __global__ __launch_bounds__(256) void conv_state_update_kernel(PrefillArgs a) {
     const int len = s1 - s0;
 #pragma unroll
     for (int j = 0; j < 3; j++) {
+        // only the W-1 entries that are stored: for j >= W-1 the row would be s1 or later,
+        // past the sequence (and past x for the last one)
         const int r = s1 - (W - 1) + j;
-        if (r >= s0) nw[j] = x[(size_t)r * XC + ch];
+        if (j >= W - 1) nw[j] = from_f32<T>(0.f);
+        else if (r >= s0) nw[j] = x[(size_t)r * XC + ch];
         else nw[j] = j + len < W - 1 ? old[j + len] : from_f32<T>(0.f);
     }
 #pragma unroll

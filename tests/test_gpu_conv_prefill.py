@@ -249,3 +249,32 @@ def test_prefill_then_fused_decode_vs_oracle():
         say(f"   decode step {s}: rel err {e:.2e}")
         assert e <= 1e-2
     assert oracle.rel_err(pool.cpu(), s_ref) <= 1e-2
+
+
+def test_zero_tokens_keep_or_clear_the_histories():
+    """Three empty sequences (total_tokens = 0): the raw projection is never read (x may be
+    empty); a sequence with has_init keeps its state and conv window, one without gets the
+    zero state and a zero window, a slotless one touches nothing."""
+    say("case conv-prefill, zero tokens")
+    H, d, W, n_slots = 2, 32, 3, 5
+    CH = 3 * H * d
+    gen = torch.Generator().manual_seed(47)
+    pool0 = torch.randn(n_slots, H, d, d, generator=gen)
+    cs0 = torch.randn(n_slots, CH, W - 1, generator=gen).to(torch.bfloat16)
+    x = torch.empty(0, CH, dtype=torch.bfloat16, device=DEV)
+    w = (torch.randn(CH, W, generator=gen) / 2).to(DEV)
+    g = torch.empty(0, H, d, device=DEV)
+    b = torch.empty(0, H, device=DEV)
+    cu = torch.zeros(4, dtype=torch.int32, device=DEV)
+    slots = torch.tensor([1, 3, -1], dtype=torch.int32, device=DEV)
+    has = torch.tensor([1, 0, 1], dtype=torch.int32, device=DEV)
+    pool, cs = pool0.clone().to(DEV), cs0.clone().to(DEV)
+    o = gdn.gdn_prefill_chunked_conv(x, w, g, b, cu, 64, pool, slots, conv_state=cs,
+                                     has_init=has, scale=0.1, qk_l2norm=True)
+    torch.cuda.synchronize()
+    pool, cs = pool.cpu(), cs.cpu()
+    assert o.numel() == 0
+    assert torch.equal(pool[1], pool0[1]) and torch.equal(cs[1], cs0[1])
+    assert torch.equal(pool[3], torch.zeros_like(pool[3])) and torch.equal(cs[3], torch.zeros_like(cs[3]))
+    for s in (0, 2, 4):
+        assert torch.equal(pool[s], pool0[s]) and torch.equal(cs[s], cs0[s]), s
