@@ -382,7 +382,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(the core shards by requests and heads with no exchange; see DESIGN.md)",
+              "(the core shards by requests and heads with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
