@@ -120,6 +120,35 @@ def bench_prefill(steps, warmup, ckpt_every=None):
                 n_ckpt=len(pos), ckpt_bytes=len(pos) * H * d * d * 4)
 
 
+def bench_prefill_batch(steps, warmup):
+    """A serving-style prefill batch, 32 sequences x 2048 tokens (H=16, d=128, chunk 64,
+    bf16): the same kernels with the chip filled by (sequence, head) units; its q, k, v (805
+    MB) exceed the 256 MB last-level cache, so one input set is reused."""
+    x = inputs.prefill_batch_config(0)
+    q, k, v, g, b, cu = (t.to(DEV) for t in (x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens))
+    T, H, d = x.q.shape
+    n = x.n_seqs
+    pool = torch.zeros((n, H, d, d), device=DEV)
+    slots = torch.arange(n, dtype=torch.int32, device=DEV)
+    need = gdn.gdn_prefill_workspace_bytes(H, d, d, torch.bfloat16, False, n, T, x.chunk)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    o = torch.empty((T, H, d), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        gdn.gdn_prefill_chunked(q, k, v, g, b, cu, x.chunk, pool, slots, scale=x.scale, o=o,
+                                workspace=ws)
+
+    ms, _ = ev_time(step, max(5, steps // 2), max(3, warmup // 10))
+    byts = traffic.prefill_bytes(T, H, d, d, 2, False, n, False)
+    flops = traffic.prefill_flops([2048] * n, H, d, d, x.chunk)
+    secs = ms * 1e-3
+    return dict(ms=ms, tokens=T, tokens_per_s=T / secs, GBps=byts / secs / 1e9,
+                hbm_frac=byts / secs / traffic.HBM_PEAK_BPS, mfma_TFLOPs=flops / secs / 1e12,
+                mfma_frac_bf16=flops / secs / traffic.BF16_MFMA_PEAK,
+                workload="GDN chunked prefill batch, 32 sequences x 2048 tokens, H=16, d=128, "
+                         "chunk 64, bf16")
+
+
 def bench_prefill_ckpt(steps, warmup, plain_ms):
     """Cost of exporting intermediate states inside the prefill: every 640 tokens (a hybrid
     cache block) and at every chunk boundary (every block-size multiple kept)."""
@@ -429,6 +458,8 @@ def main():
         if not args.no_ckpt:
             log("prefill with checkpoints ...")
             line["prefill_ckpt"] = bench_prefill_ckpt(args.steps, args.warmup, p["ms"])
+        log("prefill batch ...")
+        line["prefill_batch"] = bench_prefill_batch(args.steps, args.warmup)
         log("decode ...")
         line["decode"] = bench_decode(args.steps, args.warmup)
         log("fused decode ...")

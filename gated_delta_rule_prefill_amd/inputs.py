@@ -137,6 +137,26 @@ def prefill_config(seed: int = 0, T: int = 8192, H: int = 16, d: int = 128,
         qk_l2norm=False, chunk=chunk)
 
 
+def prefill_batch_config(seed: int = 0, n_seqs: int = 32, L: int = 2048, H: int = 16,
+                         d: int = 128, chunk: int = 64) -> PrefillInputs:
+    """A serving-style prefill batch: n_seqs sequences of L tokens (32 x 2048 = 65536 tokens),
+    H=16, d=128, chunk 64, drawn as the single-sequence workload (bf16 q/k/v, q and k unit rows,
+    fp32 gates logsigmoid(randn + 3), beta sigmoid(randn)), zero initial states."""
+    gen = _gen(seed)
+    T = n_seqs * L
+    q = torch.randn(T, H, d, generator=gen)
+    k = torch.randn(T, H, d, generator=gen)
+    v = torch.randn(T, H, d, generator=gen)
+    a = torch.randn(T, H, generator=gen)
+    b = torch.randn(T, H, generator=gen)
+    return PrefillInputs(
+        q=_unit_rows(q).to(BF16).contiguous(), k=_unit_rows(k).to(BF16).contiguous(),
+        v=v.to(BF16).contiguous(), g=gate_from_normal(a).contiguous(),
+        beta=beta_from_normal(b).contiguous(),
+        cu_seqlens=torch.arange(0, T + 1, L, dtype=torch.int32), scale=1.0 / d ** 0.5,
+        qk_l2norm=False, chunk=chunk)
+
+
 def decode_pool(seed: int, n_slots: int, H: int, dk: int, dv: int) -> torch.Tensor:
     """fp32 slot-indexed state pool [n_slots, H, dk, dv] ~ randn / sqrt(dk)."""
     gen = _gen(seed)

@@ -217,6 +217,17 @@ def test_prefill_config_full_size():
     _check(x, o, pool, o_ref, s_ref)
 
 
+def test_prefill_batch_32x2048_full():
+    """A serving-style batch at full size: 32 sequences x 2048 tokens, H=16, d=128, chunk 64,
+    bf16 (the per-(sequence, head) scan runs 8 value tiles per workgroup here). Every output
+    and final state against the oracle."""
+    say("case prefill batch 32 x 2048, H=16")
+    x = inputs.prefill_batch_config(0)
+    o, pool = run_prefill(x)
+    o_ref, s_ref = oracle_prefill(x)
+    _check(x, o, pool, o_ref, s_ref)
+
+
 def test_kda_varlen_with_conv_sampled_heads():
     """KDA-style varlen prefill at full size (8 sequences, 1k-8k tokens, H=32, d=128):
     conv1d + SiLU pre-pass, in-kernel L2 norm, per-key gate. Checked element by element on a
