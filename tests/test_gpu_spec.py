@@ -42,6 +42,7 @@ def run_spec(q, k, v, g, b, pool, table, acc, scale, l2=False):
     (torch.float32, 16, False, False, 4), (torch.float32, 64, True, True, 3),
     (torch.float32, 128, False, False, 16), (torch.bfloat16, 32, True, False, 2),
     (torch.bfloat16, 128, False, True, 4), (torch.bfloat16, 128, True, False, 5),
+    (torch.bfloat16, 128, True, True, 16),  # the largest LDS footprint the ABI accepts
 ])
 def test_spec_vs_oracle(dtype, d, perkey, l2, P):
     """8 requests; random distinct slot rows, random num_accepted; request 6 has
