@@ -61,6 +61,23 @@ def ev_time(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall
 
 
+def ev_time_reps(fn, steps, warmup):
+    """As ev_time, with an event pair around every call as well (recorded back to back on the
+    same stream, so the device never idles between calls). Returns (median ms per call,
+    mean ms per call over the whole bracket, per-call ms list)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return sorted(per)[steps // 2], ev[0].elapsed_time(ev[steps]) / steps, per
+
+
 def source_digest():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_delta_rule_prefill_amd", "csrc")
@@ -113,11 +130,12 @@ def bench_prefill(steps, warmup, ckpt_every=None):
             gdn.gdn_prefill_chunked(q, k, v, g, b, cu, x.chunk, pool, slots, scale=x.scale,
                                     o=o, workspace=ws)
 
-    ms, wall = ev_time(step, steps, warmup)
+    ms, ms_mean, per = ev_time_reps(step, steps, warmup)
     byts = traffic.prefill_bytes(T, H, d, d, 2, False, 1, False)
     flops = traffic.prefill_flops([T], H, d, d, x.chunk)
-    return dict(ms=ms, wall=wall, tokens=T, bytes=byts, flops=flops, H=H, d=d, ws_bytes=need,
-                n_ckpt=len(pos), ckpt_bytes=len(pos) * H * d * d * 4)
+    return dict(ms=ms, ms_mean=ms_mean, ms_min=min(per), ms_max=max(per), tokens=T, bytes=byts,
+                flops=flops, H=H, d=d, ws_bytes=need, n_ckpt=len(pos),
+                ckpt_bytes=len(pos) * H * d * d * 4)
 
 
 def bench_prefill_batch(steps, warmup):
@@ -435,6 +453,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": p["ms"],
+        "ms_per_step_mean": p["ms_mean"],
+        "timing": f"median of {args.steps} calls, each between its own HIP events",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
