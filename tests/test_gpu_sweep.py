@@ -1,0 +1,136 @@
+"""Seeded sweep of prefill configurations against the fp64 oracle, through the C ABI.
+
+Each case draws its own combination of element type, head dim, chunk size, gate kind, L2 norm,
+head count, ragged sequence lengths (empty and 1-token sequences included), initial states
+and slot map, and runs one of three entry points: the plain chunked prefill, the prefill with
+checkpoint exports, or the conv-fused prefill with conv histories. Outputs, final states,
+exported states and conv windows are compared with the oracle (the conv window, a copy, bit
+for bit). Bars: max|x - ref| / max|ref| <= 1e-4 (fp32 inputs) or 1e-2 (bf16 inputs).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_prefill_amd import gdn, inputs
+from gpu_util import BAR, DEV, say, to_dev
+from test_gpu_checkpoint import expected_stored, oracle_prefix_states
+from test_gpu_conv_prefill import extended, oracle_conv_prefill
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 48
+
+
+def draw(seed):
+    r = np.random.default_rng(1000 + seed)
+    dtype = [torch.float32, torch.bfloat16][r.integers(2)]
+    d = int(r.choice([16, 32, 64, 128]))
+    chunk = int(r.choice([16, 32, 64]))
+    perkey = bool(r.integers(2))
+    H = int(r.integers(1, 4))
+    n = int(r.integers(1, 7))
+    lengths = [int(x) for x in r.choice([0, 1, 2, 3, 5, 17, 40, 64, 65, 100, 130, 200], size=n)]
+    if sum(lengths) == 0:
+        lengths[0] = 33
+    mode = ["plain", "ckpt", "conv"][r.integers(3)]
+    l2 = bool(r.integers(2))
+    # The convolution's outputs are not unit vectors: without the in-kernel L2 norm,
+    # beta |k|^2 reaches 14-48 on these inputs. The delta-rule update (I - beta k k^T) is then
+    # far from contractive and the state grows without bound (|S| ~ 1e52 in the oracle
+    # itself), so no relative bar applies. The conv mode always normalises, as the KDA layer
+    # does.
+    if mode == "conv":
+        l2 = True
+    return dict(dtype=dtype, d=d, chunk=chunk, perkey=perkey, H=H, lengths=lengths, mode=mode,
+                l2=l2, width=int(r.integers(2, 5)), rng=r)
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_sweep_vs_oracle(seed):
+    c = draw(seed)
+    dtype, d, C, perkey, H, lengths, mode = (c[k] for k in ("dtype", "d", "chunk", "perkey",
+                                                            "H", "lengths", "mode"))
+    say(f"case sweep {seed}: {mode} {dtype} d={d} C={C} perkey={perkey} H={H} l2={c['l2']} "
+        f"W={c['width']} lens={lengths}")
+    r = c["rng"]
+    n = len(lengths)
+    n_slots = n + 4 + (sum(len(_ck(L, C)) for L in lengths) if mode == "ckpt" else 0)
+    slot_of = [int(s) for s in r.permutation(n + 4)[:n]]
+    if n > 1:
+        slot_of[int(r.integers(n))] = -1             # one sequence without a slot
+    has = [int(x) for x in r.integers(0, 2, size=n)]
+    bar = BAR[dtype]
+    gen = torch.Generator().manual_seed(2000 + seed)
+    pool0 = torch.randn(n_slots, H, d, d, generator=gen) / d ** 0.5
+    init = torch.zeros(n, H, d, d)
+    for i, s in enumerate(slot_of):
+        if s >= 0 and has[i]:
+            init[i] = pool0[s]
+    slots = torch.tensor(slot_of, dtype=torch.int32)
+    hi = torch.tensor(has, dtype=torch.int32)
+
+    if mode == "conv":
+        x = inputs.conv_prefill(3000 + seed, lengths, H, d, width=c["width"], dtype=dtype,
+                                perkey=perkey)
+        x.qk_l2norm = c["l2"]
+        W = c["width"]
+        CH = 3 * H * d
+        cs0 = torch.randn(n_slots, CH, W - 1, generator=gen).to(dtype)
+        X, w, g, b, cu, pd, sd, hd = to_dev(x.x, x.conv_w, x.g, x.beta, x.cu_seqlens,
+                                            pool0.clone(), slots, hi)
+        cs = cs0.clone().to(DEV)
+        o = gdn.gdn_prefill_chunked_conv(X, w, g, b, cu, C, pd, sd, conv_state=cs, has_init=hd,
+                                         scale=x.scale, qk_l2norm=x.qk_l2norm)
+        torch.cuda.synchronize()
+        o, pool, cs = o.cpu(), pd.cpu(), cs.cpu()
+        hist_rows = [cs0[s].T if (s >= 0 and has[i]) else torch.zeros(W - 1, CH, dtype=dtype)
+                     for i, s in enumerate(slot_of)]
+        o_ref, s_ref = oracle_conv_prefill(x, hist_rows, init)
+        rows, ecu = extended(x, hist_rows)
+        for i, s in enumerate(slot_of):
+            if s >= 0:
+                last = rows[int(ecu[i + 1]) - (W - 1):int(ecu[i + 1])]
+                assert torch.equal(cs[s].to(torch.float64), last.T.contiguous()), (seed, i)
+    else:
+        x = inputs.random_prefill(3000 + seed, lengths, H=H, dk=d, dv=d, dtype=dtype,
+                                  perkey=perkey, chunk=C, prenorm=not c["l2"])
+        q, k, v, g, b, cu, pd, sd, hd = to_dev(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens,
+                                              pool0.clone(), slots, hi)
+        if mode == "ckpt":
+            spec, nxt = [], n + 4
+            for L in lengths:
+                e = [(p, nxt + j) for j, p in enumerate(_ck(L, C))]
+                nxt += len(e)
+                spec.append(e)
+            cu_ck = np.concatenate([[0], np.cumsum([len(e) for e in spec])]).astype(np.int32)
+            pos = [p for e in spec for p, _ in e]
+            sl = [s for e in spec for _, s in e]
+            ck = [torch.tensor(z, dtype=torch.int32, device=DEV) for z in (cu_ck, pos, sl)]
+            o = gdn.gdn_prefill_chunked_ckpt(q, k, v, g, b, cu, C, pd, sd, *ck, has_init=hd,
+                                             scale=x.scale, qk_l2norm=x.qk_l2norm)
+        else:
+            o = gdn.gdn_prefill_chunked(q, k, v, g, b, cu, C, pd, sd, has_init=hd,
+                                        scale=x.scale, qk_l2norm=x.qk_l2norm)
+        torch.cuda.synchronize()
+        o, pool = o.cpu(), pd.cpu()
+        o_ref, s_ref = oracle.recurrence(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens,
+                                         scale=x.scale, l2norm=x.qk_l2norm, init_states=init)
+        if mode == "ckpt":
+            for i, e in enumerate(spec):
+                stored = expected_stored(e, lengths[i], C)
+                want = [p for (p, _), st in zip(e, stored) if st]
+                ref = oracle_prefix_states(x, i, want, init[i]) if want else {}
+                for (p, s), st in zip(e, stored):
+                    if st:
+                        assert oracle.rel_err(pool[s], ref[p]) <= bar, (seed, i, p)
+    if o.numel():
+        assert oracle.rel_err(o, o_ref) <= bar, seed
+    for i, s in enumerate(slot_of):
+        if s >= 0:
+            assert oracle.rel_err(pool[s], s_ref[i]) <= bar, (seed, i)
+
+
+def _ck(L, C):
+    """Checkpoint offsets for a sequence of L tokens: every chunk boundary, then the end."""
+    return [p for p in range(C, L, C)] + ([L] if L > 0 else [])
