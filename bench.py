@@ -337,6 +337,40 @@ def bench_kda(steps=5, warmup=3, rounds=3):
                          "fused into the prefill, per-key gates, in-kernel L2 norm")
 
 
+def bench_gdn_conv(steps=10, warmup=5, rounds=3):
+    """GDN (scalar gate) prefill with its short convolution, T=8192, H=16, d=128, width 4,
+    bf16, in-kernel L2 norm: the conv-fused prefill against gdn_conv1d_silu followed by the
+    prefill, timed in alternating rounds (median round reported)."""
+    T, H, d = 8192, 16, 128
+    x = inputs.conv_prefill(0, [T], H, d, width=4, perkey=False)
+    X, w, g, b, cu = (t.to(DEV) for t in (x.x, x.conv_w, x.g, x.beta, x.cu_seqlens))
+    qkv = torch.empty((3, T, H * d), dtype=torch.bfloat16, device=DEV)
+    pool = torch.zeros((1, H, d, d), device=DEV)
+    slots = torch.zeros(1, dtype=torch.int32, device=DEV)
+    need = gdn.gdn_prefill_workspace_bytes(H, d, d, torch.bfloat16, False, 1, T, 64)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    o = torch.empty((T, H, d), dtype=torch.bfloat16, device=DEV)
+
+    def two_launch():
+        gdn.gdn_conv1d_silu(X, w, cu, planes=3, y=qkv)
+        q, k, v = (qkv[i].view(T, H, d) for i in range(3))
+        gdn.gdn_prefill_chunked(q, k, v, g, b, cu, 64, pool, slots, scale=x.scale,
+                                qk_l2norm=True, o=o, workspace=ws)
+
+    def fused():
+        gdn.gdn_prefill_chunked_conv(X, w, g, b, cu, 64, pool, slots, scale=x.scale,
+                                     qk_l2norm=True, o=o, workspace=ws)
+
+    f_ms, t_ms = [], []
+    for r in range(rounds):
+        f_ms.append(ev_time(fused, steps, warmup if r == 0 else 1)[0])
+        t_ms.append(ev_time(two_launch, steps, warmup if r == 0 else 1)[0])
+    ms, ms_two = sorted(f_ms)[rounds // 2], sorted(t_ms)[rounds // 2]
+    return dict(ms=ms, tokens_per_s=T / (ms * 1e-3), ms_conv_then_prefill=ms_two,
+                workload="GDN prefill with conv + SiLU fused into it, 1 sequence, T=8192, H=16, "
+                         "d=128, conv width 4, bf16, scalar gate, in-kernel L2 norm")
+
+
 # ------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(budget_s=20.0):
     """The fp64 oracle (unmodified) on the host over the prefill workload: all 16 heads of
@@ -490,6 +524,8 @@ def main():
         line["deltalog"] = bench_deltalog()
         log("kda deltalog ...")
         line["deltalog_kda"] = bench_deltalog(M=4, perkey=True)
+        log("gdn with conv ...")
+        line["gdn_conv_prefill"] = bench_gdn_conv()
         log("kda ...")
         line["kda_prefill"] = bench_kda()
     if not args.no_cpu:
