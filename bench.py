@@ -2,22 +2,32 @@
 
 Headline (`value`): chunked-prefill throughput in tokens/s on the GDN prefill workload —
 one sequence, T=8192, H=16, d_k=d_v=128, chunk 64, bf16 q/k/v, fp32 gates and state. One
-step = one gdn_prefill_chunked call over that batch (chunk table + prep + sequential scan).
-Inputs are resident in HBM before timing; three input sets rotate so the 256 MB MALL does
-not serve them from one step to the next.
+step = one gdn_prefill_chunked call over that batch (prep + sequential scan). Inputs are
+resident in HBM before timing; three input sets rotate so the 256 MB MALL does not serve
+them from one step to the next. `ms_per_step` is the median of the timed calls, each between
+its own HIP events.
 
 Also reported on the same JSON line (secondary workloads of the same metric):
-  decode:   dense decode step, B=128, H=32, d=128, 256-slot fp32 pool, random slot map;
-            four layer pools rotate per step so the state stream comes from HBM
-  deltalog: DeltaLog vs dense decode, B=512, H=32, d=128 (1 GiB fp32 state), M=8, cycle
-            average over whole merge cycles
-  kda:      KDA-style varlen prefill, 8 sequences of 1k-8k tokens, H=32, d=128, conv1d+SiLU
-            pre-pass, in-kernel L2 norm, per-key gates
-  roofline: the prefill pass against HBM bandwidth (algorithmic bytes / event-timed
-            duration of the call); counters-based traffic when a matching profile exists
-  cpu_baseline: the fp64 oracle on the host cores over the same prefill workload
+  prefill_ckpt:     the headline call exporting the state every 640 tokens / every chunk
+  prefill_batch:    32 sequences x 2048 tokens, H=16, d=128 (a serving-style batch)
+  decode:           dense decode step, B=128, H=32, d=128, 256-slot fp32 pool, random slot
+                    map; four layer pools rotate per step so the state stream comes from HBM
+  decode_fused_kda: the fused KDA decode step (conv update, in-kernel gates, L2 norm), B=128
+  spec_decode:      the spec-decode verify step, B=128 x 4 positions
+  deltalog:         DeltaLog vs dense decode, B=512, H=32, d=128 (1 GiB fp32 state), M=8,
+                    cycle average over whole merge cycles; deltalog_kda: per-key decay, M=4
+  gdn_conv_prefill: the headline shape with the short convolution fused into the prefill,
+                    against the conv launch followed by the prefill
+  kda_prefill:      KDA-style varlen prefill, 8 sequences of 1k-8k tokens, H=32, d=128,
+                    convolution fused into the prefill, in-kernel L2 norm, per-key gates
+  roofline:         the prefill pass against HBM bandwidth (algorithmic bytes / event-timed
+                    duration of the call); counters-based traffic when a matching profile
+                    exists; a 1 GiB device copy measured in the same run
+  cpu_baseline:     the fp64 oracle on the host cores over the same prefill workload (and
+                    on one thread)
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-extras] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 50] [--no-extras] [--no-ckpt]
+                       [--no-cpu]
        python bench.py --calibrate-copy --steps 3     (counter calibration only)
 """
 import argparse
