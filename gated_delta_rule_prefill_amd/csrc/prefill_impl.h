@@ -161,7 +161,7 @@ struct Frag {
 //   P2  16x16 leaf inverses of I + A (forward substitution, one lane per column), V^T
 //   P3  2x2 block merges on fp32 MFMA (16 -> 32 -> 64), in place over A
 //   P4  -W and U on MFMA, written to the workspace
-template <typename T, int DK, int DV, int C, bool PERKEY>
+template <typename T, int DK, int DV, int C, bool PERKEY, bool CONV = false>
 struct PrepSmem {
     using F = PfCfg<T, DK, DV, C>;
     // live for the whole kernel
@@ -187,6 +187,9 @@ struct PrepSmem {
             alignas(16) T vt[PERKEY ? DV : 1][F::LDC];  // per-key gate: (diag(beta) V)^T
         } b;
     } u;
+    // per-key conv: the weights, kept for V's convolution after P0 (the other members keep
+    // their offsets)
+    alignas(16) float cw[PERKEY && CONV ? 3 * DK * 4 : 1];
 };
 
 template <bool PERKEY, int DK, int C>
@@ -251,7 +254,7 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
     constexpr int NK = DKP / KB;                       // row fragments over d_k
     constexpr int NV = ((DV + KB - 1) / KB);           // row fragments over d_v
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    auto& sm = *reinterpret_cast<PrepSmem<T, DK, DV, C, PERKEY>*>(smem_raw);
+    auto& sm = *reinterpret_cast<PrepSmem<T, DK, DV, C, PERKEY, CONV>*>(smem_raw);
     T (*const vt)[F::LDC] = PERKEY ? sm.u.b.vt : sm.u.b.va;
 
     const int H = a.H;
@@ -276,7 +279,8 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
     float wreg[NWL];
     frag xh[CONV ? 2 * NK + NV : 1];
     static_assert(!CONV || DK == DV, "the fused convolution assumes d_k == d_v");
-    static_assert(!CONV || F::LDC * sizeof(T) >= 48, "conv weights do not fit the K_in^T area");
+    static_assert(!CONV || PERKEY || F::LDC * sizeof(T) >= 48,
+                  "conv weights do not fit the K_in^T area");
     if constexpr (CONV) {
         const int W = a.conv_width;
         // tap d (token t - d) of channel ch of plane p at [(p DK + ch) 4 + d]; taps >= W are 0
@@ -373,22 +377,17 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
         gsc = (lane < loc.len && lane < C) ? a.g[(size_t)(loc.tok0 + lane) * H + h] : 0.f;
     if (tid < C && tid < loc.len) bval = a.beta[(size_t)(loc.tok0 + tid) * H + h];
 
-    if constexpr (CONV) {
-        float* wl = reinterpret_cast<float*>(&sm.kint[0][0]);  // K_in^T is written after #1
-#pragma unroll
-        for (int k = 0; k < NWL; k++) {
-            const int i = tid + k * PF_THREADS;
-            if (i < 3 * DK * 4) wl[i] = wreg[k];
-        }
-        lds_barrier();  // #0: conv weights in LDS
-#pragma unroll
-        for (int f = 0; f < 2 * NK + NV; f++) {
-            if (!own) break;
+    // Conv weights: scalar gate in the K_in^T area (written only after barrier #1); per-key
+    // gate in an area of their own, because V's convolution there runs after P0 (see below).
+    float* const wl = PERKEY ? &sm.cw[0] : reinterpret_cast<float*>(&sm.kint[0][0]);
+    // convolution + SiLU of fragment f (q: f < NK, k: f < 2 NK, v: the rest), in place;
+    // every call sits in an unrolled loop, so f is a constant there
+    auto conv_frag = [&](const int f) {
             const int p = f < NK ? 0 : (f < 2 * NK ? 1 : 2);
             const int kb = f - p * NK;
             const int c0 = kb * KB + g4 * KPL;
             frag& xf = p == 0 ? qf[kb] : (p == 1 ? kf[kb] : vf[kb]);
-            if (c0 >= DK) continue;  // zero padding columns stay zero
+            if (c0 >= DK) return;  // zero padding columns stay zero
             // x at t - d (d = 1..3) arrives by rotating the row group by d: lane s sends to
             // lane (s + d) mod 16, its own row if that lane follows it, else (wrapping
             // around, s >= 16 - d) the halo row that lane needs
@@ -415,6 +414,21 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
                 else out[e] = y;
             }
             xf = rvalid ? out : MM::zero();  // rows past the chunk stay zero
+    };
+    if constexpr (CONV) {
+#pragma unroll
+        for (int k = 0; k < NWL; k++) {
+            const int i = tid + k * PF_THREADS;
+            if (i < 3 * DK * 4) wl[i] = wreg[k];
+        }
+        lds_barrier();  // #0: conv weights in LDS
+        // q and k here (the L2 norm and the key tiles need them); per-key: v later, in time
+        // the waves would otherwise spend waiting at barriers #2 and #3
+#pragma unroll
+        for (int f = 0; f < 2 * NK + NV; f++) {
+            if (!own) break;
+            if (PERKEY && f >= 2 * NK) break;
+            conv_frag(f);
         }
     }
 
@@ -636,6 +650,12 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
             }
         }
     }
+    if constexpr (CONV && PERKEY) {  // wave 0 has the fewest A/M tiles: its V conv here
+        if (w == 0 && own) {
+#pragma unroll
+            for (int f = 2 * NK; f < 2 * NK + NV; f++) conv_frag(f);
+        }
+    }
     lds_barrier();  // #2: keys and gates are dead from here on
     if (own) {
 #pragma unroll
@@ -677,6 +697,12 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
                 sm.u.b.ar[b0 + r][b0 + col] = x[r];
                 sm.u.b.rs[b0 + r][b0 + col] = from_f32<T>(x[r]);
             }
+        }
+    }
+    if constexpr (CONV && PERKEY) {  // the other waves' V conv while wave 0 inverts leaves
+        if (w != 0 && own) {
+#pragma unroll
+            for (int f = 2 * NK; f < 2 * NK + NV; f++) conv_frag(f);
         }
     }
     // (diag(beta) V)^T: lane (g4, n) gets V[16w + 4 g4 + e][16 vb + n], plus zero padding
@@ -1197,8 +1223,9 @@ void scan_launch(const PrefillArgs& a, int nvb, unsigned grid, hipStream_t s) {
 
 template <typename T, int D, int C, bool PERKEY, bool CONV>
 hipError_t prefill_prep_cfg(const PrefillArgs& a, hipStream_t s) {
-    const size_t smem = sizeof(PrepSmem<T, D, D, C, PERKEY>);
-    static_assert(sizeof(PrepSmem<T, D, D, C, PERKEY>) <= 160 * 1024, "prep LDS over 160 KiB");
+    const size_t smem = sizeof(PrepSmem<T, D, D, C, PERKEY, CONV>);
+    static_assert(sizeof(PrepSmem<T, D, D, C, PERKEY, CONV>) <= 160 * 1024,
+                  "prep LDS over 160 KiB");
     auto prep = prefill_prep_kernel<T, D, D, C, PERKEY, CONV>;
     // dynamic LDS above 64 KiB must be allowed explicitly (idempotent, no library state);
     // done before the first launch so a refusal launches nothing
