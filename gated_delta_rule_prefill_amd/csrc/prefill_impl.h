@@ -935,8 +935,11 @@ __device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROL
             }
         } else {
             const T* mm = reinterpret_cast<const T*>(a.ws.mmat) + u * C * CP;
+            // M is lower triangular: fragments starting right of token block mb hold zeros
+            // and are neither loaded nor multiplied (mb is uniform across the wave)
 #pragma unroll
-            for (int kt = 0; kt < O::NK2; kt++) op.am[kt] = MM::load(Frag<T>::ptr(mm, mb, kt, CP, lane));
+            for (int kt = 0; kt < O::NK2; kt++)
+                if (kt * F::KB < 16 * (mb + 1)) op.am[kt] = MM::load(Frag<T>::ptr(mm, mb, kt, CP, lane));
         }
     }
 }
@@ -1148,12 +1151,14 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
             sched_fence();
             if constexpr (!E) {
 #pragma unroll
-                for (int kt = 0; kt < O::NK2; kt++)
+                for (int kt = 0; kt < O::NK2; kt++) {
+                    if (kt * KB >= 16 * (mb + 1)) continue;  // zero fragment of M
 #pragma unroll
                     for (int v = 0; v < NVB; v++) {
                         auto fb = MM::load(&et[16 * v + r16][kt * KB + kq]);
                         acc[v] = MM::mma(cur.am[kt], fb, acc[v]);  // + M E
                     }
+                }
                 // the accumulator holds 4 tokens of one column per lane; a row-major pass
                 // through LDS lets every lane store 4 adjacent columns of one token at once
                 const int tok0 = t_begin + (c - c_begin) * C;
