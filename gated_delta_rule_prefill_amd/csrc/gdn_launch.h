@@ -14,7 +14,9 @@ namespace gdn {
 //   qin   [C][DKP]   e   Q_in = s * Q * e^{G}                      row-major
 // (DKP = d_k rounded up to the MFMA contraction step, zero-padded)
 //   kgt   [d_k][CP]  e   K_g^T, K_g = K * e^{G_C - G}              (key-channel major)
-//   mmat  [C][CP]    e   M (lower triangular incl. diagonal)        row-major
+//   mmat  [C][CP]    e   M (lower triangular incl. diagonal)        row-major; the MFMA
+//                        fragments (K-step columns) that start right of a row's 16-token
+//                        block are all zero, never written and never read
 //   ut    [d_v][C]   e   U (local residuals), 16-column tiles in MFMA accumulator order
 //   decay [d_k]      f32 e^{G_C} per key channel
 struct PrefillWs {

@@ -641,10 +641,11 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
                 Frag<T>::template store_run<4>(mmat, i, jb * 16 + g4 * 4, CP, mrow);
             }
         }
-        // zero the upper tiles and the padding columns of M
+        // zero the upper tiles and the padding columns of M, where the scan reads them: it
+        // skips the fragments (KB columns) that start right of a row's token block
         for (int idx = tid; idx < C * (CP / 4); idx += PF_THREADS) {
             const int i = idx / (CP / 4), j0 = (idx % (CP / 4)) * 4;
-            if (j0 / 16 > i / 16 || j0 >= C) {
+            if ((j0 / 16 > i / 16 || j0 >= C) && (j0 / KB) * KB < 16 * (i / 16 + 1)) {
                 float z[4] = {0.f, 0.f, 0.f, 0.f};
                 Frag<T>::template store_run<4>(mmat, i, j0, CP, z);
             }
@@ -935,8 +936,9 @@ __device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROL
             }
         } else {
             const T* mm = reinterpret_cast<const T*>(a.ws.mmat) + u * C * CP;
-            // M is lower triangular: fragments starting right of token block mb hold zeros
-            // and are neither loaded nor multiplied (mb is uniform across the wave)
+            // M is lower triangular: the fragments starting right of token block mb would
+            // hold only zeros; the prep leaves them unwritten and they are neither loaded nor
+            // multiplied here (mb is uniform across the wave)
 #pragma unroll
             for (int kt = 0; kt < O::NK2; kt++)
                 if (kt * F::KB < 16 * (mb + 1)) op.am[kt] = MM::load(Frag<T>::ptr(mm, mb, kt, CP, lane));
