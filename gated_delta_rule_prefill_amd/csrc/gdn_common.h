@@ -157,6 +157,24 @@ __device__ __forceinline__ void store4<bf16>(bf16* p, const float in[4]) {
     *reinterpret_cast<bf16x4*>(p) = v;
 }
 
+// store4 with the non-temporal hint, for outputs nothing reads back soon: their lines do
+// not linger dirty in the caches, where the next kernel would pay for their write-back
+template <typename T>
+__device__ __forceinline__ void store4_nt(T* p, const float in[4]);
+template <>
+__device__ __forceinline__ void store4_nt<float>(float* p, const float in[4]) {
+    f32x4 v = {in[0], in[1], in[2], in[3]};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+template <>
+__device__ __forceinline__ void store4_nt<bf16>(bf16* p, const float in[4]) {
+    bf16x4 v;
+    v[0] = (bf16)in[0]; v[1] = (bf16)in[1]; v[2] = (bf16)in[2]; v[3] = (bf16)in[3];
+    uint64_t bits;
+    __builtin_memcpy(&bits, &v, 8);
+    __builtin_nontemporal_store(bits, reinterpret_cast<uint64_t*>(p));
+}
+
 // 8 consecutive elements <-> fp32 (one 16-byte access for bf16, two for fp32)
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float out[8]);
