@@ -159,9 +159,14 @@ __global__ __launch_bounds__(256) void conv_state_update_kernel(PrefillArgs a) {
         // only the W-1 entries that are stored: for j >= W-1 the row would be s1 or later,
         // past the sequence (and past x for the last one)
         const int r = s1 - (W - 1) + j;
+        // (rows outside [0, total_tokens), possible only with cu_seqlens that break the
+        // contract, read as zero; the old-history index is selected, never computed)
+        const int oi = j + len;
         if (j >= W - 1) nw[j] = from_f32<T>(0.f);
-        else if (r >= s0) nw[j] = x[(size_t)r * XC + ch];
-        else nw[j] = j + len < W - 1 ? old[j + len] : from_f32<T>(0.f);
+        else if (r >= s0) nw[j] = (r >= 0 && r < a.total_tokens) ? x[(size_t)r * XC + ch]
+                                                                 : from_f32<T>(0.f);
+        else nw[j] = oi == 0 ? old[0] : oi == 1 ? old[1] : (oi == 2 && W - 1 > 2) ? old[2]
+                                                                             : from_f32<T>(0.f);
     }
 #pragma unroll
     for (int j = 0; j < 3; j++)

@@ -276,6 +276,10 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
         c = (jj / H) * 8 + xcd;
         h = jj - (jj / H) * H;
     }
+    // The grid may exceed the chunk bound the workspace was sized for (rounded up to 8, or
+    // cu_seqlens that break the header's contract and describe more chunks): such a
+    // workgroup has no workspace unit and stores nothing.
+    if (c >= a.ws.max_chunks) return;
     const ChunkLoc loc =
         a.n_seqs <= SEQ_INLINE_MAX
             ? locate_chunk_inline(c, a.cu_seqlens, a.n_seqs, C, a.total_tokens)
@@ -315,7 +319,7 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
         const int hrow = loc.tok0 + w * 16 + r16 - 16;  // halo row of lanes 13..15
         const bool hlane = own && r16 >= 13;
         // a row past the chunk's last token feeds only padding rows: never loaded
-        const bool hin = hlane && hrow >= ss && hrow < loc.tok0 + loc.len;
+        const bool hin = hlane && hrow >= ss && hrow >= 0 && hrow < loc.tok0 + loc.len;
         const T* xo = xb + (size_t)(loc.tok0 + row) * XC + (size_t)h * DK;
         const T* xhp = xb + (size_t)(hin ? hrow : 0) * XC + (size_t)h * DK;
 #pragma unroll
@@ -596,51 +600,119 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
         T* mmat = reinterpret_cast<T*>(a.ws.mmat) + u * C * CP;
         if (own) {
             const int ib = w, ref = ib * 16, irow = row;
+            // Per-key gate ([LA-Infra] 附1, parts 2-3): the reference point n = ref splits
+            // e^{G_i - G_j} = e^{G_i - G_n} e^{G_n - G_j}. For an off-diagonal block (j < n
+            // <= i) both exponents are <= 0, so a factor that underflows means a true product
+            // below the fp32 range. In the diagonal block (n <= j) the key-side exponent
+            // G_n - G_j is >= 0, bounded by the block's own cumulative decay; the split is
+            // kept only while that span stays within DIAG_SPAN (both factors then lie well
+            // inside the normal fp32 / bf16 range, so the split is exact to rounding).
+            // Otherwise the wave computes the diagonal block directly, entry by entry, with
+            // the mask applied before the exponential (e^{G_i - G_j} <= 1 for every kept
+            // entry), as the page's 对角子块 computation does.
+            f32x4 dK = zero4(), dQ = zero4();
+            bool direct = false;
+            if constexpr (PERKEY) {
+                constexpr float DIAG_SPAN = 60.f;
+                const int last = min(ref + 15, C - 1);
+                bool wide = false;
+                for (int ch = lane; ch < DK; ch += WAVE)  // g <= 0: the span is G_n - G_last
+                    wide |= !(sm.u.a.gs[ref][ch] - sm.u.a.gs[last][ch] <= DIAG_SPAN);
+                direct = __ballot(wide) != 0;  // uniform across the wave
+                if (direct) {
+                    // lane (g4, r16): row i = irow, its channels kb KB + g4 KPL + e; for each
+                    // column j of the block, the partial sums over those channels are
+                    // completed across the four lane groups, and the lane whose accumulator
+                    // slot holds (j, i) (g4 = (j - ref) / 4) keeps them
+#pragma unroll 1
+                    for (int jj = 0; jj < 16; jj++) {
+                        const int j = ref + jj;
+                        float sk = 0.f, sq = 0.f;
+#pragma unroll
+                        for (int kb = 0; kb < NK; kb++) {
+                            const frag kj =
+                                MM::load(&sm.u.a.ks[((ib * NK + kb) * 64 + jj + 16 * g4) * KPL]);
+#pragma unroll
+                            for (int e = 0; e < KPL; e++) {
+                                const int ch = kb * KB + g4 * KPL + e;
+                                if (ch >= DK) continue;  // zero padding channels
+                                float xk, xq, xj;
+                                if constexpr (KPL == 1) {
+                                    xk = to_f32(kf[kb]); xq = to_f32(qf[kb]); xj = to_f32(kj);
+                                } else {
+                                    xk = to_f32(kf[kb][e]); xq = to_f32(qf[kb][e]); xj = to_f32(kj[e]);
+                                }
+                                // masked before the exponential: j > i contributes nothing
+                                const float t = j <= irow
+                                    ? xj * __expf(sm.u.a.gs[irow][ch] - sm.u.a.gs[j][ch]) : 0.f;
+                                sk = fmaf(xk, t, sk);
+                                sq = fmaf(xq, t, sq);
+                            }
+                        }
+                        sk += __shfl_xor(sk, 16, WAVE);
+                        sk += __shfl_xor(sk, 32, WAVE);
+                        sq += __shfl_xor(sq, 16, WAVE);
+                        sq += __shfl_xor(sq, 32, WAVE);
+#pragma unroll
+                        for (int e = 0; e < 4; e++)
+                            if (jj == 4 * g4 + e) {
+                                dK[e] = sk;
+                                dQ[e] = sq;
+                            }
+                    }
+                }
+                // the row-side operands k_i e^{G_i - G_n}, q_i e^{G_i - G_n} do not depend on
+                // the column block: formed once, in place (the raw rows are dead from here on)
+#pragma unroll
+                for (int kb = 0; kb < NK; kb++) {
+#pragma unroll
+                    for (int e = 0; e < KPL; e++) {
+                        const int ch = kb * KB + g4 * KPL + e;
+                        const float fi =
+                            ch < DK ? __expf(sm.u.a.gs[irow][ch] - sm.u.a.gs[ref][ch]) : 0.f;
+                        if constexpr (KPL == 1) {
+                            kf[kb] = from_f32<T>(to_f32(kf[kb]) * fi);
+                            qf[kb] = from_f32<T>(to_f32(qf[kb]) * fi);
+                        } else {
+                            kf[kb][e] = from_f32<T>(to_f32(kf[kb][e]) * fi);
+                            qf[kb][e] = from_f32<T>(to_f32(qf[kb][e]) * fi);
+                        }
+                    }
+                }
+            }
 #pragma unroll
             for (int jb = 0; jb < NB; jb++) {
                 if (jb > ib) continue;
                 f32x4 accK = zero4(), accQ = zero4();
                 const int jrow = jb * 16 + r16;
+                if (PERKEY && direct && jb == ib) {
+                    accK = dK;
+                    accQ = dQ;
+                } else {
 #pragma unroll
-                for (int kb = 0; kb < NK; kb++) {
-                    const frag ka = MM::load(&sm.u.a.ks[((jb * NK + kb) * 64 + lane) * KPL]);
-                    frag fa, fbk, fbq;
-                    if constexpr (PERKEY) {
+                    for (int kb = 0; kb < NK; kb++) {
+                        const frag ka = MM::load(&sm.u.a.ks[((jb * NK + kb) * 64 + lane) * KPL]);
+                        frag fa;
+                        if constexpr (PERKEY) {
 #pragma unroll
-                        for (int e = 0; e < KPL; e++) {
-                            const int ch = kb * KB + g4 * KPL + e;
-                            float aj = 0.f, bk = 0.f, bq = 0.f;
-                            if (ch < DK) {  // padded channels contribute zero
-                                const float gr = sm.u.a.gs[ref][ch];
-                                const float fj = __expf(gr - sm.u.a.gs[jrow][ch]);
-                                const float fi = __expf(sm.u.a.gs[irow][ch] - gr);
-                                if constexpr (KPL == 1) {
-                                    aj = to_f32(ka) * fj;
-                                    bk = to_f32(kf[kb]) * fi;
-                                    bq = to_f32(qf[kb]) * fi;
-                                } else {
-                                    aj = to_f32(ka[e]) * fj;
-                                    bk = to_f32(kf[kb][e]) * fi;
-                                    bq = to_f32(qf[kb][e]) * fi;
+                            for (int e = 0; e < KPL; e++) {
+                                const int ch = kb * KB + g4 * KPL + e;
+                                float aj = 0.f;
+                                if (ch < DK) {  // padded channels contribute zero
+                                    const float fj =
+                                        __expf(sm.u.a.gs[ref][ch] - sm.u.a.gs[jrow][ch]);
+                                    if constexpr (KPL == 1) aj = to_f32(ka) * fj;
+                                    else aj = to_f32(ka[e]) * fj;
                                 }
+                                if constexpr (KPL == 1) fa = from_f32<T>(aj);
+                                else fa[e] = from_f32<T>(aj);
                             }
-                            if constexpr (KPL == 1) {
-                                fa = from_f32<T>(aj);
-                                fbk = from_f32<T>(bk);
-                                fbq = from_f32<T>(bq);
-                            } else {
-                                fa[e] = from_f32<T>(aj);
-                                fbk[e] = from_f32<T>(bk);
-                                fbq[e] = from_f32<T>(bq);
-                            }
+                        } else {
+                            fa = ka;
                         }
-                    } else {
-                        fa = ka;
-                        fbk = kf[kb];
-                        fbq = qf[kb];
+                        accK = MM::mma(fa, kf[kb], accK);
+                        accQ = MM::mma(fa, qf[kb], accQ);
                     }
-                    accK = MM::mma(fa, fbk, accK);
-                    accQ = MM::mma(fa, fbq, accQ);
                 }
                 // lane holds D[j = jb*16 + 4*g4 + e][i = ib*16 + r16]
                 const int i = irow;
@@ -1202,9 +1274,11 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
                 for (int v = 0; v < NVB; v++) {
                     float ov[4];
                     load4<T>(&ot[mb][v][orow][oc], ov);
-                    // tokens past the sequence end go to a scratch area instead of a branch
-                    T* dst = i < len ? out + ((size_t)(tok0 + i) * H + h) * DV + vcol0 + 16 * v + oc
-                                     : dump;
+                    // tokens past the sequence end (or, with cu_seqlens that break the
+                    // contract, before token 0) go to a scratch area instead of a branch
+                    T* dst = i < len && tok0 + i >= 0
+                                 ? out + ((size_t)(tok0 + i) * H + h) * DV + vcol0 + 16 * v + oc
+                                 : dump;
                     if constexpr (NT) store4_nt<T>(dst, ov);
                     else store4<T>(dst, ov);
                 }

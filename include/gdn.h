@@ -29,7 +29,11 @@
  *     index, like a block table ([Handbook] "投机解码与 PD 分离"; [LA-Infra] "推测解码").
  *   - q/k/v/o element type is gdn_dims_t.dtype (fp32 or bf16); the forget gate is passed
  *     as its logarithm g = log(alpha) <= 0 (fp32; [LA-Infra] "完整计算顺序" uses the log gate
- *     g_i = ln alpha_i), the write gate beta in [0, 1] (fp32). The state is always fp32
+ *     g_i = ln alpha_i), the write gate beta in [0, 1] (fp32). Any finite g <= 0 is
+ *     accepted, per token and (per-key gate) per channel, however strong the cumulative
+ *     decay within a chunk: exponentials are only ever formed of non-positive sums, or of
+ *     bounded ones where their products stay exact (-inf and NaN are not accepted; the host
+ *     does not read g, so they are not rejected either). The state is always fp32
  *     ([Handbook] "练习" 2: rounding would accumulate step after step).
  *   - Supported head dims: d_k == d_v in {16, 32, 64, 128}. Chunk sizes: 16, 32, 64.
  *   - Ownership: the caller allocates and frees all memory, including workspaces sized by
@@ -106,7 +110,8 @@ int gdn_prefill_workspace_bytes(const gdn_dims_t* dims, int32_t n_seqs, int32_t 
  * sequence's tokens, using the chunk-wise rewrite of [LA-Infra] "Prefill中的Chunk微观并行"
  * (sub-sections 计算 Δchunk / 计算 Transitionchunk / 块内输出 / 完整计算顺序): in-chunk
  * cumulative log gate, A and M from C x C products (per-key gates: 16 x 16 sub-blocks with a
- * reference point, [LA-Infra] "附1. chunk内 A和M 的计算"), R = (I + A)^{-1} by a blocked
+ * reference point, diagonal sub-blocks computed directly when their decay is too strong for
+ * the split, [LA-Infra] "附1. chunk内 A和M 的计算"), R = (I + A)^{-1} by a blocked
  * triangular solve, U = R diag(beta) V, W = R diag(beta) K_in, then the sequential pass over
  * chunks E = U - W S, O = Q_in S + M E, S <- Diag(e^{G_C}) S + K_g^T E. Chunks restart at
  * every sequence boundary; the last chunk of a sequence may be short. Splitting a sequence

@@ -1,0 +1,165 @@
+"""CPU model of the chunked prefill's work mapping: which workspace unit and which token rows
+each prep and scan workgroup touches, checked for every workgroup of the grid.
+
+The prep grid covers the chunk bound rounded up to 8 (heads of one chunk on one XCD, since
+workgroups are dealt round-robin over the 8 XCDs); the scan runs one chain per
+(sequence, head). The model restates the index arithmetic of the kernels and checks that
+  - with cu_seqlens as the header requires (cu[0] = 0, non-decreasing, cu[n] = T), every
+    chunk of every sequence is prepared by exactly one workgroup into the unit the scan reads,
+    and the rows touched are the chunk's own;
+  - with cu_seqlens that break that contract (decreasing, negative, past T, describing more
+    chunks than the workspace bound), no workgroup reads or writes a workspace unit at or past
+    the bound, and no token row outside [0, T) is read or written.
+"""
+import random
+
+import pytest
+
+WAVE = 64
+
+
+def max_chunks(T, n, C):
+    return (T + n * (C - 1)) // C
+
+
+def seq_table(cu, n, C):
+    """Each wave's inline table (up to 64 sequences): exclusive / inclusive prefix sums of
+    ceil(max(0, len) / C)."""
+    excl, incl, run = [], [], 0
+    for s in range(n):
+        cnt = (max(0, cu[s + 1] - cu[s]) + C - 1) // C
+        excl.append(run)
+        run += cnt
+        incl.append(run)
+    return excl, incl
+
+
+def locate_chunk(c, cu, n, C, T):
+    excl, incl = seq_table(cu, n, C)
+    hits = [s for s in range(n) if excl[s] <= c < incl[s]]
+    if not hits:
+        return None
+    s = hits[0]
+    tok0 = cu[s] + (c - excl[s]) * C
+    ln = min(C, min(cu[s + 1], T) - tok0)
+    if tok0 < 0 or ln <= 0:
+        return None
+    return s, tok0, ln
+
+
+def prep_touch(cu, n, T, H, C, conv):
+    """For every prep workgroup: (unit, rows read, rows of the conv halo read)."""
+    mc = max_chunks(T, n, C)
+    grid = (mc if conv else (mc + 7) // 8 * 8) * H
+    out = []
+    for b in range(grid):
+        if conv:
+            c, h = b // H, b % H
+        else:
+            xcd, jj = b & 7, b >> 3
+            c, h = (jj // H) * 8 + xcd, jj % H
+        if c >= mc:
+            continue
+        loc = locate_chunk(c, cu, n, C, T)
+        if loc is None:
+            continue
+        s, tok0, ln = loc
+        rows = list(range(tok0, tok0 + ln))
+        halo = []
+        if conv:
+            ss = cu[s]
+            for w in range(C // 16):
+                for r16 in (13, 14, 15):
+                    hrow = tok0 + w * 16 + r16 - 16
+                    if hrow >= ss and hrow >= 0 and hrow < tok0 + ln:
+                        halo.append(hrow)
+        out.append((c * H + h, (c, h), rows, halo))
+    return out
+
+
+def scan_touch(cu, n, T, H, C):
+    """For every (sequence, head) chain: units read and output rows written."""
+    mc = max_chunks(T, n, C)
+    excl, incl = seq_table(cu, n, C)
+    out = []
+    for s in range(n):
+        c_end = min(incl[s], mc)
+        t_begin, t_end = cu[s], min(cu[s + 1], T)
+        for h in range(H):
+            units, rows = [], []
+            for c in range(excl[s], c_end):
+                units.append(c * H + h)
+                tok0 = t_begin + (c - excl[s]) * C
+                ln = min(C, t_end - tok0)
+                rows += [tok0 + i for i in range(C) if i < ln and tok0 + i >= 0]
+            out.append((s, h, units, rows))
+    return out
+
+
+def _valid_cu(rng, n, maxlen):
+    lens = [rng.randrange(0, maxlen) for _ in range(n)]
+    cu = [0]
+    for L in lens:
+        cu.append(cu[-1] + L)
+    return cu
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("C", [16, 64])
+@pytest.mark.parametrize("conv", [False, True])
+def test_valid_cu_seqlens_exact_cover(seed, C, conv):
+    rng = random.Random(seed)
+    n, H = rng.randrange(1, 9), rng.choice([1, 3, 16])
+    cu = _valid_cu(rng, n, 300)
+    T = cu[-1]
+    prep = prep_touch(cu, n, T, H, C, conv)
+    units = [u for u, _, _, _ in prep]
+    assert len(units) == len(set(units))  # one workgroup per unit
+    excl, incl = seq_table(cu, n, C)
+    expect = {(c, h) for s in range(n) for c in range(excl[s], incl[s]) for h in range(H)}
+    assert {ch for _, ch, _, _ in prep} == expect
+    for u, (c, h), rows, halo in prep:
+        s = next(s for s in range(n) if excl[s] <= c < incl[s])
+        assert rows and cu[s] <= rows[0] and rows[-1] < cu[s + 1]
+        assert all(cu[s] <= r < rows[-1] + 1 for r in halo)
+    for s, h, su, rows in scan_touch(cu, n, T, H, C):
+        assert su == [c * H + h for c in range(excl[s], incl[s])]
+        assert rows == list(range(cu[s], cu[s + 1]))
+
+
+BROKEN = [
+    [0, 1000, 0, 1000],          # decreasing: more chunks than the workspace bound
+    [0, 70, 30, 200, 150],       # overlapping, decreasing
+    [-64, 10, 300],              # negative start
+    [0, 50, 900],                # past total_tokens
+    [5, 5, 5],                   # cu[0] != 0
+    [0, 300, 100, 400, 0, 500],
+]
+
+
+@pytest.mark.parametrize("cu", BROKEN)
+@pytest.mark.parametrize("C", [16, 64])
+@pytest.mark.parametrize("conv", [False, True])
+def test_broken_cu_seqlens_stay_in_bounds(cu, C, conv):
+    n, H = len(cu) - 1, 3
+    T = 400 if cu != BROKEN[0] else 1000
+    mc = max_chunks(T, n, C)
+    for u, _, rows, halo in prep_touch(cu, n, T, H, C, conv):
+        assert 0 <= u < mc * H
+        assert all(0 <= r < T for r in rows + halo)
+    for _, _, units, rows in scan_touch(cu, n, T, H, C):
+        assert all(0 <= u < mc * H for u in units)
+        assert all(0 <= r < T for r in rows)
+
+
+def test_random_broken_cu_seqlens_stay_in_bounds():
+    rng = random.Random(7)
+    for _ in range(200):
+        n, H, C = rng.randrange(1, 7), rng.choice([1, 2, 5]), rng.choice([16, 32, 64])
+        T = rng.randrange(0, 500)
+        cu = [rng.randrange(-100, 700) for _ in range(n + 1)]
+        mc = max_chunks(T, n, C)
+        for u, _, rows, halo in prep_touch(cu, n, T, H, C, rng.random() < 0.5):
+            assert 0 <= u < mc * H and all(0 <= r < T for r in rows + halo)
+        for _, _, units, rows in scan_touch(cu, n, T, H, C):
+            assert all(0 <= u < mc * H for u in units) and all(0 <= r < T for r in rows)
