@@ -410,29 +410,42 @@ def cpu_baseline(budget_s=20.0):
         total += run(n)
         passes += 1
     multi = n * passes / total
-    # the same oracle on one thread, over a shorter prefix (about a tenth of the budget)
-    n1, t1, p1 = 256, 0.0, 0
-    while True:
-        sl = slice(0, n1)
-        t0 = time.perf_counter()
-        oracle.recurrence(x.q[sl], x.k[sl], x.v[sl], x.g[sl], x.beta[sl],
-                          torch.tensor([0, n1], dtype=torch.int32), scale=x.scale, n_threads=1)
-        dt1 = time.perf_counter() - t0
-        if dt1 * 4 < budget_s / 20 and n1 < x.q.shape[0]:
-            n1 *= 2
-            continue
-        t1 += dt1
-        p1 += 1
-        if t1 >= budget_s / 10:
-            break
-    return dict(value=multi, unit="tokens/s", cores=min(threads, x.q.shape[1]),
+    # the same oracle on one thread over the whole workload (one pass, a few seconds)
+    sl = slice(0, x.q.shape[0])
+    t0 = time.perf_counter()
+    oracle.recurrence(x.q[sl], x.k[sl], x.v[sl], x.g[sl], x.beta[sl],
+                      torch.tensor([0, x.q.shape[0]], dtype=torch.int32), scale=x.scale,
+                      n_threads=1)
+    t1 = time.perf_counter() - t0
+    used = min(threads, x.q.shape[1])  # one thread per (sequence, head) unit
+    return dict(value=multi, unit="tokens/s", cores=used,
                 kind="oracle",
                 sample=f"fp64 sequential recurrence, first {n} of 8192 tokens x 16 heads, "
                        f"{passes} passes in {total:.1f} s (one thread per (sequence, head) "
-                       f"unit)",
-                single_core=dict(value=n1 * p1 / t1, unit="tokens/s", cores=1,
-                                 sample=f"first {n1} tokens x 16 heads on one thread, "
-                                        f"{p1} passes in {t1:.1f} s"))
+                       f"unit, {used} threads)",
+                host=host_info(),
+                single_core=dict(value=x.q.shape[0] / t1, unit="tokens/s", cores=1,
+                                 sample=f"all 8192 tokens x 16 heads on one thread, one pass "
+                                        f"in {t1:.1f} s"))
+
+
+def host_info():
+    """The host the oracle ran on: logical CPUs the OS reports, the CPUs this process may
+    run on, and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return dict(os_cpu_count=os.cpu_count(), affinity_cpus=affinity, cpu_model=model)
 
 
 # ------------------------------------------------------------------- counter calibration

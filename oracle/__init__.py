@@ -73,7 +73,16 @@ def _pi(a):
 
 
 def default_threads():
-    return max(1, min(64, os.cpu_count() or 1))
+    """Threads for the per-unit pool: the CPUs this process may use, capped by
+    OMP_NUM_THREADS when it is set (a shared host's CPU share) and by 64."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, min(64, n))
 
 
 def recurrence(q, k, v, g, beta, cu_seqlens, scale=1.0, l2norm=False, eps=1e-6,
