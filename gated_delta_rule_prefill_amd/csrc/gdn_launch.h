@@ -17,7 +17,9 @@ namespace gdn {
 //   mmat  [C][CP]    e   M (lower triangular incl. diagonal)        row-major; the MFMA
 //                        fragments (K-step columns) that start right of a row's 16-token
 //                        block are all zero, never written and never read
-//   ut    [d_v][C]   e   U (local residuals), 16-column tiles in MFMA accumulator order
+//   ut    [d_v][C]   f32 U (local residuals), 16-column tiles in MFMA accumulator order.
+//                        fp32: E = U - W S cancels, and a rounded U would carry its rounding
+//                        into the small residual
 //   decay [d_k]      f32 e^{G_C} per key channel
 struct PrefillWs {
     int32_t* chunk_info;   // [max_chunks][4]: seq, token start, length, 0
@@ -26,7 +28,7 @@ struct PrefillWs {
     void* qin;
     void* kgt;
     void* mmat;
-    void* ut;
+    float* ut;
     float* decay;
     void* dump;            // scratch words that absorb stores of lanes past a sequence end
     int64_t max_chunks;

@@ -60,7 +60,7 @@ size_t prefill_ws_layout(int dtype, int H, int dk, int dv, int chunk, int n_seqs
     const size_t o_q = off;   off = align256(off + units * chunk * dkp * e);
     const size_t o_k = off;   off = align256(off + units * dk * cp * e);
     const size_t o_m = off;   off = align256(off + units * chunk * cp * e);
-    const size_t o_u = off;   off = align256(off + units * dv * chunk * e);
+    const size_t o_u = off;   off = align256(off + units * dv * chunk * 4);  // U in fp32
     const size_t o_d = off;   off = align256(off + units * dk * 4);
     const size_t o_x = off;   off = align256(off + 256 * 4);
     if (out != nullptr) {
@@ -71,7 +71,7 @@ size_t prefill_ws_layout(int dtype, int H, int dk, int dv, int chunk, int n_seqs
         out->qin = b + o_q;
         out->kgt = b + o_k;
         out->mmat = b + o_m;
-        out->ut = b + o_u;
+        out->ut = reinterpret_cast<float*>(b + o_u);
         out->decay = reinterpret_cast<float*>(b + o_d);
         out->dump = b + o_x;
         out->max_chunks = max_chunks;

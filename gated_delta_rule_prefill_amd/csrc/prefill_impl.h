@@ -16,7 +16,7 @@
 //   prep  (grid: chunks x heads, fully parallel): everything that depends only on the chunk
 //         — G, A and M on MFMA, R by blocked substitution in fp32, U and W on MFMA — written
 //         once to a workspace in MFMA-operand-ready layouts (-W and Q_in row-major, K_g^T
-//         key-major, M row-major, U^T value-major, e^{G_C}).
+//         key-major, M row-major, U in the scan's accumulator order and in fp32, e^{G_C}).
 //   scan  (grid: sequences x heads x d_v/16 value tiles, serial over a sequence's chunks):
 //         the only sequential part. A 16-column slice of the fp32 state lives in MFMA
 //         accumulators across the whole sequence; per chunk
@@ -180,11 +180,11 @@ struct PrepSmem {
                 alignas(16) float ar[C][C + 1];  // A (strictly lower), then R = (I + A)^{-1}
                                                  // in place; the strictly upper part is
                                                  // merge scratch
-                alignas(16) T va[PERKEY ? 1 : DV][F::LDC];  // scalar gate: (diag(beta) V)^T,
+                alignas(16) T va[PERKEY ? 1 : DV][F::LDC];  // scalar gate: V^T,
                                                             // written once R is complete
             };
             alignas(16) T rs[C][F::LDC];     // R as an MFMA operand
-            alignas(16) T vt[PERKEY ? DV : 1][F::LDC];  // per-key gate: (diag(beta) V)^T
+            alignas(16) T vt[PERKEY ? DV : 1][F::LDC];  // per-key gate: V^T
         } b;
     } u;
     // per-key conv: the weights, kept for V's convolution after P0 (the other members keep
@@ -794,17 +794,15 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
             for (int f = 2 * NK; f < 2 * NK + NV; f++) conv_frag(f);
         }
     }
-    // (diag(beta) V)^T: lane (g4, n) gets V[16w + 4 g4 + e][16 vb + n], plus zero padding
-    // tokens; per-key gate here, scalar gate after the merges (over A/R)
+    // V^T: lane (g4, n) gets V[16w + 4 g4 + e][16 vb + n] (exact in the element type), plus
+    // zero padding tokens; per-key gate here, scalar gate after the merges (over A/R)
     auto store_vt = [&]() {
         if (own) {
             const int t0 = w * 16 + g4 * 4;
 #pragma unroll
             for (int vb = 0; vb < DV / 16; vb++) {
                 const f32x4 vt4 = Ident<T>::template transpose<NV>(vf, vb, idf);
-                float vv[4];
-#pragma unroll
-                for (int e = 0; e < 4; e++) vv[e] = sm.bs[t0 + e] * vt4[e];
+                float vv[4] = {vt4[0], vt4[1], vt4[2], vt4[3]};
                 store4<T>(&vt[vb * 16 + r16][t0], vv);
             }
         }
@@ -899,10 +897,13 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
                 Frag<T>::template store_run<4>(wneg, i, c0, DKP, z);
             }
         }
-        T* ut = reinterpret_cast<T*>(a.ws.ut) + u * DV * C;
+        float* ut = a.ws.ut + u * DV * C;
         constexpr int NW = (DK / 16) * NB;  // W^T tiles: (channel block, token block)
         constexpr int NU = NB * (DV / 16);  // U tiles: (token block, value block)
-        // tile order keeps the R fragments of one token block on one wave
+        // tile order keeps the R fragments of one token block on one wave; the U tiles' A
+        // operand (R - I) diag(beta) of that token block is formed once and reused
+        frag ua[CP / KB];
+        int ua_mb = -1;
         for (int t = w; t < NW + NU; t += PF_WAVES) {
             f32x4 acc = zero4();
             if (t < NW) {
@@ -921,15 +922,44 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
             } else {
                 const int tt = t - NW;
                 const int mb = tt % NB, nb = tt / NB;  // mb: token block, nb: value block
+                // U = R diag(beta) V = diag(beta) V + (R - I) diag(beta) V. R has a unit
+                // diagonal, so beta_i V_i is U's leading term: it enters the accumulator in
+                // fp32 from the exact V, and only the small off-diagonal part goes through
+                // rounded MFMA operands (rounding diag(beta) V itself was the largest single
+                // error source of the outputs in the element type)
+                {
+                    float v4[4];
+                    load4<T>(&vt[nb * 16 + r16][mb * 16 + 4 * g4], v4);
+                    const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sm.bs[mb * 16 + 4 * g4]);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) acc[e] = b4[e] * v4[e];
+                }
+                if (mb != ua_mb) {  // uniform across the wave
+                    ua_mb = mb;
+                    const int irow = mb * 16 + r16;
+#pragma unroll
+                    for (int kb = 0; kb < CP / KB; kb++) {
+                        const auto fr = MM::load(&sm.u.b.rs[irow][kb * KB + kq]);
+#pragma unroll
+                        for (int e = 0; e < KPL; e++) {
+                            const int j = kb * KB + kq + e;
+                            float x;
+                            if constexpr (KPL == 1) x = to_f32(fr);
+                            else x = to_f32(fr[e]);
+                            x = (j == irow || j >= C) ? 0.f : x * sm.bs[j];
+                            if constexpr (KPL == 1) ua[kb] = from_f32<T>(x);
+                            else ua[kb][e] = from_f32<T>(x);
+                        }
+                    }
+                }
 #pragma unroll
                 for (int kb = 0; kb < CP / KB; kb++) {
-                    auto fa = MM::load(&sm.u.b.rs[mb * 16 + r16][kb * KB + kq]);
                     auto fb = MM::load(&vt[nb * 16 + r16][kb * KB + kq]);
-                    acc = MM::mma(fa, fb, acc);
+                    acc = MM::mma(ua[kb], fb, acc);
                 }
                 // lane: U[i = mb*16 + 4*g4 + e][v = nb*16 + r16], scan accumulator order
                 float uu[4] = {acc[0], acc[1], acc[2], acc[3]};
-                store4<T>(ut + ((size_t)(nb * NB + mb) * 64 + lane) * 4, uu);
+                store4<float>(ut + ((size_t)(nb * NB + mb) * 64 + lane) * 4, uu);
             }
         }
     }
@@ -993,13 +1023,13 @@ __device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROL
     if constexpr (PART == 0) {
         if constexpr (EROLE) {
             const T* wneg = reinterpret_cast<const T*>(a.ws.wneg) + u * C * F::DKP;
-            const T* ut = reinterpret_cast<const T*>(a.ws.ut) + u * DV * C;
+            const float* ut = a.ws.ut + u * DV * C;
 #pragma unroll
             for (int kb = 0; kb < O::NK; kb++) op.a[kb] = MM::load(Frag<T>::ptr(wneg, mb, kb, F::DKP, lane));
 #pragma unroll
             for (int v = 0; v < NVB; v++) {
                 float u4[4];
-                load4<T>(ut + ((size_t)((vcol0 / 16 + v) * F::NB + mb) * 64 + lane) * 4, u4);
+                load4<float>(ut + ((size_t)((vcol0 / 16 + v) * F::NB + mb) * 64 + lane) * 4, u4);
                 op.u[v] = f32x4{u4[0], u4[1], u4[2], u4[3]};
             }
         } else {
