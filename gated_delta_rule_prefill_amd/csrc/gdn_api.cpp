@@ -8,6 +8,7 @@
 #include <stdio.h>
 
 #include <initializer_list>
+#include <mutex>
 #include <utility>
 #include <vector>
 
@@ -102,6 +103,52 @@ int debug_distinct_slots(std::initializer_list<std::pair<const int32_t*, int64_t
 #endif
 #define SLOT_LISTS(...) (std::initializer_list<std::pair<const int32_t*, int64_t>>{__VA_ARGS__})
 
+// Workspace of the allocation-free prefill (gdn_prefill_chunked_noalloc): one copy per GPU,
+// created with the library's code object on that GPU. Host code never uses the array's name
+// as an address (on the host it is only a stand-in for the symbol); the device address of
+// each GPU's copy comes from hipGetSymbolAddress with that GPU current, kept per device.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch`, resolved on the first call with that device
+// current. The caller's stream must belong to that device.
+int scratch_for_stream(void* stream, void** out, const char* what) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(GDN_ERR_LAUNCH, "%s: no current HIP device", what);
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(GDN_ERR_UNSUPPORTED, "%s: device %d beyond the %d the library tracks", what,
+                    dev, kMaxDevices);
+    if (stream != nullptr) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(GDN_ERR_LAUNCH, "%s: cannot query the stream's device", what);
+        }
+        if (sdev != dev)
+            return fail(GDN_ERR_UNSUPPORTED, "%s: the stream belongs to device %d, device %d is "
+                                             "current", what, (int)sdev, dev);
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return fail(GDN_ERR_LAUNCH, "%s: hipGetSymbolAddress(scratch) failed: %s", what,
+                        hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GDN_OK;
+}
+
 int launch_status(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
     return ok();
@@ -148,7 +195,7 @@ int prefill_run(const gdn_dims_t* dims, const void* q, const void* k, const void
                 const int32_t* slots, const int32_t* has_init, const int32_t* ckpt_cu,
                 const int32_t* ckpt_pos, const int32_t* ckpt_slots, int32_t n_ckpt, void* o,
                 void* workspace, size_t ws_bytes, void* stream, const char* what,
-                const ConvIn* conv = nullptr) {
+                const ConvIn* conv = nullptr, bool noalloc = false) {
     int st = prefill_common_checks(dims, n_seqs, total_tokens, chunk);
     if (st) return st;
     if (conv != nullptr && (conv->width < 2 || conv->width > 4))
@@ -182,6 +229,18 @@ int prefill_run(const gdn_dims_t* dims, const void* q, const void* k, const void
         REQUIRE_PTR(g);
         REQUIRE_PTR(beta);
         REQUIRE_PTR(o);
+    }
+    if (noalloc) {
+        const size_t need = gdn::prefill_ws_layout(dims->dtype, dims->num_heads, dims->d_k,
+                                                   dims->d_v, chunk, n_seqs, total_tokens,
+                                                   nullptr, nullptr);
+        if (need > GDN_NOALLOC_SCRATCH_BYTES)
+            return fail(GDN_ERR_WORKSPACE, "%s: the call needs %zu bytes of workspace, the "
+                                           "library's per-GPU scratch holds %zu", what, need,
+                        GDN_NOALLOC_SCRATCH_BYTES);
+        st = scratch_for_stream(stream, &workspace, what);
+        if (st) return st;
+        ws_bytes = GDN_NOALLOC_SCRATCH_BYTES;
     }
     REQUIRE_PTR(workspace);
     gdn::PrefillWs ws;
@@ -320,6 +379,17 @@ int gdn_prefill_chunked_conv(const gdn_dims_t* dims, const void* x, const float*
                        total_tokens, chunk, state_pool, n_slots, slots, has_init, nullptr,
                        nullptr, nullptr, 0, o, workspace, ws_bytes, stream,
                        "gdn_prefill_chunked_conv", &conv);
+}
+
+int gdn_prefill_chunked_noalloc(const gdn_dims_t* dims, const void* q, const void* k,
+                                const void* v, const float* g, const float* beta,
+                                const int32_t* cu_seqlens, int32_t n_seqs,
+                                int32_t total_tokens, int32_t chunk, float* state_pool,
+                                int32_t n_slots, const int32_t* slots, const int32_t* has_init,
+                                void* o, void* stream) {
+    return prefill_run(dims, q, k, v, g, beta, cu_seqlens, n_seqs, total_tokens, chunk,
+                       state_pool, n_slots, slots, has_init, nullptr, nullptr, nullptr, 0, o,
+                       nullptr, 0, stream, "gdn_prefill_chunked_noalloc", nullptr, true);
 }
 
 int gdn_decode_step(const gdn_dims_t* dims, const void* q, const void* k, const void* v,

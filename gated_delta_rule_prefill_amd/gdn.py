@@ -14,6 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgdn.so")
 
 GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
+# include/gdn.h GDN_NOALLOC_SCRATCH_BYTES: the allocation-free prefill's per-GPU workspace
+GDN_NOALLOC_SCRATCH_BYTES = 128 << 20
 GDN_GATE_SCALAR, GDN_GATE_PER_KEY = 0, 1
 
 
@@ -50,6 +52,8 @@ _SIGS = {
                                  _P, _P, _P, _I, _P, _P, _SZ, _P],
     "gdn_prefill_chunked_conv": [_DIMS, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _P, _I, _P,
                                  _P, _P, _P, _SZ, _P],
+    "gdn_prefill_chunked_noalloc": [_DIMS, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _I, _P,
+                                    _P, _P, _P],
     "gdn_decode_step": [_DIMS, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, _P],
     "gdn_decode_spec": [_DIMS, _P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _P, _P],
     "gdn_decode_fused": [_DIMS, _P, _P, _I, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I, _P, _I,
@@ -169,6 +173,27 @@ def gdn_prefill_chunked(q, k, v, g, beta, cu_seqlens, chunk, state_pool, slots, 
         ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
         int(n), int(T), int(chunk), _ptr(state_pool), int(state_pool.shape[0]), _ptr(slots),
         _ptr(has_init), _ptr(o), _ptr(workspace), int(workspace.numel()), _stream(stream)))
+    return o
+
+
+def gdn_prefill_chunked_noalloc(q, k, v, g, beta, cu_seqlens, chunk, state_pool, slots,
+                                has_init=None, scale=1.0, qk_l2norm=False, o=None,
+                                stream=None):
+    """gdn_prefill_chunked without a workspace: the library's per-GPU scratch array serves
+    as one (at most GDN_NOALLOC_SCRATCH_BYTES). Nothing is allocated when `o` is given.
+    Arguments as gdn_prefill_chunked. Returns o."""
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    n = cu_seqlens.numel() - 1
+    perkey = g.dim() == 3
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+    _dev(q, k, v, g, beta, cu_seqlens, state_pool, slots, has_init, o)
+    dims = make_dims(H, dk, dv, _dtype_code(q), perkey, scale, qk_l2norm)
+    _check("gdn_prefill_chunked_noalloc", lib().gdn_prefill_chunked_noalloc(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+        int(n), int(T), int(chunk), _ptr(state_pool), int(state_pool.shape[0]), _ptr(slots),
+        _ptr(has_init), _ptr(o), _stream(stream)))
     return o
 
 

@@ -37,9 +37,10 @@
  *     ([Handbook] "练习" 2: rounding would accumulate step after step).
  *   - Supported head dims: d_k == d_v in {16, 32, 64, 128}. Chunk sizes: 16, 32, 64.
  *   - Ownership: the caller allocates and frees all memory, including workspaces sized by
- *     the *_workspace_bytes queries. The library allocates nothing, keeps no mutable global
- *     state, never synchronises, and launches only on `stream` (a hipStream_t; NULL = the
- *     default stream). Calls are asynchronous: device-side faults surface at the caller's
+ *     the *_workspace_bytes queries. The library allocates nothing and keeps no mutable
+ *     global state, except the allocation-free prefill's per-GPU device array and the cache
+ *     of its per-device addresses (gdn_prefill_chunked_noalloc); it never synchronises, and
+ *     launches only on `stream` (a hipStream_t; NULL = the default stream). Calls are asynchronous: device-side faults surface at the caller's
  *     next synchronisation.
  *   - Errors: every entry point returns a gdn_status_t. Arguments are validated on the host
  *     before any launch; a call that returns an error has launched nothing and changed no
@@ -205,6 +206,30 @@ int gdn_prefill_chunked_conv(const gdn_dims_t* dims, const void* x, const float*
                              int32_t total_tokens, int32_t chunk, float* state_pool,
                              int32_t n_slots, const int32_t* slots, const int32_t* has_init,
                              void* o, void* workspace, size_t ws_bytes, void* stream);
+
+/* Allocation-free chunked prefill, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, computation and results as gdn_prefill_chunked, without the workspace
+ * arguments: the workspace is a file-scope device array of GDN_NOALLOC_SCRATCH_BYTES bytes
+ * inside the library, one copy per GPU, which that GPU holds from the library's first use on
+ * it until the process ends. The call allocates nothing (no hipMalloc / hipFree, no
+ * allocating library routine).
+ *   - A call whose gdn_prefill_workspace_bytes(...) exceeds GDN_NOALLOC_SCRATCH_BYTES returns
+ *     GDN_ERR_WORKSPACE before any launch (split it into several calls with the state handed
+ *     over through the pool, or use gdn_prefill_chunked).
+ *   - `stream` must belong to the current device (GDN_ERR_UNSUPPORTED otherwise): the
+ *     array's address is resolved for the current device.
+ *   - Every call on one GPU shares that GPU's array. Calls ordered on one stream are safe;
+ *     calls that overlap on one GPU (different streams, or threads without ordering) race
+ *     and give undefined results. The array keeps the last call's contents, which carry no
+ *     meaning: nothing in it has to start at zero. */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int gdn_prefill_chunked_noalloc(const gdn_dims_t* dims, const void* q, const void* k,
+                                const void* v, const float* g, const float* beta,
+                                const int32_t* cu_seqlens, int32_t n_seqs,
+                                int32_t total_tokens, int32_t chunk, float* state_pool,
+                                int32_t n_slots, const int32_t* slots, const int32_t* has_init,
+                                void* o, void* stream);
 
 /* ------------------------------------------------------------------------------- decode */
 

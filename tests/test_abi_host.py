@@ -22,6 +22,7 @@ def _declared():
 def test_header_declares_the_abi():
     names = _declared()
     for n in ("gdn_prefill_chunked", "gdn_prefill_chunked_ckpt", "gdn_prefill_chunked_conv",
+              "gdn_prefill_chunked_noalloc",
               "gdn_prefill_workspace_bytes", "gdn_decode_step", "gdn_decode_spec",
               "gdn_decode_fused",
               "gdn_decode_deltalog", "gdn_deltalog_workspace_bytes", "gdn_deltalog_reset",
@@ -137,6 +138,45 @@ def test_prefill_workspace_too_small_and_sizing():
     more = ctypes.c_size_t(0)
     lib.gdn_prefill_workspace_bytes(ctypes.byref(dims), 8, 8192, 64, ctypes.byref(more))
     assert more.value > need.value
+
+
+def _prefill_noalloc(dims, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, cu=FAKE, n=2, T=100, chunk=64,
+             pool=FAKE, n_slots=4, slots=FAKE, has_init=None, o=FAKE)
+    a.update(kw)
+    return gdn.load().gdn_prefill_chunked_noalloc(
+        ctypes.byref(dims), a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["n"], a["T"],
+        a["chunk"], a["pool"], a["n_slots"], a["slots"], a["has_init"], a["o"], None)
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define GDN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m is not None
+    assert int(m.group(1)) << int(m.group(2)) == gdn.GDN_NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(cu=None), 1), (dict(slots=None), 1), (dict(o=FAKE + 2), 4),
+    (dict(chunk=48), 3), (dict(n=-1), 2), (dict(n_slots=0), 2),
+])
+def test_prefill_noalloc_rejects_bad_arguments(kw, status):
+    assert _prefill_noalloc(_dims(), **kw) == status
+    assert gdn.gdn_last_error() != ""
+
+
+def test_prefill_noalloc_rejects_calls_beyond_its_scratch_before_any_hip_call():
+    """The size check precedes every HIP call (this host has no GPU): a call whose workspace
+    would exceed the per-GPU scratch returns GDN_ERR_WORKSPACE and names both sizes."""
+    lib = gdn.load()
+    dims = _dims(H=16, dk=128, dv=128)
+    need = ctypes.c_size_t(0)
+    T = 8192
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(dims), 1, T, 64, ctypes.byref(need)) == 0
+    assert need.value > gdn.GDN_NOALLOC_SCRATCH_BYTES
+    assert _prefill_noalloc(dims, n=1, T=T) == 5
+    assert str(gdn.GDN_NOALLOC_SCRATCH_BYTES) in gdn.gdn_last_error()
+    assert _prefill_noalloc(dims, n=0, q=None) == 0  # zero sequences: a no-op
 
 
 def test_zero_sized_calls_are_noops_without_gpu():
