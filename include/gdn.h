@@ -35,13 +35,18 @@
  *     bounded ones where their products stay exact (-inf and NaN are not accepted; the host
  *     does not read g, so they are not rejected either). The state is always fp32
  *     ([Handbook] "练习" 2: rounding would accumulate step after step).
- *   - Supported head dims: d_k == d_v in {16, 32, 64, 128}. Chunk sizes: 16, 32, 64.
+ *   - Supported head dims: d_k == d_v in {16, 32, 64, 128}; d_k != d_v returns
+ *     GDN_ERR_UNSUPPORTED. This is a contract choice: every workload on the pages uses
+ *     d_k == d_v, the kernels are specialised per head dim at compile time (value tiles,
+ *     fragment counts, thread maps), and independent d_k and d_v would multiply the
+ *     prefill's instantiations (and the library's build time and size) about fourfold with
+ *     no change for the d_k == d_v paths. Chunk sizes: 16, 32, 64.
  *   - Ownership: the caller allocates and frees all memory, including workspaces sized by
  *     the *_workspace_bytes queries. The library allocates nothing and keeps no mutable
  *     global state, except the allocation-free prefill's per-GPU device array and the cache
  *     of its per-device addresses (gdn_prefill_chunked_noalloc); it never synchronises, and
- *     launches only on `stream` (a hipStream_t; NULL = the default stream). Calls are asynchronous: device-side faults surface at the caller's
- *     next synchronisation.
+ *     launches only on `stream` (a hipStream_t; NULL = the default stream). Calls are
+ *     asynchronous: device-side faults surface at the caller's next synchronisation.
  *   - Errors: every entry point returns a gdn_status_t. Arguments are validated on the host
  *     before any launch; a call that returns an error has launched nothing and changed no
  *     memory. gdn_last_error() returns a thread-local description of the last failure.
