@@ -17,9 +17,11 @@ namespace gdn {
 //   mmat  [C][CP]    e   M (lower triangular incl. diagonal)        row-major; the MFMA
 //                        fragments (K-step columns) that start right of a row's 16-token
 //                        block are all zero, never written and never read
-//   ut    [d_v][C]   f32 U (local residuals), 16-column tiles in MFMA accumulator order.
-//                        fp32: E = U - W S cancels, and a rounded U would carry its rounding
-//                        into the small residual
+//   ut    [d_v][C]   f32 U (local residuals), 16-column tiles in MFMA accumulator order,
+//                        4 bytes per value in either of two formats (PrefillArgs::u32):
+//                        fp32, or for bf16 inputs bf16 values in the first half of the
+//                        section and their rounding residuals (x 2^16, e5m2) in the third
+//                        quarter (ul). E = U - W S cancels, so U stays close to fp32.
 //   decay [d_k]      f32 e^{G_C} per key channel
 struct PrefillWs {
     int32_t* chunk_info;   // [max_chunks][4]: seq, token start, length, 0
@@ -28,7 +30,8 @@ struct PrefillWs {
     void* qin;
     void* kgt;
     void* mmat;
-    float* ut;
+    void* ut;
+    uint8_t* ul;           // residual bytes of U (bf16 inputs), inside the ut section
     float* decay;
     void* dump;            // scratch words that absorb stores of lanes past a sequence end
     int64_t max_chunks;
@@ -59,8 +62,35 @@ struct PrefillArgs {
     const float* conv_w;
     void* conv_state;
     int conv_width;
+    // U format in the workspace, chosen by the host for the whole call: 1 = fp32; 0 = bf16
+    // value plus an 8-bit residual (bf16 inputs only). The scan's 16-column tiles are bound
+    // by their per-chunk dependency chain, where decoding the residual would lengthen each
+    // chunk step; wider tiles are bound by reading the workspace, where 3 bytes per value
+    // instead of 4 shorten it. The prep stores in this format; the scan reads the format
+    // its compile-time tile width implies, so u32 must equal (scan_value_tiles(...) == 1)
+    // for bf16 inputs.
+    int u32;
     PrefillWs ws;
 };
+
+// Value width of the scan's workgroups, in 16-column tiles: the widest that still leaves at
+// least one workgroup per CU (wider tiles share each chunk's operand stream over more
+// columns; narrower ones run more sequential chains at once).
+inline int scan_value_tiles(int64_t units, int dv, int ncu) {
+    const int64_t tiles = units * (dv / 16);
+    int nvb = 1;
+    while (nvb * 2 <= dv / 16 && tiles / (nvb * 2) >= ncu) nvb *= 2;
+    return nvb;
+}
+inline int device_cu_count() {
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        ncu = 256;
+    }
+    return ncu;
+}
 
 // Chunk length / key dim rounded up to the MFMA contraction step of the element type
 // (bf16: 32, fp32: 4); the padding is zero-filled.

@@ -16,7 +16,8 @@
 //   prep  (grid: chunks x heads, fully parallel): everything that depends only on the chunk
 //         — G, A and M on MFMA, R by blocked substitution in fp32, U and W on MFMA — written
 //         once to a workspace in MFMA-operand-ready layouts (-W and Q_in row-major, K_g^T
-//         key-major, M row-major, U in the scan's accumulator order and in fp32, e^{G_C}).
+//         key-major, M row-major, U in the scan's accumulator order at close to fp32
+//         precision, e^{G_C}).
 //   scan  (grid: sequences x heads x d_v/16 value tiles, serial over a sequence's chunks):
 //         the only sequential part. A 16-column slice of the fp32 state lives in MFMA
 //         accumulators across the whole sequence; per chunk
@@ -149,6 +150,56 @@ struct Frag {
         return base + ((rb * (K / KB) + kb) * 64 + ln) * KPL;
     }
 };
+
+// U (local residuals) is stored in the scan's accumulator order at close to fp32 precision:
+// E = U - W S cancels, so a rounding of U is an error relative to U rather than to the
+// small residual. Either fp32 (u32), or, for bf16 inputs, U rounded to bf16 plus its
+// rounding residual, scaled by 2^16, in 8-bit e5m2 (3 bytes per value instead of 4): the
+// residual is at most 2^-8 |U| and e5m2 keeps it to 2^-3, so U comes back to ~2^-11
+// relative for 2^-20 <= |U| <= 224 (beyond, the clamped residual leaves plain bf16 accuracy).
+constexpr float U_RES_SCALE = 65536.f;
+constexpr float U_RES_UNSCALE = 1.f / 65536.f;
+template <typename T>
+__device__ __forceinline__ void store_u(const PrefillWs& ws, bool u32, size_t idx,
+                                        const float v[4]);
+template <>
+__device__ __forceinline__ void store_u<float>(const PrefillWs& ws, bool, size_t idx,
+                                               const float v[4]) {
+    store4<float>(reinterpret_cast<float*>(ws.ut) + idx, v);
+}
+template <>
+__device__ __forceinline__ void store_u<bf16>(const PrefillWs& ws, bool u32, size_t idx,
+                                              const float v[4]) {
+    if (u32) {
+        store4<float>(reinterpret_cast<float*>(ws.ut) + idx, v);
+        return;
+    }
+    store4<bf16>(reinterpret_cast<bf16*>(ws.ut) + idx, v);
+    float r[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        const float res = v[e] - (float)(bf16)v[e];  // exact in fp32
+        r[e] = __builtin_amdgcn_fmed3f(res * U_RES_SCALE, 57344.f, -57344.f);
+    }
+    int p = __builtin_amdgcn_cvt_pk_bf8_f32(r[0], r[1], 0, false);
+    p = __builtin_amdgcn_cvt_pk_bf8_f32(r[2], r[3], p, true);
+    *reinterpret_cast<int*>(ws.ul + idx) = p;
+}
+// The reader knows the format at compile time (the scan's tile width decides it; a runtime
+// branch inside the scan's prefetch sequence cost 17-20 % on the wide-tile scans).
+template <typename T, bool U32>
+__device__ __forceinline__ void load_u(const PrefillWs& ws, size_t idx, float out[4]) {
+    if constexpr (U32 || sizeof(T) == 4) {
+        load4<float>(reinterpret_cast<const float*>(ws.ut) + idx, out);
+    } else {
+        load4<bf16>(reinterpret_cast<const bf16*>(ws.ut) + idx, out);
+        const int p = *reinterpret_cast<const int*>(ws.ul + idx);
+        out[0] += __builtin_amdgcn_cvt_f32_bf8(p, 0) * U_RES_UNSCALE;
+        out[1] += __builtin_amdgcn_cvt_f32_bf8(p, 1) * U_RES_UNSCALE;
+        out[2] += __builtin_amdgcn_cvt_f32_bf8(p, 2) * U_RES_UNSCALE;
+        out[3] += __builtin_amdgcn_cvt_f32_bf8(p, 3) * U_RES_UNSCALE;
+    }
+}
 
 // =====================================================================================
 // prep kernel
@@ -897,7 +948,7 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
                 Frag<T>::template store_run<4>(wneg, i, c0, DKP, z);
             }
         }
-        float* ut = a.ws.ut + u * DV * C;
+        const size_t ut = u * DV * C;  // this unit's U values
         constexpr int NW = (DK / 16) * NB;  // W^T tiles: (channel block, token block)
         constexpr int NU = NB * (DV / 16);  // U tiles: (token block, value block)
         // tile order keeps the R fragments of one token block on one wave; the U tiles' A
@@ -959,7 +1010,7 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
                 }
                 // lane: U[i = mb*16 + 4*g4 + e][v = nb*16 + r16], scan accumulator order
                 float uu[4] = {acc[0], acc[1], acc[2], acc[3]};
-                store4<float>(ut + ((size_t)(nb * NB + mb) * 64 + lane) * 4, uu);
+                store_u<T>(a.ws, a.u32 != 0, ut + ((size_t)(nb * NB + mb) * 64 + lane) * 4, uu);
             }
         }
     }
@@ -1023,13 +1074,15 @@ __device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROL
     if constexpr (PART == 0) {
         if constexpr (EROLE) {
             const T* wneg = reinterpret_cast<const T*>(a.ws.wneg) + u * C * F::DKP;
-            const float* ut = a.ws.ut + u * DV * C;
+            const size_t ut = u * DV * C;  // this unit's U values
 #pragma unroll
             for (int kb = 0; kb < O::NK; kb++) op.a[kb] = MM::load(Frag<T>::ptr(wneg, mb, kb, F::DKP, lane));
 #pragma unroll
             for (int v = 0; v < NVB; v++) {
                 float u4[4];
-                load4<float>(ut + ((size_t)((vcol0 / 16 + v) * F::NB + mb) * 64 + lane) * 4, u4);
+                // 16-column tiles read fp32 U; wider ones bf16 plus the residual (the host
+                // chose the prep's store format by the same rule)
+                load_u<T, NVB == 1>(a.ws, ut + ((size_t)((vcol0 / 16 + v) * F::NB + mb) * 64 + lane) * 4, u4);
                 op.u[v] = f32x4{u4[0], u4[1], u4[2], u4[3]};
             }
         } else {
@@ -1348,6 +1401,9 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
 // =====================================================================================
 __global__ void seq_first_kernel(const int32_t* cu, int n_seqs, int C, int32_t* seq_first);
 
+// nvb comes from scan_value_tiles, which never exceeds D / 16, so the instantiated tile
+// width always equals nvb (the ternaries only keep impossible combinations from being
+// instantiated); the U format the prep stored relies on that.
 template <typename T, int D, int C, bool PERKEY, bool CKPT>
 void scan_launch(const PrefillArgs& a, int nvb, unsigned grid, hipStream_t s) {
     const dim3 block(ScanShape<C>::THREADS);
@@ -1385,19 +1441,8 @@ hipError_t prefill_prep_cfg(const PrefillArgs& a, hipStream_t s) {
 
 template <typename T, int D, int C, bool PERKEY>
 hipError_t prefill_scan_cfg(const PrefillArgs& a, hipStream_t s) {
-    // The value width per workgroup (NVB 16-column tiles) is the widest that still leaves
-    // at least one workgroup per CU: wider tiles share each chunk's operand stream over more
-    // columns (fewer bytes per column), narrower ones run more sequential chains at once.
     const int units = a.n_seqs * a.H;
-    int dev = 0, ncu = 256;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
-        (void)hipGetLastError();
-        ncu = 256;
-    }
-    const int64_t tiles = (int64_t)units * (D / SCAN_BV);
-    int nvb = 1;
-    while (nvb * 2 <= D / SCAN_BV && tiles / (nvb * 2) >= ncu) nvb *= 2;
+    const int nvb = scan_value_tiles(units, D, device_cu_count());
     const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * (D / (SCAN_BV * nvb)));
     if (a.ckpt_cu != nullptr) scan_launch<T, D, C, PERKEY, true>(a, nvb, grid, s);
     else scan_launch<T, D, C, PERKEY, false>(a, nvb, grid, s);
