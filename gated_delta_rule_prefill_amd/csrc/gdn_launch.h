@@ -20,8 +20,9 @@ namespace gdn {
 //   ut    [d_v][C]   f32 U (local residuals), 16-column tiles in MFMA accumulator order,
 //                        4 bytes per value in either of two formats (PrefillArgs::u32):
 //                        fp32, or for bf16 inputs bf16 values in the first half of the
-//                        section and their rounding residuals (x 2^16, e5m2) in the third
-//                        quarter (ul). E = U - W S cancels, so U stays close to fp32.
+//                        section and their rounding residuals (int8 fractions of the bf16
+//                        ulp) in the third quarter (ul). E = U - W S cancels, so U stays
+//                        close to fp32.
 //   decay [d_k]      f32 e^{G_C} per key channel
 struct PrefillWs {
     int32_t* chunk_info;   // [max_chunks][4]: seq, token start, length, 0

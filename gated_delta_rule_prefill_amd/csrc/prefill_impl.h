@@ -153,12 +153,14 @@ struct Frag {
 
 // U (local residuals) is stored in the scan's accumulator order at close to fp32 precision:
 // E = U - W S cancels, so a rounding of U is an error relative to U rather than to the
-// small residual. Either fp32 (u32), or, for bf16 inputs, U rounded to bf16 plus its
-// rounding residual, scaled by 2^16, in 8-bit e5m2 (3 bytes per value instead of 4): the
-// residual is at most 2^-8 |U| and e5m2 keeps it to 2^-3, so U comes back to ~2^-11
-// relative for 2^-20 <= |U| <= 224 (beyond, the clamped residual leaves plain bf16 accuracy).
-constexpr float U_RES_SCALE = 65536.f;
-constexpr float U_RES_UNSCALE = 1.f / 65536.f;
+// small residual. Either fp32 (U32), or, for bf16 inputs, U rounded to bf16 (RNE) plus its
+// rounding residual as a signed 8-bit fraction of the bf16 value's own ulp: |r| <= ulp / 2,
+// q = rint(254 r / ulp) in [-127, 127], so U comes back to about 2^-15 relative at any
+// magnitude (3 bytes per value instead of 4). ulp = 2^(e - 7) for a bf16 value in
+// [2^e, 2^(e+1)); it is applied with v_ldexp, so no division is needed.
+__device__ __forceinline__ int u_res_exp(float hi) {  // e - 7 of the bf16 value hi
+    return ((__float_as_int(hi) >> 23) & 0xFF) - 127 - 7;
+}
 template <typename T>
 __device__ __forceinline__ void store_u(const PrefillWs& ws, bool u32, size_t idx,
                                         const float v[4]);
@@ -175,15 +177,18 @@ __device__ __forceinline__ void store_u<bf16>(const PrefillWs& ws, bool u32, siz
         return;
     }
     store4<bf16>(reinterpret_cast<bf16*>(ws.ut) + idx, v);
-    float r[4];
+    uint32_t p = 0;
 #pragma unroll
     for (int e = 0; e < 4; e++) {
-        const float res = v[e] - (float)(bf16)v[e];  // exact in fp32
-        r[e] = __builtin_amdgcn_fmed3f(res * U_RES_SCALE, 57344.f, -57344.f);
+        const float hi = (float)(bf16)v[e];  // the stored value
+        const float r = v[e] - hi;           // exact in fp32
+        // zero and bf16 denormals give a huge negative exponent: r is then 0 or below any
+        // contribution that matters, and the scaled value is clamped anyway
+        const float f = __builtin_amdgcn_ldexpf(r, -u_res_exp(hi)) * 254.f;
+        const int q = (int)__builtin_amdgcn_fmed3f(rintf(f), 127.f, -127.f);
+        p |= (uint32_t)(q & 0xFF) << (8 * e);
     }
-    int p = __builtin_amdgcn_cvt_pk_bf8_f32(r[0], r[1], 0, false);
-    p = __builtin_amdgcn_cvt_pk_bf8_f32(r[2], r[3], p, true);
-    *reinterpret_cast<int*>(ws.ul + idx) = p;
+    *reinterpret_cast<uint32_t*>(ws.ul + idx) = p;
 }
 // The reader knows the format at compile time (the scan's tile width decides it; a runtime
 // branch inside the scan's prefetch sequence cost 17-20 % on the wide-tile scans).
@@ -194,10 +199,11 @@ __device__ __forceinline__ void load_u(const PrefillWs& ws, size_t idx, float ou
     } else {
         load4<bf16>(reinterpret_cast<const bf16*>(ws.ut) + idx, out);
         const int p = *reinterpret_cast<const int*>(ws.ul + idx);
-        out[0] += __builtin_amdgcn_cvt_f32_bf8(p, 0) * U_RES_UNSCALE;
-        out[1] += __builtin_amdgcn_cvt_f32_bf8(p, 1) * U_RES_UNSCALE;
-        out[2] += __builtin_amdgcn_cvt_f32_bf8(p, 2) * U_RES_UNSCALE;
-        out[3] += __builtin_amdgcn_cvt_f32_bf8(p, 3) * U_RES_UNSCALE;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int q = (p << (24 - 8 * e)) >> 24;  // sign-extended byte e
+            out[e] += __builtin_amdgcn_ldexpf((float)q * (1.f / 254.f), u_res_exp(out[e]));
+        }
     }
 }
 

@@ -259,3 +259,26 @@ def test_kda_varlen_conv_fused_all_heads():
     say(f"   rel err o={e_o:.2e} S={e_s:.2e}")
     assert np.isfinite(o.float().numpy()).all()
     assert e_o <= 1e-2 and e_s <= 1e-2
+
+
+@pytest.mark.parametrize("lengths,H", [([8192], 2), ("many", 4)])
+def test_value_scale_equivariance(lengths, H):
+    """With a zero initial state the outputs and final states are linear in v, and every
+    operation on v-derived quantities (the fp32 arithmetic, RNE to bf16, U kept in fp32 or
+    as bf16 plus a residual measured in the bf16 value's own ulp) commutes with scaling by a
+    power of two. So v * 2^10 and v * 2^-10 must give outputs and states scaled exactly, bit
+    for bit. 'many' is 64 ragged sequences, whose scan reads U as bf16 plus the residual;
+    one long sequence reads U in fp32."""
+    if lengths == "many":
+        lengths = torch.randint(1, 200, (64,), generator=torch.Generator().manual_seed(71)).tolist()
+    say(f"case value-scale equivariance, {len(lengths)} sequences, H={H}")
+    x = inputs.random_prefill(72, lengths, H=H, dk=128, dv=128)
+    o, pool = run_prefill(x)
+    o_ref, s_ref = oracle_prefill(x)
+    _check(x, o, pool, o_ref, s_ref)
+    v0 = x.v
+    for sc in (2.0 ** 10, 2.0 ** -10):
+        x.v = (v0.float() * sc).to(v0.dtype)
+        o2, pool2 = run_prefill(x)
+        assert torch.equal(o2.float(), o.float() * sc)
+        assert torch.equal(pool2, pool * sc)
