@@ -18,11 +18,13 @@ namespace gdn {
 //                        fragments (K-step columns) that start right of a row's 16-token
 //                        block are all zero, never written and never read
 //   ut    [d_v][C]   f32 U (local residuals), 16-column tiles in MFMA accumulator order,
-//                        4 bytes per value in either of two formats (PrefillArgs::u32):
-//                        fp32, or for bf16 inputs bf16 values in the first half of the
-//                        section and their rounding residuals (int8 fractions of the bf16
-//                        ulp) in the third quarter (ul). E = U - W S cancels, so U stays
-//                        close to fp32.
+//                        when the prep forms U (PrefillArgs::u_ws; E = U - W S cancels,
+//                        so U stays fp32). Otherwise the same space holds, as three
+//                        sections over all units:
+//     rr  [C][CP]    e   (R - I) diag(beta)  row-major fragments, only those at or left of
+//                        each row's diagonal block written
+//     beta [C]       f32 beta
+//     vbuf [C][d_v]  e   conv-fused prefill: v after the convolution, token rows
 //   decay [d_k]      f32 e^{G_C} per key channel
 struct PrefillWs {
     int32_t* chunk_info;   // [max_chunks][4]: seq, token start, length, 0
@@ -31,8 +33,11 @@ struct PrefillWs {
     void* qin;
     void* kgt;
     void* mmat;
-    void* ut;
-    uint8_t* ul;           // residual bytes of U (bf16 inputs), inside the ut section
+    void* ut;              // U in fp32, in the scan's accumulator order (when the prep forms U)
+    void* rr;              // (R - I) diag(beta), fragment-major A operand   (when the scan
+    float* beta;           // beta per token of the unit                      forms U; these
+    void* vbuf;            // conv-fused prefill: v rows after the convolution three share U's
+                           //                                                  section)
     float* decay;
     void* dump;            // scratch words that absorb stores of lanes past a sequence end
     int64_t max_chunks;
@@ -63,14 +68,12 @@ struct PrefillArgs {
     const float* conv_w;
     void* conv_state;
     int conv_width;
-    // U format in the workspace, chosen by the host for the whole call: 1 = fp32; 0 = bf16
-    // value plus an 8-bit residual (bf16 inputs only). The scan's 16-column tiles are bound
-    // by their per-chunk dependency chain, where decoding the residual would lengthen each
-    // chunk step; wider tiles are bound by reading the workspace, where 3 bytes per value
-    // instead of 4 shorten it. The prep stores in this format; the scan reads the format
-    // its compile-time tile width implies, so u32 must equal (scan_value_tiles(...) == 1)
-    // for bf16 inputs.
-    int u32;
+    // Who forms U = R diag(beta) V, chosen by the host for the whole call from the scan's
+    // tile width (scan_tiles): 1 = the prep, stored in fp32 (16-column scan tiles, bound by
+    // their per-chunk dependency chain, where the scan's own loads of v rows from HBM
+    // stalled each chunk); 0 = the scan, from v, (R - I) diag(beta) and beta (wider tiles,
+    // bound by reading the workspace: the prep then neither reads v nor writes U).
+    int u_ws;
     PrefillWs ws;
 };
 
@@ -91,6 +94,13 @@ inline int device_cu_count() {
         ncu = 256;
     }
     return ncu;
+}
+// The scan's value-tile width for a call (in 16-column tiles), capped per element type: an
+// fp32 scan at 128 columns would need more LDS than a CU has (S^T, E^T and V^T slices).
+inline int scan_tiles(int dtype, int64_t units, int dv) {
+    const int cap = dtype == 1 ? 8 : 4;
+    const int nvb = scan_value_tiles(units, dv, device_cu_count());
+    return nvb < cap ? nvb : cap;
 }
 
 // Chunk length / key dim rounded up to the MFMA contraction step of the element type

@@ -1,5 +1,7 @@
 // Prefill front end: per-sequence chunk table (device-side, no host synchronisation),
 // workspace carving and dispatch to the element-type instantiations.
+#include <algorithm>
+
 #include "gdn_common.h"
 #include "gdn_launch.h"
 
@@ -60,8 +62,13 @@ size_t prefill_ws_layout(int dtype, int H, int dk, int dv, int chunk, int n_seqs
     const size_t o_q = off;   off = align256(off + units * chunk * dkp * e);
     const size_t o_k = off;   off = align256(off + units * dk * cp * e);
     const size_t o_m = off;   off = align256(off + units * chunk * cp * e);
-    // U: 4 bytes per value (fp32, or bf16 values then 8-bit residuals for bf16 inputs)
-    const size_t o_u = off;   off = align256(off + units * dv * chunk * 4);
+    // U (fp32) when the prep forms it; otherwise, in the same space, (R - I) diag(beta),
+    // beta and (conv-fused prefill only; the plain prefill reads v itself) v after the
+    // convolution
+    const size_t s_r = align256(units * chunk * cp * e);
+    const size_t s_b = align256(units * chunk * 4);
+    const size_t s_v = align256(units * chunk * dv * e);
+    const size_t o_u = off;   off = align256(off + std::max(units * dv * chunk * 4, s_r + s_b + s_v));
     const size_t o_d = off;   off = align256(off + units * dk * 4);
     const size_t o_x = off;   off = align256(off + 256 * 4);
     if (out != nullptr) {
@@ -73,7 +80,9 @@ size_t prefill_ws_layout(int dtype, int H, int dk, int dv, int chunk, int n_seqs
         out->kgt = b + o_k;
         out->mmat = b + o_m;
         out->ut = b + o_u;
-        out->ul = reinterpret_cast<uint8_t*>(b + o_u + units * dv * chunk * 2);
+        out->rr = b + o_u;
+        out->beta = reinterpret_cast<float*>(b + o_u + s_r);
+        out->vbuf = b + o_u + s_r + s_b;
         out->decay = reinterpret_cast<float*>(b + o_d);
         out->dump = b + o_x;
         out->max_chunks = max_chunks;
@@ -86,9 +95,7 @@ hipError_t launch_prefill(const PrefillArgs& args, hipStream_t s) {
     // empty sequence list is a no-op
     if (args.n_seqs == 0) return hipSuccess;
     PrefillArgs a = args;
-    // U in fp32 where the scan runs 16-column tiles, else bf16 plus a residual (bf16 inputs)
-    a.u32 = a.dtype != 1 ||
-            scan_value_tiles((int64_t)a.n_seqs * a.H, a.dv, device_cu_count()) == 1;
+    a.u_ws = scan_tiles(a.dtype, (int64_t)a.n_seqs * a.H, a.dv) == 1;
     (void)hipGetLastError();  // report only errors raised by this call's launches
     const bool b16 = a.dtype == 1;
     if (a.conv_width == 0) return b16 ? launch_prefill_bf16(a, s) : launch_prefill_f32(a, s);

@@ -14,19 +14,21 @@
 //
 // Work split on MI355X:
 //   prep  (grid: chunks x heads, fully parallel): everything that depends only on the chunk
-//         — G, A and M on MFMA, R by blocked substitution in fp32, U and W on MFMA — written
-//         once to a workspace in MFMA-operand-ready layouts (-W and Q_in row-major, K_g^T
-//         key-major, M row-major, U in the scan's accumulator order at close to fp32
-//         precision, e^{G_C}).
+//         — G, A and M on MFMA, R by blocked substitution in fp32, W on MFMA — written once
+//         to a workspace in MFMA-operand-ready layouts (-W and Q_in row-major, K_g^T
+//         key-major, M row-major, e^{G_C}); U = R diag(beta) V either on MFMA here (fp32,
+//         in the scan's accumulator order) or, for the scan's wider value tiles, by the
+//         scan itself from v, with (R - I) diag(beta) and beta from the prep.
 //   scan  (grid: sequences x heads x d_v/16 value tiles, serial over a sequence's chunks):
-//         the only sequential part. A 16-column slice of the fp32 state lives in MFMA
-//         accumulators across the whole sequence; per chunk
+//         the only sequential part. A 16- to 128-column slice of the fp32 state lives in
+//         MFMA accumulators across the whole sequence; per chunk
 //           E = U - W S,  O = Q_in S + M E,  S <- Diag(e^{G_C}) S + K_g^T E
 //         with E and O rows on separate waves and each wave's operands of the next chunk
 //         prefetched into its registers during the current one.
 //         The value tiles of one (sequence, head) are placed on the same XCD so the shared
 //         per-chunk operands are served from that XCD's L2.
 #pragma once
+#include <algorithm>
 #include <climits>
 #include <type_traits>
 
@@ -151,62 +153,6 @@ struct Frag {
     }
 };
 
-// U (local residuals) is stored in the scan's accumulator order at close to fp32 precision:
-// E = U - W S cancels, so a rounding of U is an error relative to U rather than to the
-// small residual. Either fp32 (U32), or, for bf16 inputs, U rounded to bf16 (RNE) plus its
-// rounding residual as a signed 8-bit fraction of the bf16 value's own ulp: |r| <= ulp / 2,
-// q = rint(254 r / ulp) in [-127, 127], so U comes back to about 2^-15 relative at any
-// magnitude (3 bytes per value instead of 4). ulp = 2^(e - 7) for a bf16 value in
-// [2^e, 2^(e+1)); it is applied with v_ldexp, so no division is needed.
-__device__ __forceinline__ int u_res_exp(float hi) {  // e - 7 of the bf16 value hi
-    return ((__float_as_int(hi) >> 23) & 0xFF) - 127 - 7;
-}
-template <typename T>
-__device__ __forceinline__ void store_u(const PrefillWs& ws, bool u32, size_t idx,
-                                        const float v[4]);
-template <>
-__device__ __forceinline__ void store_u<float>(const PrefillWs& ws, bool, size_t idx,
-                                               const float v[4]) {
-    store4<float>(reinterpret_cast<float*>(ws.ut) + idx, v);
-}
-template <>
-__device__ __forceinline__ void store_u<bf16>(const PrefillWs& ws, bool u32, size_t idx,
-                                              const float v[4]) {
-    if (u32) {
-        store4<float>(reinterpret_cast<float*>(ws.ut) + idx, v);
-        return;
-    }
-    store4<bf16>(reinterpret_cast<bf16*>(ws.ut) + idx, v);
-    uint32_t p = 0;
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-        const float hi = (float)(bf16)v[e];  // the stored value
-        const float r = v[e] - hi;           // exact in fp32
-        // zero and bf16 denormals give a huge negative exponent: r is then 0 or below any
-        // contribution that matters, and the scaled value is clamped anyway
-        const float f = __builtin_amdgcn_ldexpf(r, -u_res_exp(hi)) * 254.f;
-        const int q = (int)__builtin_amdgcn_fmed3f(rintf(f), 127.f, -127.f);
-        p |= (uint32_t)(q & 0xFF) << (8 * e);
-    }
-    *reinterpret_cast<uint32_t*>(ws.ul + idx) = p;
-}
-// The reader knows the format at compile time (the scan's tile width decides it; a runtime
-// branch inside the scan's prefetch sequence cost 17-20 % on the wide-tile scans).
-template <typename T, bool U32>
-__device__ __forceinline__ void load_u(const PrefillWs& ws, size_t idx, float out[4]) {
-    if constexpr (U32 || sizeof(T) == 4) {
-        load4<float>(reinterpret_cast<const float*>(ws.ut) + idx, out);
-    } else {
-        load4<bf16>(reinterpret_cast<const bf16*>(ws.ut) + idx, out);
-        const int p = *reinterpret_cast<const int*>(ws.ul + idx);
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const int q = (p << (24 - 8 * e)) >> 24;  // sign-extended byte e
-            out[e] += __builtin_amdgcn_ldexpf((float)q * (1.f / 254.f), u_res_exp(out[e]));
-        }
-    }
-}
-
 // =====================================================================================
 // prep kernel
 // =====================================================================================
@@ -237,11 +183,11 @@ struct PrepSmem {
                 alignas(16) float ar[C][C + 1];  // A (strictly lower), then R = (I + A)^{-1}
                                                  // in place; the strictly upper part is
                                                  // merge scratch
-                alignas(16) T va[PERKEY ? 1 : DV][F::LDC];  // scalar gate: V^T,
-                                                            // written once R is complete
+                alignas(16) T va[PERKEY ? 1 : DV][F::LDC];  // scalar gate: V^T (when the
+                                                            // prep forms U), once R is done
             };
             alignas(16) T rs[C][F::LDC];     // R as an MFMA operand
-            alignas(16) T vt[PERKEY ? DV : 1][F::LDC];  // per-key gate: V^T
+            alignas(16) T vt[PERKEY ? DV : 1][F::LDC];  // per-key gate: V^T (prep forms U)
         } b;
     } u;
     // per-key conv: the weights, kept for V's convolution after P0 (the other members keep
@@ -313,6 +259,8 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
     extern __shared__ __align__(16) unsigned char smem_raw[];
     auto& sm = *reinterpret_cast<PrepSmem<T, DK, DV, C, PERKEY, CONV>*>(smem_raw);
     T (*const vt)[F::LDC] = PERKEY ? sm.u.b.vt : sm.u.b.va;
+    // who forms U (uniform over the grid): the prep (fp32, into the workspace) or the scan
+    const bool uws = a.u_ws != 0;
 
     // Unit mapping. Workgroups are dealt round-robin over the 8 XCDs (blockIdx % 8).
     // Without the convolution the heads of one chunk get consecutive ids within one XCD: a
@@ -431,11 +379,12 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
                 qf[kb] = MM::load(qg + c0);
             }
         }
+        // v only when the prep forms U; otherwise the scan reads it
 #pragma unroll
         for (int kb = 0; kb < NV; kb++) {
             const int c0 = kb * KB + g4 * KPL;
             vf[kb] = MM::zero();
-            if (rvalid && c0 < DV) vf[kb] = MM::load(vg + c0);
+            if (uws && rvalid && c0 < DV) vf[kb] = MM::load(vg + c0);
         }
     }
     constexpr int GP = PERKEY ? PF_THREADS / DK : 1;  // per-key gate: row segments per channel
@@ -492,6 +441,15 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
             }
             xf = rvalid ? out : MM::zero();  // rows past the chunk stay zero
     };
+    // v after the convolution to the workspace, where the scan forms U from it (rows past
+    // the chunk as zeros)
+    auto store_vrows = [&]() {
+        if (uws || !own) return;
+        T* vb = reinterpret_cast<T*>(a.ws.vbuf) + (u * C + row) * DV + g4 * KPL;
+#pragma unroll
+        for (int kb = 0; kb < NV; kb++)
+            if (kb * KB + g4 * KPL < DV) *reinterpret_cast<frag*>(vb + kb * KB) = vf[kb];
+    };
     if constexpr (CONV) {
 #pragma unroll
         for (int k = 0; k < NWL; k++) {
@@ -507,6 +465,7 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
             if (PERKEY && f >= 2 * NK) break;
             conv_frag(f);
         }
+        if constexpr (!PERKEY) store_vrows();
     }
 
     // L2 norm of q and k rows: a row lives in the 4 lane groups sharing r16
@@ -551,7 +510,10 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
             *reinterpret_cast<frag*>(&sm.u.a.ks[off]) = kf[kb];
         }
     }
-    if (tid < C) sm.bs[tid] = bval;
+    if (tid < C) {
+        sm.bs[tid] = bval;
+        if (!uws) a.ws.beta[u * C + tid] = bval;
+    }
     if constexpr (PERKEY) {
         float run = 0.f;
 #pragma unroll
@@ -800,6 +762,7 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
         if (w == 0 && own) {
 #pragma unroll
             for (int f = 2 * NK; f < 2 * NK + NV; f++) conv_frag(f);
+            store_vrows();
         }
     }
     lds_barrier();  // #2: keys and gates are dead from here on
@@ -849,10 +812,12 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
         if (w != 0 && own) {
 #pragma unroll
             for (int f = 2 * NK; f < 2 * NK + NV; f++) conv_frag(f);
+            store_vrows();
         }
     }
-    // V^T: lane (g4, n) gets V[16w + 4 g4 + e][16 vb + n] (exact in the element type), plus
-    // zero padding tokens; per-key gate here, scalar gate after the merges (over A/R)
+    // V^T (when the prep forms U): lane (g4, n) gets V[16w + 4 g4 + e][16 vb + n] (exact in
+    // the element type), plus zero padding tokens; per-key gate here, scalar gate after the
+    // merges (over A/R)
     auto store_vt = [&]() {
         if (own) {
             const int t0 = w * 16 + g4 * 4;
@@ -871,7 +836,7 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
             }
         }
     };
-    if constexpr (PERKEY) store_vt();
+    if (PERKEY && uws) store_vt();
     // zeros: R above the diagonal blocks and in the padding columns
     for (int idx = tid; idx < C * (CP / 4); idx += PF_THREADS) {
         const int i = idx / (CP / 4), j0 = (idx % (CP / 4)) * 4;
@@ -938,14 +903,43 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
         }
     }
     lds_barrier();  // #6: R complete
-    if constexpr (!PERKEY) {
+    if (!PERKEY && uws) {  // uniform across the grid
         store_vt();     // A/R is dead: V^T goes over it
         lds_barrier();  // #7
     }
 
-    // ---------------------------------------- P4: -W (fragment-major) and U (scan order)
+    // ---------------------------------- P4: -W on MFMA, and U or the scan's operands for it
+    // U = R diag(beta) V = diag(beta) V + (R - I) diag(beta) V. R has a unit diagonal, so
+    // beta_i V_i is U's leading term: it enters the accumulator in fp32 from the exact V, and
+    // only the small off-diagonal part goes through rounded MFMA operands (rounding
+    // diag(beta) V itself was the largest single error source of the outputs in the element
+    // type). Either the prep forms U here (fp32, in the scan's accumulator order), or the
+    // scan forms it the same way from v as it reads it: the prep then stores
+    // (R - I) diag(beta) as the A operand of that product (only the fragments at or left of
+    // each row's diagonal block; the others are zero and never read) and beta.
     {
         const int kq = g4 * KPL;
+        if (own && !uws) {
+            T* rr = reinterpret_cast<T*>(a.ws.rr) + u * C * CP;
+            const int mb = w, irow = row;
+#pragma unroll
+            for (int kb = 0; kb < CP / KB; kb++) {
+                if (kb * KB >= 16 * (mb + 1)) continue;
+                const auto fr = MM::load(&sm.u.b.rs[irow][kb * KB + kq]);
+                frag ra;
+#pragma unroll
+                for (int e = 0; e < KPL; e++) {
+                    const int j = kb * KB + kq + e;
+                    float x;
+                    if constexpr (KPL == 1) x = to_f32(fr);
+                    else x = to_f32(fr[e]);
+                    x = (j == irow || j >= C) ? 0.f : x * sm.bs[j];
+                    if constexpr (KPL == 1) ra = from_f32<T>(x);
+                    else ra[e] = from_f32<T>(x);
+                }
+                *reinterpret_cast<frag*>(rr + ((mb * (CP / KB) + kb) * 64 + lane) * KPL) = ra;
+            }
+        }
         T* wneg = reinterpret_cast<T*>(a.ws.wneg) + u * C * DKP;
         if constexpr (DKP > DK) {
             for (int idx = tid; idx < C * ((DKP - DK) / 4); idx += PF_THREADS) {
@@ -954,36 +948,32 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
                 Frag<T>::template store_run<4>(wneg, i, c0, DKP, z);
             }
         }
-        const size_t ut = u * DV * C;  // this unit's U values
         constexpr int NW = (DK / 16) * NB;  // W^T tiles: (channel block, token block)
-        constexpr int NU = NB * (DV / 16);  // U tiles: (token block, value block)
-        // tile order keeps the R fragments of one token block on one wave; the U tiles' A
-        // operand (R - I) diag(beta) of that token block is formed once and reused
-        frag ua[CP / KB];
-        int ua_mb = -1;
-        for (int t = w; t < NW + NU; t += PF_WAVES) {
+        for (int t = w; t < NW; t += PF_WAVES) {
             f32x4 acc = zero4();
-            if (t < NW) {
-                const int nb = t % NB, mb = t / NB;  // nb: token block, mb: channel block
+            const int nb = t % NB, mb = t / NB;  // nb: token block, mb: channel block
 #pragma unroll
-                for (int kb = 0; kb < CP / KB; kb++) {
-                    auto fa = MM::load(&sm.kint[mb * 16 + r16][kb * KB + kq]);
-                    auto fb = MM::load(&sm.u.b.rs[nb * 16 + r16][kb * KB + kq]);
-                    acc = MM::mma(fa, fb, acc);
-                }
-                // lane: W^T[ch = mb*16 + 4*g4 + e][i = nb*16 + r16]
-                float nw[4];
+            for (int kb = 0; kb < CP / KB; kb++) {
+                auto fa = MM::load(&sm.kint[mb * 16 + r16][kb * KB + kq]);
+                auto fb = MM::load(&sm.u.b.rs[nb * 16 + r16][kb * KB + kq]);
+                acc = MM::mma(fa, fb, acc);
+            }
+            // lane: W^T[ch = mb*16 + 4*g4 + e][i = nb*16 + r16]
+            float nw[4];
 #pragma unroll
-                for (int e = 0; e < 4; e++) nw[e] = -acc[e];
-                Frag<T>::template store_run<4>(wneg, nb * 16 + r16, mb * 16 + g4 * 4, DKP, nw);
-            } else {
-                const int tt = t - NW;
-                const int mb = tt % NB, nb = tt / NB;  // mb: token block, nb: value block
-                // U = R diag(beta) V = diag(beta) V + (R - I) diag(beta) V. R has a unit
-                // diagonal, so beta_i V_i is U's leading term: it enters the accumulator in
-                // fp32 from the exact V, and only the small off-diagonal part goes through
-                // rounded MFMA operands (rounding diag(beta) V itself was the largest single
-                // error source of the outputs in the element type)
+            for (int e = 0; e < 4; e++) nw[e] = -acc[e];
+            Frag<T>::template store_run<4>(wneg, nb * 16 + r16, mb * 16 + g4 * 4, DKP, nw);
+        }
+        if (uws) {
+            float* ut = reinterpret_cast<float*>(a.ws.ut) + u * DV * C;
+            constexpr int NU = NB * (DV / 16);  // U tiles: (token block, value block)
+            // tile order keeps the R fragments of one token block on one wave; the tiles'
+            // A operand (R - I) diag(beta) of that token block is formed once and reused
+            frag ua[CP / KB];
+            int ua_mb = -1;
+            for (int t = w; t < NU; t += PF_WAVES) {
+                const int mb = t % NB, nb = t / NB;  // mb: token block, nb: value block
+                f32x4 acc;
                 {
                     float v4[4];
                     load4<T>(&vt[nb * 16 + r16][mb * 16 + 4 * g4], v4);
@@ -1011,12 +1001,12 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
                 }
 #pragma unroll
                 for (int kb = 0; kb < CP / KB; kb++) {
-                    auto fb = MM::load(&vt[nb * 16 + r16][kb * KB + kq]);
-                    acc = MM::mma(ua[kb], fb, acc);
+                    if (kb * KB >= 16 * (mb + 1)) continue;  // (R - I) is zero there
+                    acc = MM::mma(ua[kb], MM::load(&vt[nb * 16 + r16][kb * KB + kq]), acc);
                 }
                 // lane: U[i = mb*16 + 4*g4 + e][v = nb*16 + r16], scan accumulator order
                 float uu[4] = {acc[0], acc[1], acc[2], acc[3]};
-                store_u<T>(a.ws, a.u32 != 0, ut + ((size_t)(nb * NB + mb) * 64 + lane) * 4, uu);
+                store4<float>(ut + ((size_t)(nb * NB + mb) * 64 + lane) * 4, uu);
             }
         }
     }
@@ -1029,14 +1019,20 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
 // blocks); each wave keeps one role for the whole sequence:
 //   E wave w < NB      E rows of token block w:  E = U + (-W) S, and the state row blocks
 //                      rb = w + j NB of the fp32 state slice, kept in its MFMA accumulators:
-//                      S <- Diag(e^{G_C}) S + K_g^T E
-//   O wave w >= NB     O rows of token block w - NB: O = Q_in S + M E, and the output stores
-// Per chunk: barrier (S^T in LDS) -> E, Q_in S -> barrier (E in LDS) -> state update and
-// S^T back to LDS (E waves) while the O waves finish M E and store O. Each wave prefetches
-// only its own operands of the next chunk into registers (-W, U and K_g^T rows, or Q_in
-// and M): a single wave pulls only a small share of a CU's vector-memory bandwidth, so the
-// per-chunk operand stream is spread over all waves of the workgroup. The split keeps the
-// two roles' work after the E barrier about equal (measured per phase with cycle stamps).
+//                      S <- Diag(e^{G_C}) S + K_g^T E; then U of its token block for the
+//                      next chunk, U = diag(beta) V + ((R - I) diag(beta)) V, from V^T in LDS
+//   O wave w >= NB     O rows of token block w - NB: O = Q_in S + M E, and the output
+//                      stores; V^T of its token block of the next chunk into LDS
+// Per chunk: barrier (S^T in LDS) -> E, Q_in S, next chunk's V^T -> barrier (E in LDS) ->
+// state update, S^T back to LDS and the next chunk's U (E waves) while the O waves finish
+// M E and store O. Each wave prefetches only its own operands of the next chunk into
+// registers (-W, K_g^T rows and (R - I) diag(beta), or Q_in, M and v rows): a single wave
+// pulls only a small share of a CU's vector-memory bandwidth, so the per-chunk operand
+// stream is spread over all waves of the workgroup. U never leaves the CU: forming it here
+// instead of in the prep saves the prep's read of v and the U round trip through HBM
+// (fp32, 4 bytes per value, against v's 2 for bf16). The E waves form it after issuing
+// their S^T stores, so its products run while those complete; in the output waves, whose
+// chunk step is the longer one, the same work lengthened every chunk.
 template <int C>
 struct ScanShape {
     static constexpr int NB = C / 16;
@@ -1056,21 +1052,62 @@ struct ScanOps {
     // with RB a multiple of the E-wave count every E wave owns full row blocks and the loop
     // stays branch-free (the compiler then waits only for the operands it needs)
     static constexpr bool RB_FULL = RB % NB == 0;
+    static constexpr int NVF = (SCAN_BV * NVB + F::KB - 1) / F::KB;  // v row fragments
     frag a[NK];                    // -W rows (E wave) or Q_in rows (O wave)
     frag am[EROLE ? 1 : NK2];      // M rows (O wave)
-    f32x4 u[NVB];                  // U of the token block per value tile (E wave)
     frag ak[EROLE ? RBW : 1][NK2]; // K_g^T rows of the wave's state row blocks (E wave)
     f32x4 dec[PERKEY ? RBW : 1];   // per key: e^{G_C} of the lane's 4 state rows
     float dec0;                    // scalar gate: e^{G_C}
+    // E wave: with 16-column tiles U of the token block, formed by the prep; with wider
+    // ones the next chunk's (R - I) diag(beta) rows and beta of the lane's 4 accumulator rows
+    f32x4 u;
+    frag ar[EROLE ? NK2 : 1];
+    f32x4 bt;
 };
+
+// Every lane issues every load below (a lane without a row reads the first element of the
+// source and drops it; fragments right of the diagonal block, which are zero, reload the
+// first one, a cache hit), so the number of loads per chunk is fixed: the compiler's wait
+// counts then stay exact, where skipped loads made it wait for the next chunk's prefetches
+// as well.
+// The next chunk's U operands of token block mb for an E wave: (R - I) diag(beta) rows and
+// beta.
+template <typename T, int DK, int DV, int C, bool PERKEY, int NVB>
+__device__ __forceinline__ void scan_load_u_in(ScanOps<T, DK, DV, C, PERKEY, true, NVB>& op,
+                                               const PrefillArgs& a, size_t un, int mb) {
+    using O = ScanOps<T, DK, DV, C, PERKEY, true, NVB>;
+    using F = PfCfg<T, DK, DV, C>;
+    using MM = typename F::MM;
+    const int lane = lane_id(), g = lane >> 4;
+    const T* rr = reinterpret_cast<const T*>(a.ws.rr) + un * C * F::CP;
+#pragma unroll
+    for (int kt = 0; kt < O::NK2; kt++)
+        op.ar[kt] = MM::load(Frag<T>::ptr(rr, mb, kt * F::KB < 16 * (mb + 1) ? kt : 0, F::CP, lane));
+    op.bt = *reinterpret_cast<const f32x4*>(a.ws.beta + un * C + mb * 16 + 4 * g);
+}
+// v rows of an O wave's token block as row fragments over the tile's columns; vrow is the
+// lane's row at the tile's first column, or null for a row past the sequence end.
+template <typename T, int NVF, int BV>
+__device__ __forceinline__ void scan_load_v(typename Mma<T>::frag (&vr)[NVF], const T* vrow,
+                                            const T* vsafe) {
+    using MM = Mma<T>;
+    const int g = lane_id() >> 4;
+#pragma unroll
+    for (int f = 0; f < NVF; f++) {
+        const int col = f * MM::KB + g * MM::KPL;
+        const bool ok = vrow != nullptr && col < BV;
+        const auto x = MM::load(ok ? vrow + col : vsafe);
+        vr[f] = ok ? x : MM::zero();
+    }
+}
 
 // Operand loads of one chunk for one wave, in two parts issued at different points of the
 // previous chunk: part 0 (first needed: -W and U, or Q_in) and part 1 (K_g^T rows and decay,
 // or M). Issuing a wave's whole set at once stalls it on a full vector-memory queue.
 template <int PART, typename T, int DK, int DV, int C, bool PERKEY, bool EROLE, int NVB>
 __device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROLE, NVB>& op,
-                                              const PrefillArgs& a, size_t u, int vcol0,
-                                              int mb, int w) {
+                                              const PrefillArgs& a, size_t u, size_t un,
+                                              int vcol0, int mb, int w) {
     using O = ScanOps<T, DK, DV, C, PERKEY, EROLE, NVB>;
     using F = PfCfg<T, DK, DV, C>;
     using MM = typename F::MM;
@@ -1080,16 +1117,11 @@ __device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROL
     if constexpr (PART == 0) {
         if constexpr (EROLE) {
             const T* wneg = reinterpret_cast<const T*>(a.ws.wneg) + u * C * F::DKP;
-            const size_t ut = u * DV * C;  // this unit's U values
 #pragma unroll
             for (int kb = 0; kb < O::NK; kb++) op.a[kb] = MM::load(Frag<T>::ptr(wneg, mb, kb, F::DKP, lane));
-#pragma unroll
-            for (int v = 0; v < NVB; v++) {
-                float u4[4];
-                // 16-column tiles read fp32 U; wider ones bf16 plus the residual (the host
-                // chose the prep's store format by the same rule)
-                load_u<T, NVB == 1>(a.ws, ut + ((size_t)((vcol0 / 16 + v) * F::NB + mb) * 64 + lane) * 4, u4);
-                op.u[v] = f32x4{u4[0], u4[1], u4[2], u4[3]};
+            if constexpr (NVB == 1) {  // U of this lane's accumulator slots (fp32)
+                const float* ut = reinterpret_cast<const float*>(a.ws.ut) + u * DV * C;
+                op.u = *reinterpret_cast<const f32x4*>(ut + ((size_t)((vcol0 / 16) * F::NB + mb) * 64 + lane) * 4);
             }
         } else {
             const T* qin = reinterpret_cast<const T*>(a.ws.qin) + u * C * F::DKP;
@@ -1111,14 +1143,16 @@ __device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROL
                         op.dec[j] = *reinterpret_cast<const f32x4*>(dec + rb * 16 + (lane >> 4) * 4);
                 }
             }
+            if constexpr (NVB > 1) scan_load_u_in(op, a, un, mb);
         } else {
             const T* mm = reinterpret_cast<const T*>(a.ws.mmat) + u * C * CP;
             // M is lower triangular: the fragments starting right of token block mb would
-            // hold only zeros; the prep leaves them unwritten and they are neither loaded nor
-            // multiplied here (mb is uniform across the wave)
+            // hold only zeros; the prep leaves them unwritten and they are never multiplied
+            // here (mb is uniform across the wave). In their place the wave reloads its first
+            // fragment, to keep the number of loads fixed (see scan_load_u_in).
 #pragma unroll
             for (int kt = 0; kt < O::NK2; kt++)
-                if (kt * F::KB < 16 * (mb + 1)) op.am[kt] = MM::load(Frag<T>::ptr(mm, mb, kt, CP, lane));
+                op.am[kt] = MM::load(Frag<T>::ptr(mm, mb, kt * F::KB < 16 * (mb + 1) ? kt : 0, CP, lane));
         }
     }
 }
@@ -1142,12 +1176,14 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
     __shared__ __align__(16) T st[BV][F::LDK];   // S^T slice (MFMA B operand)
     __shared__ __align__(16) T et[BV][F::LDC];   // E^T slice
     __shared__ __align__(16) T ot[NB][NVB][16][16];  // O tiles of the O waves, row-major
+    constexpr bool UWS = NVB == 1;  // U from the workspace (formed by the prep)
+    __shared__ __align__(16) T vt[UWS ? 1 : BV][F::LDC];  // V^T slice of the next chunk
 
     // XCD-aware unit mapping: all value tiles of a (sequence, head) on one XCD
     const int id = blockIdx.x;
     const int xcd = id & 7, jj = id >> 3;
     const int unit = (jj / NVT) * 8 + xcd;
-    const int vt = jj % NVT;
+    const int vtile = jj % NVT;
     const int H = a.H;
     if (unit >= a.n_seqs * H) return;
     const int n = unit / H, h = unit - (unit / H) * H;
@@ -1156,7 +1192,7 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
     const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
     const int r16 = lane & 15, g = lane >> 4;
     const int kq = g * KPL;
-    const int vcol0 = vt * BV;
+    const int vcol0 = vtile * BV;
     // clamps keep inconsistent cu_seqlens inside the workspace and the token range
     int c_first, c_last1;
     if (a.n_seqs <= SEQ_INLINE_MAX) {
@@ -1195,9 +1231,11 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
             }
         }
     }
-    if constexpr (CP > C) {
-        for (int idx = threadIdx.x; idx < BV * (CP - C); idx += THREADS)
+    if constexpr (CP > C) {  // token padding of E^T and V^T stays zero
+        for (int idx = threadIdx.x; idx < BV * (CP - C); idx += THREADS) {
             et[idx / (CP - C)][C + idx % (CP - C)] = from_f32<T>(0.f);
+            if constexpr (!UWS) vt[idx / (CP - C)][C + idx % (CP - C)] = from_f32<T>(0.f);
+        }
     }
     if constexpr (F::DKP > DK) {  // padded state rows stay zero
         for (int idx = threadIdx.x; idx < BV * (F::DKP - DK); idx += THREADS)
@@ -1276,6 +1314,50 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
         } while (ck.chunk == c);
     };
 
+    // U of a chunk in two steps one barrier apart: each O wave writes V^T of its token block
+    // (exact in the element type) into vt; then, with all of V^T there, each E wave forms
+    // U = diag(beta) V + ((R - I) diag(beta)) V of its token block in registers.
+    const T* const vsrc = reinterpret_cast<const T*>(a.conv_width != 0 ? a.ws.vbuf : a.v);
+    const int mbo = w - NB;  // an O wave's token block
+    // the lane's v row of chunk cc (O waves) at the tile's first column; null past the end
+    auto vrow_of = [&](int cc) -> const T* {
+        const int tok0 = t_begin + (cc - c_begin) * C;
+        const int i = mbo * 16 + r16;
+        if (i >= min(C, t_end - tok0) || tok0 + i < 0) return nullptr;
+        if (a.conv_width != 0) return vsrc + ((size_t)(cc * H + h) * C + i) * DV + vcol0;
+        return vsrc + ((size_t)(tok0 + i) * H + h) * DV + vcol0;
+    };
+    frag idf[Ident<T>::N];
+    Ident<T>::make(idf);
+    using EOps = ScanOps<T, DK, DV, C, PERKEY, true, NVB>;
+    constexpr int NVF = EOps::NVF;
+    auto load_v = [&](frag (&vr)[NVF], int cc) { scan_load_v<T, NVF, BV>(vr, vrow_of(cc), vsrc); };
+    auto stage_vt = [&](const frag (&vr)[NVF]) {
+#pragma unroll
+        for (int vb = 0; vb < NVB; vb++) {
+            const f32x4 t4 = Ident<T>::template transpose<NVF>(vr, vb, idf);
+            float vv[4] = {t4[0], t4[1], t4[2], t4[3]};
+            store4<T>(&vt[vb * 16 + r16][mbo * 16 + 4 * g], vv);
+        }
+    };
+    f32x4 un[NVB];  // E wave: U of its token block, next chunk
+    auto form_u = [&](const EOps& op) {
+#pragma unroll
+        for (int v = 0; v < NVB; v++) {
+            float v4[4];
+            load4<T>(&vt[16 * v + r16][w * 16 + 4 * g], v4);
+            f32x4 acc;
+#pragma unroll
+            for (int e = 0; e < 4; e++) acc[e] = op.bt[e] * v4[e];
+#pragma unroll
+            for (int kt = 0; kt < EOps::NK2; kt++) {
+                if (kt * KB >= 16 * (w + 1)) continue;  // (R - I) is zero there
+                acc = MM::mma(op.ar[kt], MM::load(&vt[16 * v + r16][kt * KB + kq]), acc);
+            }
+            un[v] = acc;
+        }
+    };
+
     // the sequential pass for one role; both roles meet the same two barriers per chunk
     auto run = [&](auto role) {
         constexpr bool E = decltype(role)::value;
@@ -1308,19 +1390,24 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
         // operands of chunk c + 1 are loaded while chunk c is computed; prefetch indices are
         // clamped to the last chunk so every load is unconditional
         const int clast = c_end - 1;
-        auto ld = [&](auto part, O& op, int c) {
+        auto ld = [&](auto part, O& op, int c) {  // U operands: of the chunk after c
             scan_load_ops<decltype(part)::value, T, DK, DV, C, PERKEY, E, NVB>(
-                op, a, (size_t)min(c, clast) * H + h, vcol0, mb, w);
+                op, a, (size_t)min(c, clast) * H + h, (size_t)min(c + 1, clast) * H + h, vcol0,
+                mb, w);
         };
         using part0 = std::integral_constant<int, 0>;
         using part1 = std::integral_constant<int, 1>;
-        auto step = [&](const O& cur, O& nxt, int c) {
+        // O waves: v rows in a ring of two slots by chunk parity; at chunk c slot c holds
+        // V_{c+1}, which is staged and replaced by V_{c+3}: two chunks of latency cover the
+        // rows' trip from HBM (with one, the waves stalled on them every chunk)
+        auto step = [&](const O& cur, O& nxt, frag (&vq)[NVF], int c) {
             lds_barrier();  // st holds S_c^T
             ld(part1(), nxt, c + 1);
             sched_fence();
             f32x4 acc[NVB];
 #pragma unroll
-            for (int v = 0; v < NVB; v++) acc[v] = E ? cur.u[E ? v : 0] : zero4();
+            for (int v = 0; v < NVB; v++)
+                acc[v] = E ? (UWS ? cur.u : un[v]) : zero4();
 #pragma unroll
             for (int kb = 0; kb < O::NK; kb++)
 #pragma unroll
@@ -1334,8 +1421,11 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
                     float ev[4] = {acc[v][0], acc[v][1], acc[v][2], acc[v][3]};
                     store4<T>(&et[16 * v + r16][mb * 16 + 4 * g], ev);
                 }
+            } else if constexpr (!UWS) {
+                stage_vt(vq);  // V^T of chunk c + 1
+                load_v(vq, min(c + 3, clast));
             }
-            lds_barrier();  // et holds E_c
+            lds_barrier();  // et holds E_c, vt V_{c+1}^T
             ld(part0(), nxt, c + 1);
             sched_fence();
             if constexpr (!E) {
@@ -1373,23 +1463,42 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
                 }
             } else {
                 update_state(cur);
+                if constexpr (!UWS) form_u(cur);  // U_{c+1}, while the S^T stores complete
                 if constexpr (CKPT)
                     if (c == ck.chunk) ck_hit(c);
             }
         };
         O op0, op1;
+        frag vqa[NVF], vqb[NVF];
         ld(part0(), op0, c_begin);
         ld(part1(), op0, c_begin);
+        if constexpr (!E && !UWS) {
+            load_v(vqa, min(c_begin + 1, clast));
+            load_v(vqb, min(c_begin + 2, clast));
+        }
         // two chunks per iteration, then the odd one (a break in the middle of the body
         // compiles to a slower loop)
         int c = c_begin;
         for (; c + 1 < c_end; c += 2) {
-            step(op0, op1, c);
-            step(op1, op0, c + 1);
+            step(op0, op1, vqa, c);
+            step(op1, op0, vqb, c + 1);
         }
-        if (c < c_end) step(op0, op1, c);
+        if (c < c_end) step(op0, op1, vqa, c);
     };
     if (c_begin < c_end) {
+        if constexpr (!UWS) {  // U of the first chunk (the loop forms the later ones ahead)
+            if (!ewave) {
+                frag v0[NVF];
+                load_v(v0, c_begin);
+                stage_vt(v0);
+                lds_barrier();
+            } else {
+                EOps op;
+                scan_load_u_in(op, a, (size_t)c_begin * H + h, w);
+                lds_barrier();
+                form_u(op);
+            }
+        }
         if (w < NB) {
             // an E wave shares its SIMD with an O wave; issuing its instructions first keeps
             // the state chain, which every chunk waits on, ahead of the output work
@@ -1407,17 +1516,19 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
 // =====================================================================================
 __global__ void seq_first_kernel(const int32_t* cu, int n_seqs, int C, int32_t* seq_first);
 
-// nvb comes from scan_value_tiles, which never exceeds D / 16, so the instantiated tile
-// width always equals nvb (the ternaries only keep impossible combinations from being
-// instantiated); the U format the prep stored relies on that.
+// nvb comes from scan_tiles, which never exceeds D / 16 (nor 4 for fp32), so the
+// instantiated tile width always equals nvb (the ternaries only keep impossible
+// combinations from being instantiated): the grid was sized for it, and the prep chose who
+// forms U by it.
 template <typename T, int D, int C, bool PERKEY, bool CKPT>
 void scan_launch(const PrefillArgs& a, int nvb, unsigned grid, hipStream_t s) {
     const dim3 block(ScanShape<C>::THREADS);
+    constexpr int N8 = D >= 128 && sizeof(T) == 2 ? 8 : 1;  // see scan_tiles
     switch (nvb) {
         case 1: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, 1, CKPT>), dim3(grid), block, 0, s, a); break;
         case 2: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, D >= 32 ? 2 : 1, CKPT>), dim3(grid), block, 0, s, a); break;
         case 4: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, D >= 64 ? 4 : 1, CKPT>), dim3(grid), block, 0, s, a); break;
-        default: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, D >= 128 ? 8 : 1, CKPT>), dim3(grid), block, 0, s, a); break;
+        default: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, N8, CKPT>), dim3(grid), block, 0, s, a); break;
     }
 }
 
@@ -1448,7 +1559,7 @@ hipError_t prefill_prep_cfg(const PrefillArgs& a, hipStream_t s) {
 template <typename T, int D, int C, bool PERKEY>
 hipError_t prefill_scan_cfg(const PrefillArgs& a, hipStream_t s) {
     const int units = a.n_seqs * a.H;
-    const int nvb = scan_value_tiles(units, D, device_cu_count());
+    const int nvb = scan_tiles(a.dtype, units, D);
     const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * (D / (SCAN_BV * nvb)));
     if (a.ckpt_cu != nullptr) scan_launch<T, D, C, PERKEY, true>(a, nvb, grid, s);
     else scan_launch<T, D, C, PERKEY, false>(a, nvb, grid, s);

@@ -129,9 +129,11 @@ def test_prefill_workspace_too_small_and_sizing():
     dims = _dims(H=16, dk=128, dv=128)
     need = ctypes.c_size_t(0)
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(dims), 1, 8192, 64, ctypes.byref(need)) == 0
-    # 128 chunks x 16 heads x (W, Q_in, K_g^T, M in bf16 + U in 4 bytes per value (fp32, or
-    # bf16 with an 8-bit residual) + decay in fp32) + table
-    per = 64 * 128 * 2 * 2 + 64 * 128 * 4 + 64 * 64 * 2 + 128 * 64 * 2 + 128 * 4
+    # 128 chunks x 16 heads x (W, Q_in, K_g^T, M in bf16 + U in fp32, a space shared with
+    # the scan's own U operands ((R - I) diag(beta) and the conv-fused call's v rows in
+    # bf16, beta in fp32), + decay in fp32) + table
+    per = (64 * 128 * 2 * 2 + 128 * 64 * 2 + 64 * 64 * 2
+           + max(64 * 128 * 4, 64 * 64 * 2 + 64 * 4 + 64 * 128 * 2) + 128 * 4)
     assert need.value >= 128 * 16 * per
     assert need.value < 128 * 16 * per + 64 * 1024
     assert _prefill(dims, ws_bytes=need.value - 1, n=1, T=8192) == 5
