@@ -25,6 +25,8 @@ namespace gdn {
 //                        each row's diagonal block written
 //     beta [C]       f32 beta
 //     vbuf [C][d_v]  e   conv-fused prefill: v after the convolution, token rows
+//     qs   [C]       f32 raw-q scan (PrefillArgs::q_raw): s e^{G_i} / |q_i| per token,
+//                        in place of qin
 //   decay [d_k]      f32 e^{G_C} per key channel
 struct PrefillWs {
     int32_t* chunk_info;   // [max_chunks][4]: seq, token start, length, 0
@@ -36,8 +38,8 @@ struct PrefillWs {
     void* ut;              // U in fp32, in the scan's accumulator order (when the prep forms U)
     void* rr;              // (R - I) diag(beta), fragment-major A operand   (when the scan
     float* beta;           // beta per token of the unit                      forms U; these
-    void* vbuf;            // conv-fused prefill: v rows after the convolution three share U's
-                           //                                                  section)
+    void* vbuf;            // conv-fused prefill: v rows after the convolution these share
+    float* qs;             // raw-q scan: per-token row factor of q              U's section)
     float* decay;
     void* dump;            // scratch words that absorb stores of lanes past a sequence end
     int64_t max_chunks;
@@ -74,6 +76,13 @@ struct PrefillArgs {
     // stalled each chunk); 0 = the scan, from v, (R - I) diag(beta) and beta (wider tiles,
     // bound by reading the workspace: the prep then neither reads v nor writes U).
     int u_ws;
+    // 1 (scalar gate, q given, the scan forms U): the scan multiplies q itself by S and
+    // scales each output row by s e^{G_i} / |q_i| (the prep's qs) instead of reading Q_in,
+    // which the prep then does not write. A per-key gate scales q per channel, and the
+    // conv-fused prefill has no q in memory, so both keep Q_in; so do 16-column scan tiles,
+    // whose chunk step is bound by operand ingest (raw q rows arrive as 16 strided pieces
+    // per load instead of one contiguous fragment).
+    int q_raw;
     PrefillWs ws;
 };
 

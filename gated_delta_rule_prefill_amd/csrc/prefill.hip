@@ -63,12 +63,14 @@ size_t prefill_ws_layout(int dtype, int H, int dk, int dv, int chunk, int n_seqs
     const size_t o_k = off;   off = align256(off + units * dk * cp * e);
     const size_t o_m = off;   off = align256(off + units * chunk * cp * e);
     // U (fp32) when the prep forms it; otherwise, in the same space, (R - I) diag(beta),
-    // beta and (conv-fused prefill only; the plain prefill reads v itself) v after the
-    // convolution
+    // beta, (conv-fused prefill only; the plain prefill reads v itself) v after the
+    // convolution and (raw-q scan only) the output row factors
     const size_t s_r = align256(units * chunk * cp * e);
     const size_t s_b = align256(units * chunk * 4);
     const size_t s_v = align256(units * chunk * dv * e);
-    const size_t o_u = off;   off = align256(off + std::max(units * dv * chunk * 4, s_r + s_b + s_v));
+    const size_t s_q = align256(units * chunk * 4);
+    const size_t o_u = off;
+    off = align256(off + std::max(units * dv * chunk * 4, s_r + s_b + s_v + s_q));
     const size_t o_d = off;   off = align256(off + units * dk * 4);
     const size_t o_x = off;   off = align256(off + 256 * 4);
     if (out != nullptr) {
@@ -83,6 +85,7 @@ size_t prefill_ws_layout(int dtype, int H, int dk, int dv, int chunk, int n_seqs
         out->rr = b + o_u;
         out->beta = reinterpret_cast<float*>(b + o_u + s_r);
         out->vbuf = b + o_u + s_r + s_b;
+        out->qs = reinterpret_cast<float*>(b + o_u + s_r + s_b + s_v);
         out->decay = reinterpret_cast<float*>(b + o_d);
         out->dump = b + o_x;
         out->max_chunks = max_chunks;
@@ -96,6 +99,7 @@ hipError_t launch_prefill(const PrefillArgs& args, hipStream_t s) {
     if (args.n_seqs == 0) return hipSuccess;
     PrefillArgs a = args;
     a.u_ws = scan_tiles(a.dtype, (int64_t)a.n_seqs * a.H, a.dv) == 1;
+    a.q_raw = a.gate == 0 && a.conv_width == 0 && !a.u_ws;
     (void)hipGetLastError();  // report only errors raised by this call's launches
     const bool b16 = a.dtype == 1;
     if (a.conv_width == 0) return b16 ? launch_prefill_bf16(a, s) : launch_prefill_f32(a, s);

@@ -469,6 +469,7 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
     }
 
     // L2 norm of q and k rows: a row lives in the 4 lane groups sharing r16
+    float iqn = 1.f;  // 1 / |q| of the lane's row (1 without the norm)
     if (a.l2norm) {
         float sk = 0.f, sq = 0.f;
 #pragma unroll
@@ -488,6 +489,7 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
         sq += __shfl_xor(sq, 16, WAVE);
         sq += __shfl_xor(sq, 32, WAVE);
         const float ik = rsqrtf(sk + 1e-6f), iq = rsqrtf(sq + 1e-6f);
+        iqn = iq;
 #pragma unroll
         for (int kb = 0; kb < NK; kb++) {
             if constexpr (KPL == 1) {
@@ -547,25 +549,30 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
     frag idf[Ident<T>::N];
     Ident<T>::make(idf);
     if (own) {
-        // Q_in = s * Q * e^{G} -> workspace (fragment-major slot of this lane)
+        // Q_in = s * Q * e^{G} -> workspace (fragment-major slot of this lane); or, when the
+        // scan multiplies q itself, only the row factor s e^{G_i} / |q_i|
         T* qin = reinterpret_cast<T*>(a.ws.qin) + u * C * DKP;
         const float erow = PERKEY ? 1.f : sm.eg[row];
+        const bool qraw = !PERKEY && a.q_raw;
+        if (qraw && g4 == 0) a.ws.qs[u * C + row] = a.scale * erow * iqn;
+        if (!qraw) {
 #pragma unroll
-        for (int kb = 0; kb < NK; kb++) {
-            float vals[KPL];
+            for (int kb = 0; kb < NK; kb++) {
+                float vals[KPL];
 #pragma unroll
-            for (int e = 0; e < KPL; e++) {
-                const int ch = kb * KB + g4 * KPL + e;
-                float qv;
-                if constexpr (KPL == 1) qv = to_f32(qf[kb]);
-                else qv = to_f32(qf[kb][e]);
-                float f = erow;
-                if constexpr (PERKEY) f = ch < DK ? __expf(sm.u.a.gs[row][ch]) : 0.f;
-                vals[e] = a.scale * qv * f;
+                for (int e = 0; e < KPL; e++) {
+                    const int ch = kb * KB + g4 * KPL + e;
+                    float qv;
+                    if constexpr (KPL == 1) qv = to_f32(qf[kb]);
+                    else qv = to_f32(qf[kb][e]);
+                    float f = erow;
+                    if constexpr (PERKEY) f = ch < DK ? __expf(sm.u.a.gs[row][ch]) : 0.f;
+                    vals[e] = a.scale * qv * f;
+                }
+                T* dst = qin + ((w * NK + kb) * 64 + lane) * KPL;
+                if constexpr (KPL == 8) store8<T>(dst, vals);
+                else *dst = from_f32<T>(vals[0]);
             }
-            T* dst = qin + ((w * NK + kb) * 64 + lane) * KPL;
-            if constexpr (KPL == 8) store8<T>(dst, vals);
-            else *dst = from_f32<T>(vals[0]);
         }
         // K transposes: lane (g4, n) gets K[16w + 4 g4 + e][16 cb + n]; scaled twice into
         // (beta K_in)^T (LDS) and K_g^T (workspace, fragment-major)
@@ -1063,6 +1070,7 @@ struct ScanOps {
     f32x4 u;
     frag ar[EROLE ? NK2 : 1];
     f32x4 bt;
+    f32x4 qs;  // O wave reading q itself: the output row factors of the lane's 4 rows
 };
 
 // Every lane issues every load below (a lane without a row reads the first element of the
@@ -1104,10 +1112,12 @@ __device__ __forceinline__ void scan_load_v(typename Mma<T>::frag (&vr)[NVF], co
 // Operand loads of one chunk for one wave, in two parts issued at different points of the
 // previous chunk: part 0 (first needed: -W and U, or Q_in) and part 1 (K_g^T rows and decay,
 // or M). Issuing a wave's whole set at once stalls it on a full vector-memory queue.
-template <int PART, typename T, int DK, int DV, int C, bool PERKEY, bool EROLE, int NVB>
+// QRAW: the O waves read q rows (qrow: the lane's row, or null past the sequence end) and
+// the row factors instead of Q_in.
+template <int PART, bool QRAW, typename T, int DK, int DV, int C, bool PERKEY, bool EROLE, int NVB>
 __device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROLE, NVB>& op,
                                               const PrefillArgs& a, size_t u, size_t un,
-                                              int vcol0, int mb, int w) {
+                                              int vcol0, const T* qrow, int mb, int w) {
     using O = ScanOps<T, DK, DV, C, PERKEY, EROLE, NVB>;
     using F = PfCfg<T, DK, DV, C>;
     using MM = typename F::MM;
@@ -1123,6 +1133,16 @@ __device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROL
                 const float* ut = reinterpret_cast<const float*>(a.ws.ut) + u * DV * C;
                 op.u = *reinterpret_cast<const f32x4*>(ut + ((size_t)((vcol0 / 16) * F::NB + mb) * 64 + lane) * 4);
             }
+        } else if constexpr (QRAW) {  // q rows as they are, padded channels zero
+            const T* qsafe = reinterpret_cast<const T*>(a.q);
+#pragma unroll
+            for (int kb = 0; kb < O::NK; kb++) {
+                const int col = kb * F::KB + (lane >> 4) * F::KPL;
+                const bool ok = qrow != nullptr && col < DK;
+                const auto x = MM::load(ok ? qrow + col : qsafe);
+                op.a[kb] = ok ? x : MM::zero();
+            }
+            op.qs = *reinterpret_cast<const f32x4*>(a.ws.qs + u * C + mb * 16 + (lane >> 4) * 4);
         } else {
             const T* qin = reinterpret_cast<const T*>(a.ws.qin) + u * C * F::DKP;
 #pragma unroll
@@ -1162,7 +1182,9 @@ __device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROL
 // units to fill the chip with.
 // CKPT: also export the states a checkpoint list asks for (its own instantiation, so the
 // pass without checkpoints carries none of the bookkeeping).
-template <typename T, int DK, int DV, int C, bool PERKEY, int NVB, bool CKPT>
+// QRAW: the output waves multiply q itself by S and scale each row by the prep's factor
+// s e^{G_i} / |q_i| (scalar gate, q given, tiles wider than 16 columns; PrefillArgs::q_raw).
+template <typename T, int DK, int DV, int C, bool PERKEY, int NVB, bool CKPT, bool QRAW>
 __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(PrefillArgs a) {
     using F = PfCfg<T, DK, DV, C>;
     using MM = typename F::MM;
@@ -1320,6 +1342,13 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
     const T* const vsrc = reinterpret_cast<const T*>(a.conv_width != 0 ? a.ws.vbuf : a.v);
     const int mbo = w - NB;  // an O wave's token block
     // the lane's v row of chunk cc (O waves) at the tile's first column; null past the end
+    // the lane's q row of chunk cc (O waves); null past the end
+    auto qrow_of = [&](int cc) -> const T* {
+        const int tok0 = t_begin + (cc - c_begin) * C;
+        const int i = mbo * 16 + r16;
+        if (i >= min(C, t_end - tok0) || tok0 + i < 0) return nullptr;
+        return reinterpret_cast<const T*>(a.q) + ((size_t)(tok0 + i) * H + h) * DK;
+    };
     auto vrow_of = [&](int cc) -> const T* {
         const int tok0 = t_begin + (cc - c_begin) * C;
         const int i = mbo * 16 + r16;
@@ -1391,9 +1420,11 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
         // clamped to the last chunk so every load is unconditional
         const int clast = c_end - 1;
         auto ld = [&](auto part, O& op, int c) {  // U operands: of the chunk after c
-            scan_load_ops<decltype(part)::value, T, DK, DV, C, PERKEY, E, NVB>(
-                op, a, (size_t)min(c, clast) * H + h, (size_t)min(c + 1, clast) * H + h, vcol0,
-                mb, w);
+            constexpr int PART = decltype(part)::value;
+            const int cc = min(c, clast);
+            scan_load_ops<PART, QRAW, T, DK, DV, C, PERKEY, E, NVB>(
+                op, a, (size_t)cc * H + h, (size_t)min(c + 1, clast) * H + h, vcol0,
+                QRAW && !E && PART == 0 ? qrow_of(cc) : nullptr, mb, w);
         };
         using part0 = std::integral_constant<int, 0>;
         using part1 = std::integral_constant<int, 1>;
@@ -1421,7 +1452,13 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
                     float ev[4] = {acc[v][0], acc[v][1], acc[v][2], acc[v][3]};
                     store4<T>(&et[16 * v + r16][mb * 16 + 4 * g], ev);
                 }
-            } else if constexpr (!UWS) {
+            } else if constexpr (QRAW) {  // O = diag(s e^{G} / |q|) q S + M E
+#pragma unroll
+                for (int v = 0; v < NVB; v++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) acc[v][e] *= cur.qs[e];
+            }
+            if constexpr (!E && !UWS) {
                 stage_vt(vq);  // V^T of chunk c + 1
                 load_v(vq, min(c + 3, clast));
             }
@@ -1520,16 +1557,22 @@ __global__ void seq_first_kernel(const int32_t* cu, int n_seqs, int C, int32_t* 
 // instantiated tile width always equals nvb (the ternaries only keep impossible
 // combinations from being instantiated): the grid was sized for it, and the prep chose who
 // forms U by it.
-template <typename T, int D, int C, bool PERKEY, bool CKPT>
-void scan_launch(const PrefillArgs& a, int nvb, unsigned grid, hipStream_t s) {
+template <typename T, int D, int C, bool PERKEY, bool CKPT, bool QRAW>
+void scan_launch_q(const PrefillArgs& a, int nvb, unsigned grid, hipStream_t s) {
     const dim3 block(ScanShape<C>::THREADS);
     constexpr int N8 = D >= 128 && sizeof(T) == 2 ? 8 : 1;  // see scan_tiles
     switch (nvb) {
-        case 1: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, 1, CKPT>), dim3(grid), block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, D >= 32 ? 2 : 1, CKPT>), dim3(grid), block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, D >= 64 ? 4 : 1, CKPT>), dim3(grid), block, 0, s, a); break;
-        default: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, N8, CKPT>), dim3(grid), block, 0, s, a); break;
+        // 16-column tiles never read q themselves (PrefillArgs::q_raw)
+        case 1: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, 1, CKPT, false>), dim3(grid), block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, D >= 32 ? 2 : 1, CKPT, QRAW>), dim3(grid), block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, D >= 64 ? 4 : 1, CKPT, QRAW>), dim3(grid), block, 0, s, a); break;
+        default: hipLaunchKernelGGL((prefill_scan_kernel<T, D, D, C, PERKEY, N8, CKPT, QRAW>), dim3(grid), block, 0, s, a); break;
     }
+}
+template <typename T, int D, int C, bool PERKEY, bool CKPT>
+void scan_launch(const PrefillArgs& a, int nvb, unsigned grid, hipStream_t s) {
+    if (!PERKEY && a.q_raw) scan_launch_q<T, D, C, PERKEY, CKPT, !PERKEY>(a, nvb, grid, s);
+    else scan_launch_q<T, D, C, PERKEY, CKPT, false>(a, nvb, grid, s);
 }
 
 template <typename T, int D, int C, bool PERKEY, bool CONV>
