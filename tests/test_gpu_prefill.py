@@ -264,11 +264,10 @@ def test_kda_varlen_conv_fused_all_heads():
 @pytest.mark.parametrize("lengths,H", [([8192], 2), ("many", 4)])
 def test_value_scale_equivariance(lengths, H):
     """With a zero initial state the outputs and final states are linear in v, and every
-    operation on v-derived quantities (the fp32 arithmetic, RNE to bf16, U kept in fp32 or
-    as bf16 plus a residual measured in the bf16 value's own ulp) commutes with scaling by a
-    power of two. So v * 2^10 and v * 2^-10 must give outputs and states scaled exactly, bit
-    for bit. 'many' is 64 ragged sequences, whose scan reads U as bf16 plus the residual;
-    one long sequence reads U in fp32."""
+    operation on v-derived quantities (the fp32 arithmetic, RNE to bf16, U in fp32) commutes
+    with scaling by a power of two. So v * 2^10 and v * 2^-10 must give outputs and states
+    scaled exactly, bit for bit. 'many' is 64 ragged sequences, whose scan forms U itself
+    from v; one long sequence reads the prep's U."""
     if lengths == "many":
         lengths = torch.randint(1, 200, (64,), generator=torch.Generator().manual_seed(71)).tolist()
     say(f"case value-scale equivariance, {len(lengths)} sequences, H={H}")
