@@ -1393,23 +1393,22 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
         using O = ScanOps<T, DK, DV, C, PERKEY, E, NVB>;
         const int mb = E ? w : w - NB;
         auto update_state = [&](const O& cur) {  // E waves, after the E barrier
-            frag fe[NVB][O::NK2];
+            // one value tile at a time: its E^T fragments are live only for that tile
 #pragma unroll
-            for (int v = 0; v < NVB; v++)
+            for (int v = 0; v < NVB; v++) {
+                frag fe[O::NK2];
 #pragma unroll
-                for (int kt = 0; kt < O::NK2; kt++) fe[v][kt] = MM::load(&et[16 * v + r16][kt * KB + kq]);
+                for (int kt = 0; kt < O::NK2; kt++) fe[kt] = MM::load(&et[16 * v + r16][kt * KB + kq]);
 #pragma unroll
-            for (int j = 0; j < RBW; j++) {
-                const int rb = w + j * NB;
-                if (RB_FULL || rb < RB) {
-#pragma unroll
-                    for (int v = 0; v < NVB; v++) {
+                for (int j = 0; j < RBW; j++) {
+                    const int rb = w + j * NB;
+                    if (RB_FULL || rb < RB) {
 #pragma unroll
                         for (int e = 0; e < 4; e++)
                             acc_s[j][v][e] *= PERKEY ? cur.dec[PERKEY ? j : 0][e] : cur.dec0;
 #pragma unroll
                         for (int kt = 0; kt < O::NK2; kt++)
-                            acc_s[j][v] = MM::mma(cur.ak[j][kt], fe[v][kt], acc_s[j][v]);  // + K_g^T E
+                            acc_s[j][v] = MM::mma(cur.ak[j][kt], fe[kt], acc_s[j][v]);  // + K_g^T E
                         float sv[4] = {acc_s[j][v][0], acc_s[j][v][1], acc_s[j][v][2], acc_s[j][v][3]};
                         store4<T>(&st[16 * v + r16][rb * 16 + 4 * g], sv);
                     }
