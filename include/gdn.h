@@ -188,8 +188,12 @@ int gdn_prefill_chunked_ckpt(const gdn_dims_t* dims, const void* q, const void* 
  * go to memory; everything after is gdn_prefill_chunked. For sequence n, head h, channel c
  * of plane p (q, k, v), token t of the sequence and W = conv_width:
  *   q|k|v[t, h, c] = SiLU(sum_{j<W} w[ch, j] x[t - (W-1) + j, ch]),  ch = p H d + h d + c,
- * accumulated in fp32 from the oldest tap and rounded to dtype, bit-identical to
- * gdn_conv1d_silu(planes = 3) followed by gdn_prefill_chunked on its three planes. A token
+ * accumulated in fp32 from the oldest tap and rounded to dtype: the values
+ * gdn_conv1d_silu(planes = 3) writes, bit for bit. The outputs and states are those of
+ * gdn_prefill_chunked on its three planes bit for bit with a per-key gate, or when the
+ * call has few enough (sequence, head) pairs that its scan runs 16-column value tiles;
+ * otherwise, with a scalar gate, gdn_prefill_chunked multiplies the given q itself and
+ * scales each output row afterwards, and the two agree to rounding. A token
  * before the sequence start is the slot's conv history conv_state[slot, ch, W-1-m] (m tokens
  * before the start, m <= W-1) when conv_state is given and has_init[n] is nonzero, else 0.
  * After the call, conv_state[slot] (when given, for valid slots) holds the last W-1 inputs
