@@ -166,11 +166,13 @@ def bench_prefill_batch(steps, warmup):
         gdn.gdn_prefill_chunked(q, k, v, g, b, cu, x.chunk, pool, slots, scale=x.scale, o=o,
                                 workspace=ws)
 
-    ms, _ = ev_time(step, max(5, steps // 2), max(3, warmup // 10))
+    # median of per-call event pairs, after enough calls for the clocks to settle (as the
+    # headline figure)
+    ms, ms_mean, _ = ev_time_reps(step, max(10, steps // 2), max(10, warmup // 5))
     byts = traffic.prefill_bytes(T, H, d, d, 2, False, n, False)
     flops = traffic.prefill_flops([2048] * n, H, d, d, x.chunk)
     secs = ms * 1e-3
-    return dict(ms=ms, tokens=T, tokens_per_s=T / secs, GBps=byts / secs / 1e9,
+    return dict(ms=ms, ms_mean=ms_mean, tokens=T, tokens_per_s=T / secs, GBps=byts / secs / 1e9,
                 hbm_frac=byts / secs / traffic.HBM_PEAK_BPS, mfma_TFLOPs=flops / secs / 1e12,
                 mfma_frac_bf16=flops / secs / traffic.BF16_MFMA_PEAK,
                 workload="GDN chunked prefill batch, 32 sequences x 2048 tokens, H=16, d=128, "

@@ -50,6 +50,26 @@ def test_noalloc_prefill_two_calls_match_workspace_prefill(dtype, perkey):
         assert e_o <= BAR[dtype] and e_s <= BAR[dtype]
 
 
+@pytest.mark.parametrize("perkey", [False, True])
+def test_noalloc_prefill_wide_then_narrow_tiles(perkey):
+    """64 sequences x 4 heads (128-column scan tiles: the scan forms U and, for the scalar
+    gate, reads q itself), then a small call (16-column tiles: the prep forms U) over the same
+    scratch: each bit-identical to the workspace prefill and within the oracle's bar."""
+    lengths = torch.randint(0, 150, (64,), generator=torch.Generator().manual_seed(83)).tolist()
+    wide = inputs.random_prefill(84, lengths, H=4, dk=128, dv=128, perkey=perkey,
+                                 with_init=True)
+    narrow = inputs.random_prefill(85, [200, 7], H=2, dk=128, dv=128, perkey=perkey,
+                                   with_init=True)
+    for name, x in (("wide tiles", wide), ("then narrow tiles", narrow)):
+        say(f"case noalloc prefill bf16 perkey={perkey}: {name}")
+        (o_ws, p_ws), (o_na, p_na) = _both(x)
+        assert torch.equal(o_na, o_ws) and torch.equal(p_na, p_ws)
+        o_ref, s_ref = oracle_prefill(x)
+        e_o, e_s = oracle.rel_err(o_na, o_ref), oracle.rel_err(p_na, s_ref)
+        say(f"   bit-identical to the workspace prefill; vs oracle o={e_o:.2e} S={e_s:.2e}")
+        assert e_o <= BAR[torch.bfloat16] and e_s <= BAR[torch.bfloat16]
+
+
 def test_noalloc_prefill_rejects_oversized_call_without_touching_memory():
     say("case noalloc prefill beyond the scratch size")
     T, H, d = 8192, 16, 128
