@@ -2,7 +2,8 @@
 
 Each case draws its own combination of element type, head dim, chunk size, gate kind, L2 norm,
 head count, ragged sequence lengths (empty and 1-token sequences included), initial states
-and slot map, and runs one of three entry points: the plain chunked prefill, the prefill with
+and slot map (a second set with enough sequences for the scan's wide value tiles), and runs
+one of three entry points: the plain chunked prefill, the prefill with
 checkpoint exports, or the conv-fused prefill with conv histories. Outputs, final states,
 exported states and conv windows are compared with the oracle (the conv window, a copy, bit
 for bit). Bars: max|x - ref| / max|ref| <= 1e-4 (fp32 inputs) or 1e-2 (bf16 inputs).
@@ -20,16 +21,21 @@ from test_gpu_conv_prefill import extended, oracle_conv_prefill
 pytestmark = pytest.mark.gpu
 
 N_CASES = 48
+N_WIDE = 16
 
 
-def draw(seed):
+def draw(seed, wide=False):
+    """wide: enough (sequence, head) units (4 heads, 16-104 sequences) that the scan runs
+    32- to 128-column value tiles, where it forms U itself and, for the scalar gate with q
+    given, reads q itself."""
     r = np.random.default_rng(1000 + seed)
     dtype = [torch.float32, torch.bfloat16][r.integers(2)]
-    d = int(r.choice([16, 32, 64, 128]))
+    d = int(r.choice([32, 64, 128] if wide else [16, 32, 64, 128]))
     chunk = int(r.choice([16, 32, 64]))
     perkey = bool(r.integers(2))
-    H = int(r.integers(1, 4))
-    n = int(r.integers(1, 7))
+    H = 4 if wide else int(r.integers(1, 4))
+    n_min = -(-2 * 256 // (H * d // 16))
+    n = int(r.integers(n_min, n_min + 25)) if wide else int(r.integers(1, 7))
     lengths = [int(x) for x in r.choice([0, 1, 2, 3, 5, 17, 40, 64, 65, 100, 130, 200], size=n)]
     if sum(lengths) == 0:
         lengths[0] = 33
@@ -48,11 +54,23 @@ def draw(seed):
 
 @pytest.mark.parametrize("seed", range(N_CASES))
 def test_sweep_vs_oracle(seed):
-    c = draw(seed)
+    _run_case(draw(seed), seed)
+
+
+@pytest.mark.parametrize("seed", range(N_WIDE))
+def test_sweep_wide_tiles_vs_oracle(seed):
+    c = draw(500 + seed, wide=True)
+    n, d = len(c["lengths"]), c["d"]
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    assert n * c["H"] * (d // 16) // 2 >= ncu  # at least 32-column scan tiles
+    _run_case(c, 500 + seed)
+
+
+def _run_case(c, seed):
     dtype, d, C, perkey, H, lengths, mode = (c[k] for k in ("dtype", "d", "chunk", "perkey",
                                                             "H", "lengths", "mode"))
     say(f"case sweep {seed}: {mode} {dtype} d={d} C={C} perkey={perkey} H={H} l2={c['l2']} "
-        f"W={c['width']} lens={lengths}")
+        f"W={c['width']} n={len(lengths)} lens={lengths[:8]}")
     r = c["rng"]
     n = len(lengths)
     n_slots = n + 4 + (sum(len(_ck(L, C)) for L in lengths) if mode == "ckpt" else 0)
