@@ -78,20 +78,30 @@ def prep_touch(cu, n, T, H, C, conv):
 
 
 def scan_touch(cu, n, T, H, C):
-    """For every (sequence, head) chain: units read and output rows written."""
+    """For every (sequence, head) chain: units read and token rows touched. A chain reads the
+    workspace units of its chunks and, one and three chunks ahead (clamped to its last
+    chunk), the units and the v and q rows of later chunks (wide value tiles); it writes the
+    output rows of its chunks. Every row index goes through the same test (row within the
+    chunk's length, token index not negative) before it is used."""
     mc = max_chunks(T, n, C)
     excl, incl = seq_table(cu, n, C)
     out = []
     for s in range(n):
-        c_end = min(incl[s], mc)
+        c_begin, c_end = excl[s], min(incl[s], mc)
+        clast = c_end - 1
         t_begin, t_end = cu[s], min(cu[s + 1], T)
+
+        def rows_of(cc):
+            tok0 = t_begin + (cc - c_begin) * C
+            ln = min(C, t_end - tok0)
+            return [tok0 + i for i in range(C) if i < ln and tok0 + i >= 0]
+
         for h in range(H):
             units, rows = [], []
-            for c in range(excl[s], c_end):
-                units.append(c * H + h)
-                tok0 = t_begin + (c - excl[s]) * C
-                ln = min(C, t_end - tok0)
-                rows += [tok0 + i for i in range(C) if i < ln and tok0 + i >= 0]
+            for c in range(c_begin, c_end):
+                for cc in sorted({c, min(c + 1, clast), min(c + 3, clast)}):
+                    units.append(cc * H + h)
+                    rows += rows_of(cc)
             out.append((s, h, units, rows))
     return out
 
@@ -123,8 +133,8 @@ def test_valid_cu_seqlens_exact_cover(seed, C, conv):
         assert rows and cu[s] <= rows[0] and rows[-1] < cu[s + 1]
         assert all(cu[s] <= r < rows[-1] + 1 for r in halo)
     for s, h, su, rows in scan_touch(cu, n, T, H, C):
-        assert su == [c * H + h for c in range(excl[s], incl[s])]
-        assert rows == list(range(cu[s], cu[s + 1]))
+        assert set(su) == {c * H + h for c in range(excl[s], incl[s])}
+        assert set(rows) == set(range(cu[s], cu[s + 1]))
 
 
 BROKEN = [
