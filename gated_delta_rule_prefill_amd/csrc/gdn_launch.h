@@ -28,6 +28,13 @@ namespace gdn {
 //     qs   [C]       f32 raw-q scan (PrefillArgs::q_raw): s e^{G_i} / |q_i| per token,
 //                        in place of qin
 //   decay [d_k]      f32 e^{G_C} per key channel
+// Two-segment scan (PrefillArgs::seg) only:
+//   lbuf  [C][DKP]   e   outputs of the second segment's identity run (L), row-major
+//                        fragments; its zero-state outputs (fp32) replace U in ut, in the
+//                        same order, as U is consumed
+// and per (sequence, head): the state at the split, fp32 [d_k][d_v] (smid) and as bf16
+// [d_v][d_k] (smidt, an MFMA B operand), and the second segment's transition (ptrans) and
+// zero-state final state (delta), fp32 [d_k][d_v].
 struct PrefillWs {
     int32_t* chunk_info;   // [max_chunks][4]: seq, token start, length, 0
     int32_t* seq_first;    // [n_seqs + 1] first chunk index of each sequence
@@ -41,6 +48,11 @@ struct PrefillWs {
     void* vbuf;            // conv-fused prefill: v rows after the convolution these share
     float* qs;             // raw-q scan: per-token row factor of q              U's section)
     float* decay;
+    void* lbuf;            // two-segment scan only (null otherwise)
+    float* smid;
+    void* smidt;
+    float* ptrans;
+    float* delta;
     void* dump;            // scratch words that absorb stores of lanes past a sequence end
     int64_t max_chunks;
 };
@@ -83,6 +95,12 @@ struct PrefillArgs {
     // whose chunk step is bound by operand ingest (raw q rows arrive as 16 strided pieces
     // per load instead of one contiguous fragment).
     int q_raw;
+    // 1: the scan runs each long sequence as two segments at once (seg_scan): the first from
+    // the initial state, the second both from zero with the real U and from the identity
+    // with U = 0, and a combine pass adds (identity-run outputs) x (state at the split) to
+    // the second segment's outputs and forms the final state. Chosen by the host when the
+    // call's (sequence, head) units leave at least half of the CUs idle.
+    int seg;
     PrefillWs ws;
 };
 
@@ -110,6 +128,20 @@ inline int scan_tiles(int dtype, int64_t units, int dv) {
     const int cap = dtype == 1 ? 8 : 4;
     const int nvb = scan_value_tiles(units, dv, device_cu_count());
     return nvb < cap ? nvb : cap;
+}
+
+// Two-segment scan: bf16, d_k = d_v = 128, C = 64, no checkpoints, both segments' workgroups
+// (one 16-column tile, and a 16-column value tile beside an identity tile) fitting on the
+// chip at once, and sequences long enough on average to split (SEG_MIN_CHUNKS, the length
+// below which a sequence stays in one piece, as the device decides per sequence). At most
+// 64 sequences: the combine pass keeps their chunk ranges in one wave.
+constexpr int SEG_MIN_CHUNKS = 16;
+inline bool seg_scan(int dtype, int H, int dk, int dv, int chunk, int n_seqs,
+                     int64_t total_tokens) {
+    const int64_t units = (int64_t)n_seqs * H;
+    return dtype == 1 && dk == 128 && dv == 128 && chunk == 64 && units > 0 && n_seqs <= 64 &&
+           2 * units * (dv / 16) <= device_cu_count() &&
+           total_tokens >= (int64_t)n_seqs * SEG_MIN_CHUNKS * chunk;
 }
 
 // Chunk length / key dim rounded up to the MFMA contraction step of the element type

@@ -72,6 +72,14 @@ size_t prefill_ws_layout(int dtype, int H, int dk, int dv, int chunk, int n_seqs
     const size_t o_u = off;
     off = align256(off + std::max(units * dv * chunk * 4, s_r + s_b + s_v + s_q));
     const size_t o_d = off;   off = align256(off + units * dk * 4);
+    // two-segment scan: L per unit, and four d_k x d_v states per (sequence, head)
+    const bool seg = seg_scan(dtype, H, dk, dv, chunk, n_seqs, total_tokens);
+    const size_t sh = (size_t)n_seqs * H * dk * dv;
+    const size_t o_l = off;   if (seg) off = align256(off + units * chunk * dkp * e);
+    const size_t o_sm = off;  if (seg) off = align256(off + sh * 4);
+    const size_t o_st = off;  if (seg) off = align256(off + sh * 2);
+    const size_t o_p = off;   if (seg) off = align256(off + sh * 4);
+    const size_t o_dl = off;  if (seg) off = align256(off + sh * 4);
     const size_t o_x = off;   off = align256(off + 256 * 4);
     if (out != nullptr) {
         char* b = static_cast<char*>(base);
@@ -87,6 +95,11 @@ size_t prefill_ws_layout(int dtype, int H, int dk, int dv, int chunk, int n_seqs
         out->vbuf = b + o_u + s_r + s_b;
         out->qs = reinterpret_cast<float*>(b + o_u + s_r + s_b + s_v);
         out->decay = reinterpret_cast<float*>(b + o_d);
+        out->lbuf = seg ? b + o_l : nullptr;
+        out->smid = seg ? reinterpret_cast<float*>(b + o_sm) : nullptr;
+        out->smidt = seg ? b + o_st : nullptr;
+        out->ptrans = seg ? reinterpret_cast<float*>(b + o_p) : nullptr;
+        out->delta = seg ? reinterpret_cast<float*>(b + o_dl) : nullptr;
         out->dump = b + o_x;
         out->max_chunks = max_chunks;
     }
@@ -100,6 +113,9 @@ hipError_t launch_prefill(const PrefillArgs& args, hipStream_t s) {
     PrefillArgs a = args;
     a.u_ws = scan_tiles(a.dtype, (int64_t)a.n_seqs * a.H, a.dv) == 1;
     a.q_raw = a.gate == 0 && a.conv_width == 0 && !a.u_ws;
+    // the workspace holds the two-segment sections exactly when seg_scan holds
+    a.seg = a.ckpt_cu == nullptr && a.ws.lbuf != nullptr &&
+            seg_scan(a.dtype, a.H, a.dk, a.dv, a.chunk, a.n_seqs, a.total_tokens);
     (void)hipGetLastError();  // report only errors raised by this call's launches
     const bool b16 = a.dtype == 1;
     if (a.conv_width == 0) return b16 ? launch_prefill_bf16(a, s) : launch_prefill_f32(a, s);

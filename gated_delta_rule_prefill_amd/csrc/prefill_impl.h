@@ -1019,6 +1019,16 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
     }
 }
 
+// First chunk of a sequence's second segment in the two-segment scan (c1: the sequence stays
+// in one piece). A first-segment workgroup (one tile) runs a chunk faster than a
+// second-segment one (two tiles), so the first segment takes SEG_A_64 / 64 of the chunks
+// (the fastest split measured on the 8192-token, 16-head call; 34 to 37 were within noise).
+constexpr int SEG_A_64 = 35;
+__device__ __forceinline__ int seg_mid(int c0, int c1) {
+    const int n = c1 - c0;
+    return n < SEG_MIN_CHUNKS ? c1 : c0 + (n * SEG_A_64 + 63) / 64;
+}
+
 // =====================================================================================
 // scan kernel: the sequential state pass over chunks
 // =====================================================================================
@@ -1113,8 +1123,9 @@ __device__ __forceinline__ void scan_load_v(typename Mma<T>::frag (&vr)[NVF], co
 // previous chunk: part 0 (first needed: -W and U, or Q_in) and part 1 (K_g^T rows and decay,
 // or M). Issuing a wave's whole set at once stalls it on a full vector-memory queue.
 // QRAW: the O waves read q rows (qrow: the lane's row, or null past the sequence end) and
-// the row factors instead of Q_in.
-template <int PART, bool QRAW, typename T, int DK, int DV, int C, bool PERKEY, bool EROLE, int NVB>
+// the row factors instead of Q_in. UW: the E waves read U (fp32, formed by the prep) for
+// the tile at vcol0, else the operands that form it here.
+template <int PART, bool QRAW, bool UW, typename T, int DK, int DV, int C, bool PERKEY, bool EROLE, int NVB>
 __device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROLE, NVB>& op,
                                               const PrefillArgs& a, size_t u, size_t un,
                                               int vcol0, const T* qrow, int mb, int w) {
@@ -1129,7 +1140,7 @@ __device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROL
             const T* wneg = reinterpret_cast<const T*>(a.ws.wneg) + u * C * F::DKP;
 #pragma unroll
             for (int kb = 0; kb < O::NK; kb++) op.a[kb] = MM::load(Frag<T>::ptr(wneg, mb, kb, F::DKP, lane));
-            if constexpr (NVB == 1) {  // U of this lane's accumulator slots (fp32)
+            if constexpr (UW) {  // U of this lane's accumulator slots (fp32)
                 const float* ut = reinterpret_cast<const float*>(a.ws.ut) + u * DV * C;
                 op.u = *reinterpret_cast<const f32x4*>(ut + ((size_t)((vcol0 / 16) * F::NB + mb) * 64 + lane) * 4);
             }
@@ -1163,7 +1174,7 @@ __device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROL
                         op.dec[j] = *reinterpret_cast<const f32x4*>(dec + rb * 16 + (lane >> 4) * 4);
                 }
             }
-            if constexpr (NVB > 1) scan_load_u_in(op, a, un, mb);
+            if constexpr (!UW) scan_load_u_in(op, a, un, mb);
         } else {
             const T* mm = reinterpret_cast<const T*>(a.ws.mmat) + u * C * CP;
             // M is lower triangular: the fragments starting right of token block mb would
@@ -1184,8 +1195,17 @@ __device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROL
 // pass without checkpoints carries none of the bookkeeping).
 // QRAW: the output waves multiply q itself by S and scale each row by the prep's factor
 // s e^{G_i} / |q_i| (scalar gate, q given, tiles wider than 16 columns; PrefillArgs::q_raw).
-template <typename T, int DK, int DV, int C, bool PERKEY, int NVB, bool CKPT, bool QRAW>
-__global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(PrefillArgs a) {
+// SEG (two-segment scan, PrefillArgs::seg): 0 = the whole sequence; 1 = its first segment,
+// chunks [c_first, seg_mid), from the initial state, ending with the state at the split in
+// the workspace (or, for a sequence too short to split, the final state in the pool as
+// usual); 2 = its second segment, chunks [seg_mid, c_end), with NVB = 2: the 16-column value
+// tile run from a zero state (outputs O0, fp32 in the workspace, and final state Delta)
+// beside the matching 16 columns of the identity run (state I, U = 0: outputs L and final
+// state P, the segment's transition). Every quantity of the pass is affine in the incoming
+// state, so with S_mid the state at the split the true outputs are O0 + L S_mid and the
+// final state is P S_mid + Delta, which the combine pass forms.
+template <typename T, int DK, int DV, int C, bool PERKEY, int NVB, bool CKPT, bool QRAW, int SEG>
+__device__ __forceinline__ void prefill_scan_body(const PrefillArgs& a, const int id) {
     using F = PfCfg<T, DK, DV, C>;
     using MM = typename F::MM;
     using frag = typename MM::frag;
@@ -1194,15 +1214,19 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
     constexpr int RB = DK / 16, RBW = (RB + NB - 1) / NB;   // state row blocks per E wave
     constexpr bool RB_FULL = RB % NB == 0;
     constexpr int BV = SCAN_BV * NVB;
-    constexpr int NVT = DV / BV;
+    constexpr bool HYB = SEG == 2;  // value tile + identity tile
+    static_assert(!HYB || NVB == 2, "the second segment pairs two tiles");
+    static_assert(SEG == 0 || (!CKPT && !QRAW), "two-segment scan: no checkpoints, Q_in");
+    constexpr int TW = HYB ? SCAN_BV : BV;  // value columns of the workgroup
+    constexpr int NVT = DV / TW;
     __shared__ __align__(16) T st[BV][F::LDK];   // S^T slice (MFMA B operand)
     __shared__ __align__(16) T et[BV][F::LDC];   // E^T slice
     __shared__ __align__(16) T ot[NB][NVB][16][16];  // O tiles of the O waves, row-major
-    constexpr bool UWS = NVB == 1;  // U from the workspace (formed by the prep)
+    constexpr bool UWS = NVB == 1 || HYB;  // U from the workspace (formed by the prep)
     __shared__ __align__(16) T vt[UWS ? 1 : BV][F::LDC];  // V^T slice of the next chunk
 
-    // XCD-aware unit mapping: all value tiles of a (sequence, head) on one XCD
-    const int id = blockIdx.x;
+    // XCD-aware unit mapping: all value tiles of a (sequence, head) on one XCD (id is the
+    // workgroup's index within its role; both roles' grids are multiples of 8)
     const int xcd = id & 7, jj = id >> 3;
     const int unit = (jj / NVT) * 8 + xcd;
     const int vtile = jj % NVT;
@@ -1214,7 +1238,7 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
     const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
     const int r16 = lane & 15, g = lane >> 4;
     const int kq = g * KPL;
-    const int vcol0 = vtile * BV;
+    const int vcol0 = vtile * TW;
     // clamps keep inconsistent cu_seqlens inside the workspace and the token range
     int c_first, c_last1;
     if (a.n_seqs <= SEQ_INLINE_MAX) {
@@ -1225,12 +1249,17 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
         c_first = a.ws.seq_first[n];
         c_last1 = a.ws.seq_first[n + 1];
     }
-    const int c_begin = c_first;
-    const int c_end = (int)min((int64_t)c_last1, a.ws.max_chunks);
+    // this workgroup's chunks [c_begin, c_end); token offsets count from c_first
+    const int c_seq_end = (int)min((int64_t)c_last1, a.ws.max_chunks);
+    const int c_mid = SEG != 0 ? seg_mid(c_first, c_seq_end) : c_seq_end;
+    const int c_begin = SEG == 2 ? c_mid : c_first;
+    const int c_end = SEG == 1 ? c_mid : c_seq_end;
+    if (HYB && c_begin >= c_end) return;  // sequence not split (uniform across the workgroup)
+    const bool split = SEG == 1 && c_mid < c_seq_end;  // first segment of a split sequence
     const int t_begin = a.cu_seqlens[n], t_end = min(a.cu_seqlens[n + 1], a.total_tokens);
     const int slot = a.slots[n];
     const bool valid = slot >= 0 && slot < a.n_slots;
-    const bool init = valid && a.has_init != nullptr && a.has_init[n] != 0;
+    const bool init = !HYB && valid && a.has_init != nullptr && a.has_init[n] != 0;
     float* S = valid ? a.state_pool + ((size_t)slot * H + h) * DK * DV : nullptr;
 
     // state slice in the E waves' accumulators:
@@ -1247,7 +1276,10 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int row = rb * 16 + 4 * g + e;
-                    acc_s[j][v][e] = init ? S[(size_t)row * DV + vcol0 + 16 * v + r16] : 0.f;
+                    if (HYB)  // value tile from zero, identity tile from columns of I
+                        acc_s[j][v][e] = v == 1 && row == vcol0 + r16 ? 1.f : 0.f;
+                    else
+                        acc_s[j][v][e] = init ? S[(size_t)row * DV + vcol0 + 16 * v + r16] : 0.f;
                     st[16 * v + r16][row] = from_f32<T>(acc_s[j][v][e]);
                 }
             }
@@ -1316,7 +1348,7 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
             const bool use = p > 0 && p <= len && (p % C == 0 || p == len) && p >= ck.high;
             ck.high = max(ck.high, p);
             if (use) {
-                ck.chunk = c_begin + (p + C - 1) / C - 1;
+                ck.chunk = c_first + (p + C - 1) / C - 1;
                 ck.slot = sl;
                 break;
             }
@@ -1344,13 +1376,13 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
     // the lane's v row of chunk cc (O waves) at the tile's first column; null past the end
     // the lane's q row of chunk cc (O waves); null past the end
     auto qrow_of = [&](int cc) -> const T* {
-        const int tok0 = t_begin + (cc - c_begin) * C;
+        const int tok0 = t_begin + (cc - c_first) * C;
         const int i = mbo * 16 + r16;
         if (i >= min(C, t_end - tok0) || tok0 + i < 0) return nullptr;
         return reinterpret_cast<const T*>(a.q) + ((size_t)(tok0 + i) * H + h) * DK;
     };
     auto vrow_of = [&](int cc) -> const T* {
-        const int tok0 = t_begin + (cc - c_begin) * C;
+        const int tok0 = t_begin + (cc - c_first) * C;
         const int i = mbo * 16 + r16;
         if (i >= min(C, t_end - tok0) || tok0 + i < 0) return nullptr;
         if (a.conv_width != 0) return vsrc + ((size_t)(cc * H + h) * C + i) * DV + vcol0;
@@ -1421,7 +1453,7 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
         auto ld = [&](auto part, O& op, int c) {  // U operands: of the chunk after c
             constexpr int PART = decltype(part)::value;
             const int cc = min(c, clast);
-            scan_load_ops<PART, QRAW, T, DK, DV, C, PERKEY, E, NVB>(
+            scan_load_ops<PART, QRAW, UWS, T, DK, DV, C, PERKEY, E, NVB>(
                 op, a, (size_t)cc * H + h, (size_t)min(c + 1, clast) * H + h, vcol0,
                 QRAW && !E && PART == 0 ? qrow_of(cc) : nullptr, mb, w);
         };
@@ -1437,7 +1469,7 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
             f32x4 acc[NVB];
 #pragma unroll
             for (int v = 0; v < NVB; v++)
-                acc[v] = E ? (UWS ? cur.u : un[v]) : zero4();
+                acc[v] = E ? (UWS ? (HYB && v == 1 ? zero4() : cur.u) : un[v]) : zero4();
 #pragma unroll
             for (int kb = 0; kb < O::NK; kb++)
 #pragma unroll
@@ -1474,9 +1506,25 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
                         acc[v] = MM::mma(cur.am[kt], fb, acc[v]);  // + M E
                     }
                 }
+                if constexpr (HYB) {
+                    // O0 (fp32) over this chunk's U, in the same accumulator order: the E
+                    // waves took U_c into their E rows before the E barrier. L (bf16) as
+                    // row-major fragments of a C x d_k A operand, through LDS like O below.
+                    const size_t uo = (size_t)c * H + h;
+                    float* o0 = reinterpret_cast<float*>(a.ws.ut) + uo * DV * C;
+                    *reinterpret_cast<f32x4*>(o0 + ((size_t)((vcol0 / 16) * NB + mb) * 64 + lane) * 4) = acc[0];
+#pragma unroll
+                    for (int e = 0; e < 4; e++) ot[mb][1][4 * g + e][r16] = from_f32<T>(acc[1][e]);
+                    asm volatile("" ::: "memory");  // LDS accesses of one wave complete in order
+                    float lv[4];
+                    load4<T>(&ot[mb][1][lane >> 2][(lane & 3) * 4], lv);
+                    T* lb = reinterpret_cast<T*>(a.ws.lbuf) + uo * C * F::DKP;
+                    Frag<T>::template store_run<4>(lb, mb * 16 + (lane >> 2), vcol0 + (lane & 3) * 4, F::DKP, lv);
+                    return;
+                }
                 // the accumulator holds 4 tokens of one column per lane; a row-major pass
                 // through LDS lets every lane store 4 adjacent columns of one token at once
-                const int tok0 = t_begin + (c - c_begin) * C;
+                const int tok0 = t_begin + (c - c_first) * C;
                 const int len = min(C, t_end - tok0);
 #pragma unroll
                 for (int v = 0; v < NVB; v++)
@@ -1544,7 +1592,184 @@ __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(Pre
             run(std::integral_constant<bool, false>());
         }
     }
-    if (valid && ewave) store_state(S);
+    if (!ewave) return;
+    if constexpr (SEG == 2) {  // Delta (value tile) and P (identity tile), columns vcol0..+16
+        float* dl = a.ws.delta + (size_t)unit * DK * DV;
+        float* pt = a.ws.ptrans + (size_t)unit * DK * DV;
+#pragma unroll
+        for (int j = 0; j < RBW; j++) {
+            const int rb = w + j * NB;
+            if (rb < RB) {
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const size_t idx = (size_t)(rb * 16 + 4 * g + e) * DV + vcol0 + r16;
+                    dl[idx] = acc_s[j][0][e];
+                    pt[idx] = acc_s[j][1][e];
+                }
+            }
+        }
+    } else if (split) {  // the state at the split: fp32, and bf16 transposed
+        store_state(a.ws.smid + (size_t)unit * DK * DV);
+        T* smt = reinterpret_cast<T*>(a.ws.smidt) + (size_t)unit * DV * DK;
+#pragma unroll
+        for (int j = 0; j < RBW; j++) {
+            const int rb = w + j * NB;
+            if (rb < RB) {
+                float sv[4] = {acc_s[j][0][0], acc_s[j][0][1], acc_s[j][0][2], acc_s[j][0][3]};
+                store4<T>(smt + (size_t)(vcol0 + r16) * DK + rb * 16 + 4 * g, sv);
+            }
+        }
+    } else if (valid) {
+        store_state(S);
+    }
+}
+
+template <typename T, int DK, int DV, int C, bool PERKEY, int NVB, bool CKPT, bool QRAW>
+__global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(PrefillArgs a) {
+    prefill_scan_body<T, DK, DV, C, PERKEY, NVB, CKPT, QRAW, 0>(a, blockIdx.x);
+}
+// Both segments in one launch: workgroups [0, half) run first segments (one 16-column tile),
+// the rest second segments (value tile + identity tile), on the CUs the first leave idle.
+template <typename T, int D, int C, bool PERKEY>
+__global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_seg_kernel(PrefillArgs a,
+                                                                                  int half) {
+    if ((int)blockIdx.x < half)
+        prefill_scan_body<T, D, D, C, PERKEY, 1, false, false, 1>(a, blockIdx.x);
+    else
+        prefill_scan_body<T, D, D, C, PERKEY, 2, false, false, 2>(a, blockIdx.x - half);
+}
+
+// =====================================================================================
+// combine pass of the two-segment scan (bf16)
+// =====================================================================================
+// Workgroups [0, n_seqs H d_k / 16): 16 state rows of a (sequence, head) whose sequence was
+// split, S = P S_mid + Delta on fp32 MFMA, written to its pool slot (none for a slot outside
+// the pool). They come first so they run beside the rest. Then one workgroup per chunk of a
+// second segment (counted over the sequences, head-minor): O = O0 + L S_mid on bf16 MFMA
+// (O0 in fp32; L and S_mid rounded to bf16, as the scan rounds Q_in and S for Q_in S), one
+// wave per 16-token block, written to o.
+constexpr int CB_THREADS = 256;
+// second-segment chunks of a call, at most (the grid's chunk part is H times this)
+inline int64_t seg_b_chunks_bound(int64_t max_chunks) {
+    return (max_chunks * (64 - SEG_A_64) + 63) / 64 + 1;
+}
+template <int DK, int DV, int C>
+__global__ __launch_bounds__(CB_THREADS) void prefill_seg_combine_kernel(PrefillArgs a) {
+    using T = bf16;
+    using MM = Mma<T>;
+    using MF = Mma<float>;
+    constexpr int KB = MM::KB, KPL = MM::KPL, NB = C / 16, NT = DV / 16;
+    constexpr int LDT = DK + 8;   // S_mid^T rows in LDS (bf16, 16-byte padding)
+    constexpr int LDO = DV + 8;   // output rows in LDS
+    static_assert(NB == CB_THREADS / WAVE, "one wave per 16-token block");
+    static_assert(DK % KB == 0 && DK % 16 == 0, "no key padding");
+    static_assert(NB * 16 * LDO <= DV * LDT, "output rows reuse the S_mid^T space");
+    __shared__ __align__(16) T lds[DV * LDT];
+    const int H = a.H;
+    const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
+    const int r16 = lane & 15, g = lane >> 4;
+    // lane n: chunk range [c0l, c1l) of sequence n (clamped as in the scan), its
+    // second-segment chunk count nbl and their exclusive prefix pex over the sequences
+    const WaveSeqTable t = wave_seq_table(a.cu_seqlens, a.n_seqs, C);
+    const int c0l = t.excl, c1l = (int)min((int64_t)t.incl, a.ws.max_chunks);
+    const int nbl = lane < a.n_seqs ? max(0, c1l - seg_mid(c0l, c1l)) : 0;
+    int pin = nbl;
+#pragma unroll
+    for (int off = 1; off < WAVE; off <<= 1) {
+        const int y = __shfl_up(pin, off, WAVE);
+        if (lane >= off) pin += y;
+    }
+    const int pex = pin - nbl;
+    const int n_state = a.n_seqs * H * (DK / 16);
+
+    if ((int)blockIdx.x < n_state) {
+        const int unit = (int)blockIdx.x / (DK / 16), rb = (int)blockIdx.x % (DK / 16);
+        const int n = unit / H, h = unit - n * H;
+        if (__builtin_amdgcn_readlane(nbl, n) == 0) return;  // not split: stored by the scan
+        const int slot = a.slots[n];
+        if (slot < 0 || slot >= a.n_slots) return;
+        const float* P = a.ws.ptrans + (size_t)unit * DK * DV;
+        const float* Sm = a.ws.smid + (size_t)unit * DK * DV;
+        const float* Dl = a.ws.delta + (size_t)unit * DK * DV;
+        float* S = a.state_pool + ((size_t)slot * H + h) * DK * DV;
+        // A operand: lane (r16, g) holds P[16 rb + r16][16 q + 4 g + e] in pa[q][e], and the
+        // B operand of step (q, e) the same key rows of S_mid, so each step contracts over
+        // keys 16 q + e + {0, 4, 8, 12}: all d_k keys once over the DK / 4 steps
+        f32x4 pa[DK / 16];
+#pragma unroll
+        for (int q = 0; q < DK / 16; q++)
+            pa[q] = *reinterpret_cast<const f32x4*>(P + (size_t)(16 * rb + r16) * DK + 16 * q + 4 * g);
+        for (int tv = w; tv < NT; tv += CB_THREADS / WAVE) {
+            f32x4 acc;
+#pragma unroll
+            for (int e = 0; e < 4; e++) acc[e] = Dl[(size_t)(16 * rb + 4 * g + e) * DV + 16 * tv + r16];
+            float sb[DK / 4];
+#pragma unroll
+            for (int q = 0; q < DK / 16; q++)
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    sb[4 * q + e] = Sm[(size_t)(16 * q + 4 * g + e) * DV + 16 * tv + r16];
+#pragma unroll
+            for (int q = 0; q < DK / 16; q++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) acc = MF::mma(pa[q][e], sb[4 * q + e], acc);
+#pragma unroll
+            for (int e = 0; e < 4; e++) S[(size_t)(16 * rb + 4 * g + e) * DV + 16 * tv + r16] = acc[e];
+        }
+        return;
+    }
+    const int id = (int)blockIdx.x - n_state;
+    const int h = id % H, k = id / H;
+    const uint64_t m = __ballot(lane < a.n_seqs && pex <= k && k < pin);
+    if (m == 0) return;
+    const int n = __builtin_ctzll(m);
+    const int c0 = __builtin_amdgcn_readlane(c0l, n), c1 = __builtin_amdgcn_readlane(c1l, n);
+    const int c = seg_mid(c0, c1) + (k - __builtin_amdgcn_readlane(pex, n));
+    const size_t u = (size_t)c * H + h;
+    const float* o0 = reinterpret_cast<const float*>(a.ws.ut) + u * DV * C;
+    const T* lb = reinterpret_cast<const T*>(a.ws.lbuf) + u * C * DK;
+    const T* smt = reinterpret_cast<const T*>(a.ws.smidt) + (size_t)(n * H + h) * DV * DK;
+    const int mb = w;
+    f32x4 acc[NT];
+#pragma unroll
+    for (int tv = 0; tv < NT; tv++)
+        acc[tv] = *reinterpret_cast<const f32x4*>(o0 + ((size_t)(tv * NB + mb) * 64 + lane) * 4);
+    typename MM::frag al[DK / KB];
+#pragma unroll
+    for (int kb = 0; kb < DK / KB; kb++) al[kb] = MM::load(Frag<T>::ptr(lb, mb, kb, DK, lane));
+    // S_mid^T into LDS once for all four waves
+#pragma unroll
+    for (int it = 0; it < DV * DK / 8 / CB_THREADS; it++) {
+        const int p = (int)threadIdx.x + it * CB_THREADS, row = p / (DK / 8), c8 = p % (DK / 8);
+        *reinterpret_cast<MM::frag*>(&lds[row * LDT + c8 * 8]) =
+            *reinterpret_cast<const MM::frag*>(smt + (size_t)row * DK + c8 * 8);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kb = 0; kb < DK / KB; kb++)
+#pragma unroll
+        for (int tv = 0; tv < NT; tv++)
+            acc[tv] = MM::mma(al[kb], MM::load(&lds[(16 * tv + r16) * LDT + kb * KB + g * KPL]), acc[tv]);
+    __syncthreads();  // the S_mid^T space now holds each wave's output rows
+    T* ob = lds + mb * 16 * LDO;
+#pragma unroll
+    for (int tv = 0; tv < NT; tv++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) ob[(4 * g + e) * LDO + 16 * tv + r16] = from_f32<T>(acc[tv][e]);
+    asm volatile("" ::: "memory");  // LDS accesses of one wave complete in order
+    const int tok0 = a.cu_seqlens[n] + (c - c0) * C;
+    const int len = min(C, min(a.cu_seqlens[n + 1], a.total_tokens) - tok0);
+    const int row = lane >> 2, i = mb * 16 + row;
+    if (i < len && tok0 + i >= 0) {
+        T* dst = reinterpret_cast<T*>(a.o) + ((size_t)(tok0 + i) * H + h) * DV;
+#pragma unroll
+        for (int q = 0; q < DV / 32; q++) {  // 4 lanes per row, 8 columns per piece
+            const int col = ((lane & 3) + 4 * q) * 8;
+            float v8[8];
+            load8<T>(&ob[row * LDO + col], v8);
+            store8<T>(dst + col, v8);
+        }
+    }
 }
 
 // =====================================================================================
@@ -1601,6 +1826,17 @@ hipError_t prefill_prep_cfg(const PrefillArgs& a, hipStream_t s) {
 template <typename T, int D, int C, bool PERKEY>
 hipError_t prefill_scan_cfg(const PrefillArgs& a, hipStream_t s) {
     const int units = a.n_seqs * a.H;
+    if constexpr (std::is_same<T, bf16>::value && D == 128 && C == 64) {
+        if (a.seg) {  // see seg_scan
+            const unsigned half = (unsigned)(((units + 7) / 8) * 8 * (D / SCAN_BV));
+            hipLaunchKernelGGL((prefill_scan_seg_kernel<T, D, C, PERKEY>), dim3(2 * half),
+                               dim3(ScanShape<C>::THREADS), 0, s, a, (int)half);
+            const int64_t nb = seg_b_chunks_bound(a.ws.max_chunks) * a.H + (int64_t)units * (D / 16);
+            hipLaunchKernelGGL((prefill_seg_combine_kernel<D, D, C>), dim3((unsigned)nb),
+                               dim3(CB_THREADS), 0, s, a);
+            return hipGetLastError();
+        }
+    }
     const int nvb = scan_tiles(a.dtype, units, D);
     const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * (D / (SCAN_BV * nvb)));
     if (a.ckpt_cu != nullptr) scan_launch<T, D, C, PERKEY, true>(a, nvb, grid, s);

@@ -1,0 +1,151 @@
+"""Two-segment scan on the GPU vs the fp64 oracle, through the C ABI.
+
+With bf16, d_k = d_v = 128, C = 64 and few (sequence, head) units (at most one sixteenth of
+the CU count), the scan runs each sequence of at least 16 chunks as two segments at once:
+the first from the initial state, the second from a zero state beside an identity run that
+yields the segment's transition, and a combine pass adds (identity-run outputs) x (state at
+the split) to the second segment's outputs and forms the final state ([LA-Infra] "Linear
+Attention Chunk-Wise": chunk states compose as S_C = Transition S_0 + Delta). These cases
+cover split and unsplit sequences in one call, ragged and empty sequences, initial states,
+slots outside the pool, both gates, very strong decay, the in-kernel L2 norm and the fused
+convolution. Bar: max|x - ref| / max|ref| <= 1e-2 (bf16 inputs).
+"""
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_prefill_amd import gdn, inputs
+from gpu_util import BAR, oracle_prefill, run_prefill, say
+from test_gpu_conv_prefill import oracle_conv_prefill, run_fused
+
+pytestmark = pytest.mark.gpu
+
+BF = torch.bfloat16
+
+
+def seg_active(H, n_seqs, T, perkey=False):
+    """True when the library sizes the workspace for the two-segment scan for this call."""
+    plain = ((T + n_seqs * 63) // 64) * H * (
+        64 * 128 * 2 * 2 + 128 * 64 * 2 + 64 * 64 * 2
+        + max(64 * 128 * 4, 64 * 64 * 2 + 64 * 4 + 64 * 128 * 2) + 128 * 4)
+    need = gdn.gdn_prefill_workspace_bytes(H, 128, 128, BF, perkey, n_seqs, T, 64)
+    return need > plain + n_seqs * H * 128 * 128 * 14
+
+
+def _check(x, o, pool, heads=None):
+    o_ref, s_ref = oracle_prefill(x)
+    e_o, e_s = oracle.rel_err(o, o_ref), oracle.rel_err(pool, s_ref)
+    say(f"   rel err o={e_o:.2e} S={e_s:.2e}")
+    assert e_o <= BAR[BF] and e_s <= BAR[BF]
+
+
+@pytest.mark.parametrize("lengths,H,perkey,init,l2", [
+    ([4096], 2, False, True, True),        # one sequence, 64 chunks: split 37 / 27
+    ([3000], 4, True, True, False),        # ragged last chunk, per-key gate
+    ([1024], 1, False, False, True),       # exactly 16 chunks: the shortest split
+    ([5000, 0, 700, 1024], 2, False, True, True),  # split, empty, unsplit, split
+    ([2222, 4500], 4, True, False, True),
+])
+def test_two_segment_vs_oracle(lengths, H, perkey, init, l2):
+    T = sum(lengths)
+    say(f"case two-segment scan lengths={lengths} H={H} perkey={perkey} init={init} l2={l2}")
+    assert seg_active(H, len(lengths), T, perkey)
+    x = inputs.random_prefill(91, lengths, H=H, dk=128, dv=128, dtype=BF, perkey=perkey,
+                              prenorm=not l2, with_init=init)
+    o, pool = run_prefill(x)
+    _check(x, o, pool)
+
+
+def test_two_segment_slots_outside_pool_and_untouched_slots():
+    """A sequence whose slot is -1 (no state read or written) and one whose slot is past the
+    pool, beside split ones: outputs still match, the other pool slots stay bit-identical."""
+    lengths = [3100, 2048, 1500]
+    n, H = 3, 2
+    assert seg_active(H, n, sum(lengths))
+    say("case two-segment scan with slots outside the pool")
+    x = inputs.random_prefill(92, lengths, H=H, dk=128, dv=128, dtype=BF, with_init=True)
+    pool0 = torch.randn(5, H, 128, 128, generator=torch.Generator().manual_seed(3))
+    pool0[4] = x.init_states[0]
+    slots = torch.tensor([4, -1, 7], dtype=torch.int32)  # 7 is past a 5-slot pool
+    has_init = torch.tensor([1, 1, 1], dtype=torch.int32)
+    o, pool = run_prefill(x, pool=pool0.clone(), slots=slots, has_init=has_init)
+    init = torch.zeros(n, H, 128, 128)
+    init[0] = x.init_states[0]
+    o_ref, s_ref = oracle_prefill(x, init=init)
+    e_o = oracle.rel_err(o, o_ref)
+    e_s = oracle.rel_err(pool[4], s_ref[0])
+    say(f"   rel err o={e_o:.2e} S={e_s:.2e}")
+    assert e_o <= BAR[BF] and e_s <= BAR[BF]
+    assert torch.equal(pool[:4], pool0[:4])
+
+
+@pytest.mark.parametrize("perkey", [False, True])
+def test_two_segment_strong_decay(perkey):
+    """Gates at -6 on every step and a -100 token inside a block of the second segment: the
+    transition of that segment is then (near) zero and the combine must still be exact."""
+    lengths = [4000]
+    H = 2
+    say(f"case two-segment scan with strong decay perkey={perkey}")
+    x = inputs.random_prefill(93, lengths, H=H, dk=128, dv=128, dtype=BF, perkey=perkey,
+                              with_init=True)
+    g = torch.full_like(x.g, -6.0)
+    g[3000] = -100.0
+    x.g = g
+    o, pool = run_prefill(x)
+    _check(x, o, pool)
+
+
+def test_two_segment_conv_fused():
+    """Conv-fused prefill of 2 sequences x 4 heads (split), with a conv history and an
+    initial state for one of them."""
+    lengths = [2100, 1500]
+    n, H, d, W = 2, 4, 128, 4
+    assert seg_active(H, n, sum(lengths))
+    say("case two-segment scan, conv-fused prefill")
+    x = inputs.conv_prefill(94, lengths, H, d, width=W, dtype=BF, perkey=False)
+    CH = 3 * H * d
+    cs0 = torch.zeros(n, CH, W - 1, dtype=BF)
+    cs0[0] = x.conv_hist[0]
+    pool0 = torch.zeros(n, H, d, d)
+    pool0[0] = x.init_states[0]
+    init = torch.zeros(n, H, d, d)
+    init[0] = x.init_states[0]
+    hist_rows = [x.conv_hist[0].T, torch.zeros(W - 1, CH, dtype=BF)]
+    o, pool, _ = run_fused(x, pool0, torch.arange(n, dtype=torch.int32),
+                           torch.tensor([1, 0], dtype=torch.int32), cs0, chunk=64)
+    o_ref, s_ref = oracle_conv_prefill(x, hist_rows, init)
+    e_o, e_s = oracle.rel_err(o, o_ref), oracle.rel_err(pool, s_ref)
+    say(f"   rel err o={e_o:.2e} S={e_s:.2e}")
+    assert e_o <= BAR[BF] and e_s <= BAR[BF]
+
+
+def test_two_segment_against_one_segment():
+    """The same call with a checkpoint list (which keeps the scan in one segment) and
+    without: both within the bar of the oracle and of each other, and the two-segment call
+    is deterministic."""
+    lengths = [3500]
+    H = 2
+    x = inputs.random_prefill(95, lengths, H=H, dk=128, dv=128, dtype=BF, with_init=True)
+    say("case two-segment vs one-segment scan")
+    o, pool = run_prefill(x)
+    o2, pool2 = run_prefill(x)
+    assert torch.equal(o, o2) and torch.equal(pool, pool2)
+    q, k, v, g, b, cu = (t.to("cuda:0") for t in (x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens))
+    pd = x.init_states.clone().float().to("cuda:0")
+    ext = torch.randn(1, H, 128, 128).to("cuda:0")
+    pool_ck = torch.cat([pd, ext])
+    o1 = gdn.gdn_prefill_chunked_ckpt(
+        q, k, v, g, b, cu, 64, pool_ck, torch.zeros(1, dtype=torch.int32, device="cuda:0"),
+        torch.tensor([0, 1], dtype=torch.int32, device="cuda:0"),
+        torch.tensor([3500], dtype=torch.int32, device="cuda:0"),
+        torch.tensor([1], dtype=torch.int32, device="cuda:0"),
+        has_init=torch.ones(1, dtype=torch.int32, device="cuda:0"), scale=x.scale,
+        qk_l2norm=x.qk_l2norm).cpu()
+    pool1 = pool_ck.cpu()
+    torch.cuda.synchronize()
+    _check(x, o, pool)
+    _check(x, o1, pool1[:1])
+    assert torch.equal(pool1[1], pool1[0])  # the checkpoint at the end is the final state
+    e = oracle.rel_err(o, o1)
+    say(f"   two vs one segment: rel diff o={e:.2e}")
+    assert e <= 1e-2
