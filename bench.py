@@ -2,7 +2,9 @@
 
 Headline (`value`): chunked-prefill throughput in tokens/s on the GDN prefill workload —
 one sequence, T=8192, H=16, d_k=d_v=128, chunk 64, bf16 q/k/v, fp32 gates and state. One
-step = one gdn_prefill_chunked call over that batch (prep + sequential scan). Inputs are
+step = one gdn_prefill_chunked call over that batch (prep, the sequential scan in two
+segments, and the combine of the segments; 16 (sequence, head) units leave half of the CUs
+to the second segment). Inputs are
 resident in HBM before timing; three input sets rotate so the 256 MB MALL does not serve
 them from one step to the next. `ms_per_step` is the median of the timed calls, each between
 its own HIP events.
@@ -525,7 +527,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": traffic.HBM_PEAK_BPS / 1e9,
                      "unit": "GB/s", "frac": achieved / traffic.HBM_PEAK_BPS,
                      "traffic": hbm_traffic,
-                     "kernel": "gdn_prefill_chunked pass (seq_first + prep + scan kernels)",
+                     "kernel": "gdn_prefill_chunked pass (prep, two-segment scan and combine kernels)",
                      "algorithmic_bytes": p["bytes"],
                      "mfma_TFLOPs": p["flops"] / secs / 1e12,
                      "mfma_frac_bf16": p["flops"] / secs / traffic.BF16_MFMA_PEAK},
