@@ -10,6 +10,12 @@ workgroups are dealt round-robin over the 8 XCDs); the scan runs one chain per
   - with cu_seqlens that break that contract (decreasing, negative, past T, describing more
     chunks than the workspace bound), no workgroup reads or writes a workspace unit at or past
     the bound, and no token row outside [0, T) is read or written.
+The same holds for the two-segment scan (first segment [c0, mid), second [mid, c_end) with
+mid = c0 + ceil(35 n / 64) for n >= 16 chunks) and its combine pass, whose chunk workgroups
+are numbered over the second segments' chunks of all sequences: with valid cu_seqlens every
+second-segment chunk of every (sequence, head) is combined by exactly one workgroup within
+the grid bound, and the first segments and the combine together write every output row
+once.
 """
 import random
 
@@ -173,3 +179,131 @@ def test_random_broken_cu_seqlens_stay_in_bounds():
             assert 0 <= u < mc * H and all(0 <= r < T for r in rows + halo)
         for _, _, units, rows in scan_touch(cu, n, T, H, C):
             assert all(0 <= u < mc * H for u in units) and all(0 <= r < T for r in rows)
+
+
+# ------------------------------------------------------------------ two-segment scan
+SEG_MIN_CHUNKS, SEG_A_64 = 16, 35
+
+
+def seg_mid(c0, c1):
+    n = c1 - c0
+    return c1 if n < SEG_MIN_CHUNKS else c0 + (n * SEG_A_64 + 63) // 64
+
+
+def seg_scan_touch(cu, n, T, H, C):
+    """Both segments' workgroups: (sequence, head, units read, units written, rows written).
+    A second-segment workgroup writes its chunks' zero-state outputs over their U and their
+    L, both in the unit's own workspace slots, and no token rows."""
+    mc = max_chunks(T, n, C)
+    excl, incl = seq_table(cu, n, C)
+    out = []
+    for s in range(n):
+        c0, c_end = excl[s], min(incl[s], mc)
+        mid = seg_mid(c0, c_end)
+        t_begin, t_end = cu[s], min(cu[s + 1], T)
+
+        def rows_of(cc):
+            tok0 = t_begin + (cc - c0) * C
+            ln = min(C, t_end - tok0)
+            return [tok0 + i for i in range(C) if i < ln and tok0 + i >= 0]
+
+        for h in range(H):
+            for lo, hi, second in ((c0, mid, False), (mid, c_end, True)):
+                if second and lo >= hi:
+                    continue
+                clast = hi - 1
+                rd, wr, rows = [], [], []
+                for c in range(lo, hi):
+                    rd += [cc * H + h for cc in {c, min(c + 1, clast)}]
+                    if second:
+                        wr.append(c * H + h)
+                    else:
+                        rows += rows_of(c)
+                out.append((s, h, rd, wr, rows))
+    return out
+
+
+def combine_touch(cu, n, T, H, C):
+    """Chunk workgroups of the combine: (sequence, head, chunk, unit, rows written)."""
+    mc = max_chunks(T, n, C)
+    excl, incl = seq_table(cu, n, C)
+    c1l = [min(x, mc) for x in incl]
+    nbl = [max(0, c1l[s] - seg_mid(excl[s], c1l[s])) for s in range(n)]
+    pin, run = [], 0
+    for x in nbl:
+        run += x
+        pin.append(run)
+    pex = [pin[s] - nbl[s] for s in range(n)]
+    bound = (mc * (64 - SEG_A_64) + 63) // 64 + 1
+    out = []
+    for b in range(bound * H):
+        h, k = b % H, b // H
+        hits = [s for s in range(n) if pex[s] <= k < pin[s]]
+        if not hits:
+            continue
+        s = hits[0]
+        c = seg_mid(excl[s], c1l[s]) + (k - pex[s])
+        tok0 = cu[s] + (c - excl[s]) * C
+        ln = min(C, min(cu[s + 1], T) - tok0)
+        rows = [tok0 + i for i in range(C) if i < ln and tok0 + i >= 0]
+        out.append((s, h, c, c * H + h, rows))
+    return out
+
+
+def _long_cu(rng, n):
+    lens = [rng.choice([0, rng.randrange(1, 900), rng.randrange(1000, 9000)]) for _ in range(n)]
+    cu = [0]
+    for L in lens:
+        cu.append(cu[-1] + L)
+    return cu
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_two_segment_exact_cover(seed):
+    rng = random.Random(100 + seed)
+    n, H, C = rng.randrange(1, 17), rng.choice([1, 2, 4]), 64
+    cu = _long_cu(rng, n)
+    T = cu[-1]
+    excl, incl = seq_table(cu, n, C)
+    written = {}
+    for s, h, rd, wr, rows in seg_scan_touch(cu, n, T, H, C):
+        assert set(rd) <= {c * H + h for c in range(excl[s], incl[s])}
+        for r in rows:
+            written[(r, h)] = written.get((r, h), 0) + 1
+    comb = combine_touch(cu, n, T, H, C)
+    seen = set()
+    for s, h, c, u, rows in comb:
+        assert seg_mid(excl[s], incl[s]) <= c < incl[s]
+        assert (s, h, c) not in seen
+        seen.add((s, h, c))
+        for r in rows:
+            written[(r, h)] = written.get((r, h), 0) + 1
+    expect = {(s, h, c) for s in range(n) for h in range(H)
+              for c in range(seg_mid(excl[s], incl[s]), incl[s])}
+    assert seen == expect
+    assert written == {(r, h): 1 for r in range(T) for h in range(H)}
+
+
+@pytest.mark.parametrize("cu", BROKEN)
+def test_two_segment_broken_cu_seqlens_stay_in_bounds(cu):
+    n, H, C = len(cu) - 1, 3, 64
+    for T in (400, 1000, 5000):
+        mc = max_chunks(T, n, C)
+        for _, _, rd, wr, rows in seg_scan_touch(cu, n, T, H, C):
+            assert all(0 <= u < mc * H for u in rd + wr)
+            assert all(0 <= r < T for r in rows)
+        for _, _, _, u, rows in combine_touch(cu, n, T, H, C):
+            assert 0 <= u < mc * H and all(0 <= r < T for r in rows)
+
+
+def test_two_segment_random_broken_cu_seqlens_stay_in_bounds():
+    rng = random.Random(11)
+    for _ in range(200):
+        n, H, C = rng.randrange(1, 9), rng.choice([1, 2, 5]), 64
+        T = rng.randrange(0, 6000)
+        cu = [rng.randrange(-500, 7000) for _ in range(n + 1)]
+        mc = max_chunks(T, n, C)
+        for _, _, rd, wr, rows in seg_scan_touch(cu, n, T, H, C):
+            assert all(0 <= u < mc * H for u in rd + wr) and all(0 <= r < T for r in rows)
+        for _, _, _, u, rows in combine_touch(cu, n, T, H, C):
+            assert 0 <= u < mc * H and all(0 <= r < T for r in rows)
