@@ -70,6 +70,26 @@ def test_noalloc_prefill_wide_then_narrow_tiles(perkey):
         assert e_o <= BAR[torch.bfloat16] and e_s <= BAR[torch.bfloat16]
 
 
+@pytest.mark.parametrize("perkey", [False, True])
+def test_noalloc_prefill_two_segment_scan(perkey):
+    """Few (sequence, head) units with long sequences: the scan runs in two segments and a
+    combine pass, with their extra workspace sections in the scratch. A 4096-token, 2-head
+    call, then a 2000-token, 1-head one over the same scratch: each bit-identical to the
+    workspace prefill and within the oracle's bar."""
+    first = inputs.random_prefill(86, [4096], H=2, dk=128, dv=128, perkey=perkey,
+                                  with_init=True)
+    second = inputs.random_prefill(87, [2000], H=1, dk=128, dv=128, perkey=perkey,
+                                   with_init=True)
+    for name, x in (("first, larger", first), ("second, smaller", second)):
+        say(f"case noalloc prefill, two-segment scan, perkey={perkey}: {name} call")
+        (o_ws, p_ws), (o_na, p_na) = _both(x)
+        assert torch.equal(o_na, o_ws) and torch.equal(p_na, p_ws)
+        o_ref, s_ref = oracle_prefill(x)
+        e_o, e_s = oracle.rel_err(o_na, o_ref), oracle.rel_err(p_na, s_ref)
+        say(f"   bit-identical to the workspace prefill; vs oracle o={e_o:.2e} S={e_s:.2e}")
+        assert e_o <= BAR[torch.bfloat16] and e_s <= BAR[torch.bfloat16]
+
+
 def test_noalloc_prefill_rejects_oversized_call_without_touching_memory():
     say("case noalloc prefill beyond the scratch size")
     T, H, d = 8192, 16, 128
