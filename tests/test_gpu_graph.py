@@ -44,9 +44,11 @@ def test_decode_step_graph_replays_match_eager():
         assert torch.equal(o, ref_o) and torch.equal(pool, ref_pool), r
 
 
-def test_prefill_graph_replays_match_eager():
-    say("case graph: prefill")
-    x = inputs.random_prefill(73, [300, 77, 128], H=4, dk=128, dv=128, with_init=True)
+@pytest.mark.parametrize("lengths", [[300, 77, 128], [2500, 1300]])
+def test_prefill_graph_replays_match_eager(lengths):
+    """[2500, 1300] x 4 heads runs the two-segment scan and its combine pass."""
+    say(f"case graph: prefill {lengths}")
+    x = inputs.random_prefill(73, lengths, H=4, dk=128, dv=128, with_init=True)
     q, k, v, g_, b, cu = to_dev(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens)
     n = x.n_seqs
     pool = x.init_states.clone().to(DEV)
@@ -64,7 +66,7 @@ def test_prefill_graph_replays_match_eager():
         gdn.gdn_prefill_chunked(q, k, v, g_, b, cu, 64, pool, slots, has_init=hi, scale=x.scale,
                                 o=o, workspace=ws)
     for r in _replays():
-        y = inputs.random_prefill(74 + r, [300, 77, 128], H=4, dk=128, dv=128, with_init=True)
+        y = inputs.random_prefill(74 + r, lengths, H=4, dk=128, dv=128, with_init=True)
         for s_, n_ in zip((q, k, v, g_, b), to_dev(y.q, y.k, y.v, y.g, y.beta)):
             s_.copy_(n_)
         pool.copy_(y.init_states.to(DEV))
