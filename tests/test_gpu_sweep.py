@@ -2,7 +2,8 @@
 
 Each case draws its own combination of element type, head dim, chunk size, gate kind, L2 norm,
 head count, ragged sequence lengths (empty and 1-token sequences included), initial states
-and slot map (a second set with enough sequences for the scan's wide value tiles), and runs
+and slot map (a second set with enough sequences for the scan's wide value tiles, a third
+with few long sequences for its two-segment form), and runs
 one of three entry points: the plain chunked prefill, the prefill with
 checkpoint exports, or the conv-fused prefill with conv histories. Outputs, final states,
 exported states and conv windows are compared with the oracle (the conv window, a copy, bit
@@ -22,12 +23,15 @@ pytestmark = pytest.mark.gpu
 
 N_CASES = 48
 N_WIDE = 16
+N_SEG = 12
 
 
-def draw(seed, wide=False):
+def draw(seed, wide=False, seg=False):
     """wide: enough (sequence, head) units (4 heads, 16-104 sequences) that the scan runs
     32- to 128-column value tiles, where it forms U itself and, for the scalar gate with q
-    given, reads q itself."""
+    given, reads q itself. seg: bf16, d = 128, C = 64, at most 16 units and long sequences
+    (at least 16 chunks on average), where the scan runs each sequence of 16 or more chunks
+    in two segments (a checkpoint list keeps it in one)."""
     r = np.random.default_rng(1000 + seed)
     dtype = [torch.float32, torch.bfloat16][r.integers(2)]
     d = int(r.choice([32, 64, 128] if wide else [16, 32, 64, 128]))
@@ -37,6 +41,14 @@ def draw(seed, wide=False):
     n_min = -(-2 * 256 // (H * d // 16))
     n = int(r.integers(n_min, n_min + 25)) if wide else int(r.integers(1, 7))
     lengths = [int(x) for x in r.choice([0, 1, 2, 3, 5, 17, 40, 64, 65, 100, 130, 200], size=n)]
+    if seg:
+        dtype, d, chunk = torch.bfloat16, 128, 64
+        H = int(r.choice([1, 2, 4]))
+        n = int(r.integers(1, min(6, 16 // H) + 1))
+        lengths = [int(x) for x in r.choice([0, 1, 65, 700, 1023, 1024, 1100, 2000, 3500, 5000],
+                                            size=n)]
+        if sum(lengths) < 1024 * n:
+            lengths[int(r.integers(n))] += 1024 * n - sum(lengths) + int(r.integers(0, 700))
     if sum(lengths) == 0:
         lengths[0] = 33
     mode = ["plain", "ckpt", "conv"][r.integers(3)]
@@ -64,6 +76,15 @@ def test_sweep_wide_tiles_vs_oracle(seed):
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
     assert n * c["H"] * (d // 16) // 2 >= ncu  # at least 32-column scan tiles
     _run_case(c, 500 + seed)
+
+
+@pytest.mark.parametrize("seed", range(N_SEG))
+def test_sweep_two_segment_vs_oracle(seed):
+    c = draw(800 + seed, seg=True)
+    n = len(c["lengths"])
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    assert 2 * n * c["H"] * 8 <= ncu and sum(c["lengths"]) >= 1024 * n
+    _run_case(c, 800 + seed)
 
 
 def _run_case(c, seed):
