@@ -11,6 +11,8 @@ its own HIP events.
 
 Also reported on the same JSON line (secondary workloads of the same metric):
   prefill_ckpt:     the headline call exporting the state every 640 tokens / every chunk
+                    (checkpoint lists keep the scan in one segment; a one-checkpoint call
+                    is the reference)
   prefill_batch:    32 sequences x 2048 tokens, H=16, d=128 (a serving-style batch)
   decode:           dense decode step, B=128, H=32, d=128, 256-slot fp32 pool, random slot
                     map; four layer pools rotate per step so the state stream comes from HBM
@@ -183,13 +185,20 @@ def bench_prefill_batch(steps, warmup):
 
 def bench_prefill_ckpt(steps, warmup, plain_ms):
     """Cost of exporting intermediate states inside the prefill: every 640 tokens (a hybrid
-    cache block) and at every chunk boundary (every block-size multiple kept)."""
+    cache block) and at every chunk boundary (every block-size multiple kept). A checkpoint
+    list keeps the scan in one segment, so a call with a single checkpoint (after 8128 of the
+    8192 tokens) is timed too: extra_ms is against the plain (two-segment) call,
+    extra_ms_vs_one_checkpoint against that one-segment call."""
     out = {"workload": "GDN chunked prefill T=8192 H=16 d=128 chunk 64 bf16, exporting the "
                        "fp32 state every N tokens", "ms_plain": plain_ms}
+    one = bench_prefill(steps, warmup, ckpt_every=8128)
+    out["one_checkpoint"] = dict(n_ckpt=one["n_ckpt"], ms=one["ms"],
+                                 extra_ms=one["ms"] - plain_ms)
     for every in (640, 64):
         r = bench_prefill(steps, warmup, ckpt_every=every)
         out[f"every_{every}"] = dict(n_ckpt=r["n_ckpt"], ms=r["ms"],
                                      extra_ms=r["ms"] - plain_ms,
+                                     extra_ms_vs_one_checkpoint=r["ms"] - one["ms"],
                                      export_MiB=r["ckpt_bytes"] / 2**20,
                                      tokens_per_s=r["tokens"] / (r["ms"] * 1e-3))
     return out
