@@ -11,7 +11,9 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libgdn.so")
+# GDN_LIB names another build of the same library (for instance one whose host code carries
+# sanitizers); by default the in-tree libgdn.so
+LIB_PATH = os.environ.get("GDN_LIB") or os.path.join(HERE, "libgdn.so")
 
 GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
 # include/gdn.h GDN_NOALLOC_SCRATCH_BYTES: the allocation-free prefill's per-GPU workspace
