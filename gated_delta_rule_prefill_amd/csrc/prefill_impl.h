@@ -122,6 +122,24 @@ __device__ __forceinline__ ChunkLoc locate_chunk(int c, const int32_t* seq_first
     return r;
 }
 
+// Two-segment scan (PrefillArgs::seg): a first-segment workgroup (one tile) runs a chunk
+// faster than a second-segment one (two tiles), so the first segment takes SEG_A_64 / 64 of
+// a sequence's chunks (the fastest split measured on the 8192-token, 16-head call; 34 to 37
+// were within noise).
+constexpr int SEG_A_64 = 35;
+// Prep order for the two-segment scan: dispatch slot i of NG groups of 8 chunks -> the
+// group prepared there. The scan starts each segment at its first chunks, so those are
+// prepared last (the likeliest to be still cached when the scan reads them): the first
+// segment's groups (the first SEG_A_64 / 64, as the split) and the second's interleave in
+// descending order, ending with group 0 and the second segment's first group. Same-box
+// headline scan 61 -> 59.4 µs; one plain descending order gained nothing.
+__device__ __forceinline__ int seg_prep_group(int i, int NG) {
+    const int sg = (NG * SEG_A_64 + 63) / 64, na = sg, nb = NG - sg, mn = min(na, nb);
+    const int r = NG - 1 - i;  // 0: dispatched last
+    if (r < 2 * mn) return (r % 2 == 0) ? r / 2 : sg + r / 2;
+    return na > nb ? r - mn : sg + (r - mn);
+}
+
 // Fragment-major layout of an R x K MFMA A-operand matrix (R a multiple of 16, K of KB):
 // the 16 x KB fragment (row block rb, k block kb) is stored as 64 lane slots of KPL elements,
 // slot `lane` holding X[16 rb + (lane & 15)][kb KB + (lane >> 4) KPL + e]. A wave then loads a
@@ -278,7 +296,9 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
         h = blockIdx.x - c * H;
     } else {
         const int xcd = blockIdx.x & 7, jj = blockIdx.x >> 3;
-        c = (jj / H) * 8 + xcd;
+        int grp = jj / H;
+        if (a.seg) grp = seg_prep_group(grp, (int)((a.ws.max_chunks + 7) / 8));
+        c = grp * 8 + xcd;
         h = jj - (jj / H) * H;
     }
     // The grid may exceed the chunk bound the workspace was sized for (rounded up to 8, or
@@ -1020,10 +1040,7 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
 }
 
 // First chunk of a sequence's second segment in the two-segment scan (c1: the sequence stays
-// in one piece). A first-segment workgroup (one tile) runs a chunk faster than a
-// second-segment one (two tiles), so the first segment takes SEG_A_64 / 64 of the chunks
-// (the fastest split measured on the 8192-token, 16-head call; 34 to 37 were within noise).
-constexpr int SEG_A_64 = 35;
+// in one piece), at SEG_A_64 / 64 of its chunks.
 __device__ __forceinline__ int seg_mid(int c0, int c1) {
     const int n = c1 - c0;
     return n < SEG_MIN_CHUNKS ? c1 : c0 + (n * SEG_A_64 + 63) / 64;

@@ -53,8 +53,20 @@ def locate_chunk(c, cu, n, C, T):
     return s, tok0, ln
 
 
-def prep_touch(cu, n, T, H, C, conv):
-    """For every prep workgroup: (unit, rows read, rows of the conv halo read)."""
+def seg_prep_group(i, NG, a64=35):
+    """The two-segment scan's prep order: dispatch slot i -> chunk group."""
+    sg = (NG * a64 + 63) // 64
+    na, nb = sg, NG - sg
+    mn = min(na, nb)
+    r = NG - 1 - i
+    if r < 2 * mn:
+        return r // 2 if r % 2 == 0 else sg + r // 2
+    return r - mn if na > nb else sg + (r - mn)
+
+
+def prep_touch(cu, n, T, H, C, conv, seg=False):
+    """For every prep workgroup: (unit, rows read, rows of the conv halo read). seg: the
+    chunk-group order of a call that runs the two-segment scan."""
     mc = max_chunks(T, n, C)
     grid = (mc if conv else (mc + 7) // 8 * 8) * H
     out = []
@@ -63,7 +75,8 @@ def prep_touch(cu, n, T, H, C, conv):
             c, h = b // H, b % H
         else:
             xcd, jj = b & 7, b >> 3
-            c, h = (jj // H) * 8 + xcd, jj % H
+            grp = seg_prep_group(jj // H, (mc + 7) // 8) if seg else jj // H
+            c, h = grp * 8 + xcd, jj % H
         if c >= mc:
             continue
         loc = locate_chunk(c, cu, n, C, T)
@@ -306,4 +319,32 @@ def test_two_segment_random_broken_cu_seqlens_stay_in_bounds():
         for _, _, rd, wr, rows in seg_scan_touch(cu, n, T, H, C):
             assert all(0 <= u < mc * H for u in rd + wr) and all(0 <= r < T for r in rows)
         for _, _, _, u, rows in combine_touch(cu, n, T, H, C):
+            assert 0 <= u < mc * H and all(0 <= r < T for r in rows)
+
+
+def test_seg_prep_order_is_a_permutation():
+    for NG in range(1, 200):
+        assert sorted(seg_prep_group(i, NG) for i in range(NG)) == list(range(NG))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_two_segment_prep_exact_cover(seed):
+    rng = random.Random(200 + seed)
+    n, H, C = rng.randrange(1, 9), rng.choice([1, 3, 16]), 64
+    cu = _long_cu(rng, n)
+    T = cu[-1]
+    prep = prep_touch(cu, n, T, H, C, False, seg=True)
+    units = [u for u, _, _, _ in prep]
+    assert len(units) == len(set(units))
+    excl, incl = seq_table(cu, n, C)
+    expect = {(c, h) for s in range(n) for c in range(excl[s], incl[s]) for h in range(H)}
+    assert {ch for _, ch, _, _ in prep} == expect
+
+
+@pytest.mark.parametrize("cu", BROKEN)
+def test_two_segment_prep_broken_cu_seqlens_stay_in_bounds(cu):
+    n, H, C = len(cu) - 1, 3, 64
+    for T in (400, 1000, 5000):
+        mc = max_chunks(T, n, C)
+        for u, _, rows, _ in prep_touch(cu, n, T, H, C, False, seg=True):
             assert 0 <= u < mc * H and all(0 <= r < T for r in rows)
