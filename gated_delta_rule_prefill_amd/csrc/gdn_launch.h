@@ -133,9 +133,11 @@ inline int scan_tiles(int dtype, int64_t units, int dv) {
 // Two-segment scan: bf16, d_k = d_v = 128, C = 64, no checkpoints, both segments' workgroups
 // (one 16-column tile, and a 16-column value tile beside an identity tile) fitting on the
 // chip at once, and sequences long enough on average to split (SEG_MIN_CHUNKS, the length
-// below which a sequence stays in one piece, as the device decides per sequence). At most
+// below which a sequence stays in one piece, as the device decides per sequence: below
+// ~32-48 chunks the combine pass cost more than the shorter chain saved, measured on one
+// sequence at H = 4, 8 and 16). At most
 // 64 sequences: the combine pass keeps their chunk ranges in one wave.
-constexpr int SEG_MIN_CHUNKS = 16;
+constexpr int SEG_MIN_CHUNKS = 40;
 inline bool seg_scan(int dtype, int H, int dk, int dv, int chunk, int n_seqs,
                      int64_t total_tokens) {
     const int64_t units = (int64_t)n_seqs * H;

@@ -1,7 +1,7 @@
 """Two-segment scan on the GPU vs the fp64 oracle, through the C ABI.
 
 With bf16, d_k = d_v = 128, C = 64 and few (sequence, head) units (at most one sixteenth of
-the CU count), the scan runs each sequence of at least 16 chunks as two segments at once:
+the CU count), the scan runs each sequence of at least 40 chunks as two segments at once:
 the first from the initial state, the second from a zero state beside an identity run that
 yields the segment's transition, and a combine pass adds (identity-run outputs) x (state at
 the split) to the second segment's outputs and forms the final state ([LA-Infra] "Linear
@@ -40,11 +40,11 @@ def _check(x, o, pool, heads=None):
 
 
 @pytest.mark.parametrize("lengths,H,perkey,init,l2", [
-    ([4096], 2, False, True, True),        # one sequence, 64 chunks: split 37 / 27
+    ([4096], 2, False, True, True),        # one sequence, 64 chunks: split 35 / 29
     ([3000], 4, True, True, False),        # ragged last chunk, per-key gate
-    ([1024], 1, False, False, True),       # exactly 16 chunks: the shortest split
-    ([5000, 0, 700, 1024], 2, False, True, True),  # split, empty, unsplit, split
-    ([2222, 4500], 4, True, False, True),
+    ([2560], 1, False, False, True),       # exactly 40 chunks: the shortest split
+    ([9000, 0, 700, 2560], 2, False, True, True),  # split, empty, unsplit, split
+    ([2222, 4500], 4, True, False, True),  # unsplit (35 chunks), split
 ])
 def test_two_segment_vs_oracle(lengths, H, perkey, init, l2):
     T = sum(lengths)
@@ -59,7 +59,7 @@ def test_two_segment_vs_oracle(lengths, H, perkey, init, l2):
 def test_two_segment_slots_outside_pool_and_untouched_slots():
     """A sequence whose slot is -1 (no state read or written) and one whose slot is past the
     pool, beside split ones: outputs still match, the other pool slots stay bit-identical."""
-    lengths = [3100, 2048, 1500]
+    lengths = [5100, 2600, 1500]
     n, H = 3, 2
     assert seg_active(H, n, sum(lengths))
     say("case two-segment scan with slots outside the pool")
@@ -96,9 +96,9 @@ def test_two_segment_strong_decay(perkey):
 
 
 def test_two_segment_conv_fused():
-    """Conv-fused prefill of 2 sequences x 4 heads (split), with a conv history and an
+    """Conv-fused prefill of 2 sequences x 4 heads (both split), with a conv history and an
     initial state for one of them."""
-    lengths = [2100, 1500]
+    lengths = [4100, 2600]
     n, H, d, W = 2, 4, 128, 4
     assert seg_active(H, n, sum(lengths))
     say("case two-segment scan, conv-fused prefill")

@@ -30,7 +30,7 @@ def draw(seed, wide=False, seg=False):
     """wide: enough (sequence, head) units (4 heads, 16-104 sequences) that the scan runs
     32- to 128-column value tiles, where it forms U itself and, for the scalar gate with q
     given, reads q itself. seg: bf16, d = 128, C = 64, at most 16 units and long sequences
-    (at least 16 chunks on average), where the scan runs each sequence of 16 or more chunks
+    (at least 40 chunks on average), where the scan runs each sequence of 40 or more chunks
     in two segments (a checkpoint list keeps it in one)."""
     r = np.random.default_rng(1000 + seed)
     dtype = [torch.float32, torch.bfloat16][r.integers(2)]
@@ -45,10 +45,10 @@ def draw(seed, wide=False, seg=False):
         dtype, d, chunk = torch.bfloat16, 128, 64
         H = int(r.choice([1, 2, 4]))
         n = int(r.integers(1, min(6, 16 // H) + 1))
-        lengths = [int(x) for x in r.choice([0, 1, 65, 700, 1023, 1024, 1100, 2000, 3500, 5000],
+        lengths = [int(x) for x in r.choice([0, 1, 65, 700, 2559, 2560, 2600, 3500, 5000, 8000],
                                             size=n)]
-        if sum(lengths) < 1024 * n:
-            lengths[int(r.integers(n))] += 1024 * n - sum(lengths) + int(r.integers(0, 700))
+        if sum(lengths) < 2560 * n:
+            lengths[int(r.integers(n))] += 2560 * n - sum(lengths) + int(r.integers(0, 700))
     if sum(lengths) == 0:
         lengths[0] = 33
     mode = ["plain", "ckpt", "conv"][r.integers(3)]
@@ -83,7 +83,7 @@ def test_sweep_two_segment_vs_oracle(seed):
     c = draw(800 + seed, seg=True)
     n = len(c["lengths"])
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
-    assert 2 * n * c["H"] * 8 <= ncu and sum(c["lengths"]) >= 1024 * n
+    assert 2 * n * c["H"] * 8 <= ncu and sum(c["lengths"]) >= 2560 * n
     _run_case(c, 800 + seed)
 
 

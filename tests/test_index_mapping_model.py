@@ -11,7 +11,7 @@ workgroups are dealt round-robin over the 8 XCDs); the scan runs one chain per
     chunks than the workspace bound), no workgroup reads or writes a workspace unit at or past
     the bound, and no token row outside [0, T) is read or written.
 The same holds for the two-segment scan (first segment [c0, mid), second [mid, c_end) with
-mid = c0 + ceil(35 n / 64) for n >= 16 chunks) and its combine pass, whose chunk workgroups
+mid = c0 + ceil(35 n / 64) for n >= 40 chunks) and its combine pass, whose chunk workgroups
 are numbered over the second segments' chunks of all sequences: with valid cu_seqlens every
 second-segment chunk of every (sequence, head) is combined by exactly one workgroup within
 the grid bound, and the first segments and the combine together write every output row
@@ -195,7 +195,7 @@ def test_random_broken_cu_seqlens_stay_in_bounds():
 
 
 # ------------------------------------------------------------------ two-segment scan
-SEG_MIN_CHUNKS, SEG_A_64 = 16, 35
+SEG_MIN_CHUNKS, SEG_A_64 = 40, 35
 
 
 def seg_mid(c0, c1):
