@@ -28,13 +28,14 @@ namespace gdn {
 //     qs   [C]       f32 raw-q scan (PrefillArgs::q_raw): s e^{G_i} / |q_i| per token,
 //                        in place of qin
 //   decay [d_k]      f32 e^{G_C} per key channel
-// Two-segment scan (PrefillArgs::seg) only:
-//   lbuf  [C][DKP]   e   outputs of the second segment's identity run (L), row-major
+// Segmented scan (PrefillArgs::seg = K, the most segments a sequence is cut into) only:
+//   lbuf  [C][DKP]   e   outputs of the identity run of the chunk's segment (L), row-major
 //                        fragments; its zero-state outputs (fp32) replace U in ut, in the
 //                        same order, as U is consumed
-// and per (sequence, head): the state at the split, fp32 [d_k][d_v] (smid) and as bf16
-// [d_v][d_k] (smidt, an MFMA B operand), and the second segment's transition (ptrans) and
-// zero-state final state (delta), fp32 [d_k][d_v].
+// and per (segment boundary j = 1 .. K-1, sequence, head), boundary-major: the state at the
+// start of segment j, fp32 [d_k][d_v] (smid) and as bf16 [d_v][d_k] (smidt, an MFMA B
+// operand), and segment j's transition (ptrans) and zero-state final state (delta), fp32
+// [d_k][d_v].
 struct PrefillWs {
     int32_t* chunk_info;   // [max_chunks][4]: seq, token start, length, 0
     int32_t* seq_first;    // [n_seqs + 1] first chunk index of each sequence
@@ -48,7 +49,7 @@ struct PrefillWs {
     void* vbuf;            // conv-fused prefill: v rows after the convolution these share
     float* qs;             // raw-q scan: per-token row factor of q              U's section)
     float* decay;
-    void* lbuf;            // two-segment scan only (null otherwise)
+    void* lbuf;            // segmented scan only (null otherwise)
     float* smid;
     void* smidt;
     float* ptrans;
@@ -95,11 +96,13 @@ struct PrefillArgs {
     // whose chunk step is bound by operand ingest (raw q rows arrive as 16 strided pieces
     // per load instead of one contiguous fragment).
     int q_raw;
-    // 1: the scan runs each long sequence as two segments at once (seg_scan): the first from
-    // the initial state, the second both from zero with the real U and from the identity
-    // with U = 0, and a combine pass adds (identity-run outputs) x (state at the split) to
-    // the second segment's outputs and forms the final state. Chosen by the host when the
-    // call's (sequence, head) units leave at least half of the CUs idle.
+    // K >= 2: the scan cuts each long sequence into up to K segments run at once
+    // (seg_segments): the first from the initial state, each later one both from zero with the
+    // real U and from the identity with U = 0; a chain pass (K > 2) carries the state across
+    // the segment boundaries, and a combine pass adds (identity-run outputs) x (state at the
+    // segment's start) to each later segment's outputs and forms the final state. Chosen by
+    // the host when the call's (sequence, head) units leave at least half of the CUs idle;
+    // 0: one segment.
     int seg;
     PrefillWs ws;
 };
@@ -130,20 +133,61 @@ inline int scan_tiles(int dtype, int64_t units, int dv) {
     return nvb < cap ? nvb : cap;
 }
 
-// Two-segment scan: bf16, d_k = d_v = 128, C = 64, no checkpoints, both segments' workgroups
-// (one 16-column tile, and a 16-column value tile beside an identity tile) fitting on the
-// chip at once, and sequences long enough on average to split (SEG_MIN_CHUNKS, the length
-// below which a sequence stays in one piece, as the device decides per sequence: below
-// ~32-48 chunks the combine pass cost more than the shorter chain saved, measured on one
-// sequence at H = 4, 8 and 16). At most
-// 64 sequences: the combine pass keeps their chunk ranges in one wave.
+// Segmented scan: bf16, d_k = d_v = 128, C = 64, no checkpoints, and few enough (sequence,
+// head) units that at least two segments' workgroups (one 16-column tile for a first
+// segment, a 16-column value tile beside an identity tile for each later one) fit on the
+// chip at once; sequences long enough on average to split (SEG_MIN_CHUNKS, the length below
+// which a sequence stays in one piece, as the device decides per sequence: below ~32-48
+// chunks the combine pass cost more than the shorter chain saved, measured on one sequence
+// at H = 4, 8 and 16). At most 64 sequences: the combine and chain passes keep their chunk
+// ranges in one wave. Returns K, the most segments a sequence may be cut into (as many as
+// the CUs hold, at most SEG_MAX, and no more than a sequence of all total_tokens would
+// take: a K above what any sequence reaches would only add an empty chain launch), or 0.
 constexpr int SEG_MIN_CHUNKS = 40;
-inline bool seg_scan(int dtype, int H, int dk, int dv, int chunk, int n_seqs,
-                     int64_t total_tokens) {
+constexpr int SEG_MAX = 8;
+// Segments of a sequence of n chunks: one below SEG_MIN_CHUNKS, two below SEG_MULTI_CHUNKS,
+// then min(K, n / SEG_PER_CHUNKS). Each segment past the second adds a step to the chain
+// pass (~2.6 µs, bound by its fp32 products); measured on one sequence at H = 1-4, three
+// segments at 64 chunks ran ~1.5 µs slower than two, four at 96 chunks 2-4 µs faster, and
+// six at 128 chunks 9-10 µs faster.
+constexpr int SEG_MULTI_CHUNKS = 80;
+constexpr int SEG_PER_CHUNKS = 20;
+__host__ __device__ inline int seg_count(int n, int kmax) {
+    if (n < SEG_MIN_CHUNKS || kmax < 2) return 1;
+    if (n < SEG_MULTI_CHUNKS) return 2;
+    const int k = n / SEG_PER_CHUNKS;
+    return k < kmax ? k : kmax;
+}
+inline int seg_segments(int dtype, int H, int dk, int dv, int chunk, int n_seqs,
+                        int64_t total_tokens) {
     const int64_t units = (int64_t)n_seqs * H;
-    return dtype == 1 && dk == 128 && dv == 128 && chunk == 64 && units > 0 && n_seqs <= 64 &&
-           2 * units * (dv / 16) <= device_cu_count() &&
-           total_tokens >= (int64_t)n_seqs * SEG_MIN_CHUNKS * chunk;
+    if (!(dtype == 1 && dk == 128 && dv == 128 && chunk == 64 && units > 0 && n_seqs <= 64 &&
+          total_tokens >= (int64_t)n_seqs * SEG_MIN_CHUNKS * chunk))
+        return 0;
+    const int64_t k = device_cu_count() / (units * (dv / 16));
+    if (k < 2) return 0;
+    const int64_t longest = (total_tokens + chunk - 1) / chunk;  // chunks, at most
+    return seg_count(longest < SEG_MAX * SEG_PER_CHUNKS ? (int)longest : SEG_MAX * SEG_PER_CHUNKS,
+                     k < SEG_MAX ? (int)k : SEG_MAX);
+}
+// First segment's share of a sequence cut into k segments, in 64ths. A first-segment
+// workgroup (one tile) runs a chunk faster than a later segment's (two tiles); with the
+// measured two-segment optimum of 35 / 64 (the 8192-token, 16-head call; 34 to 37 were
+// within noise), a later chunk costs 35 / 29 of a first one, and the share
+// 35 / (35 + 29 (k - 1)) lets all k segments end together: k = 2..8 -> 35, 24, 18, 15, 12,
+// 11, 9.
+__host__ __device__ inline int seg_first_64(int k) {
+    const int d = 29 * k + 6;
+    return (2240 + d / 2) / d;
+}
+// First chunk of segment j (0 <= j <= k) of a sequence's chunks [c0, c1) cut into k: the
+// first segment takes seg_first_64(k) / 64 of them (rounded up), the others share the rest
+// evenly (j = k: c1).
+__host__ __device__ inline int seg_bound(int c0, int c1, int j, int k) {
+    if (j <= 0) return c0;
+    if (j >= k) return c1;
+    const int b1 = c0 + ((c1 - c0) * seg_first_64(k) + 63) / 64;
+    return b1 + (j - 1) * (c1 - b1) / (k - 1);
 }
 
 // Chunk length / key dim rounded up to the MFMA contraction step of the element type

@@ -72,9 +72,11 @@ size_t prefill_ws_layout(int dtype, int H, int dk, int dv, int chunk, int n_seqs
     const size_t o_u = off;
     off = align256(off + std::max(units * dv * chunk * 4, s_r + s_b + s_v + s_q));
     const size_t o_d = off;   off = align256(off + units * dk * 4);
-    // two-segment scan: L per unit, and four d_k x d_v states per (sequence, head)
-    const bool seg = seg_scan(dtype, H, dk, dv, chunk, n_seqs, total_tokens);
-    const size_t sh = (size_t)n_seqs * H * dk * dv;
+    // segmented scan: L per unit, and four d_k x d_v states per (segment boundary, sequence,
+    // head)
+    const int kseg = seg_segments(dtype, H, dk, dv, chunk, n_seqs, total_tokens);
+    const bool seg = kseg != 0;
+    const size_t sh = (size_t)(seg ? kseg - 1 : 0) * n_seqs * H * dk * dv;
     const size_t o_l = off;   if (seg) off = align256(off + units * chunk * dkp * e);
     const size_t o_sm = off;  if (seg) off = align256(off + sh * 4);
     const size_t o_st = off;  if (seg) off = align256(off + sh * 2);
@@ -113,9 +115,11 @@ hipError_t launch_prefill(const PrefillArgs& args, hipStream_t s) {
     PrefillArgs a = args;
     a.u_ws = scan_tiles(a.dtype, (int64_t)a.n_seqs * a.H, a.dv) == 1;
     a.q_raw = a.gate == 0 && a.conv_width == 0 && !a.u_ws;
-    // the workspace holds the two-segment sections exactly when seg_scan holds
-    a.seg = a.ckpt_cu == nullptr && a.ws.lbuf != nullptr &&
-            seg_scan(a.dtype, a.H, a.dk, a.dv, a.chunk, a.n_seqs, a.total_tokens);
+    // the workspace holds the segmented-scan sections, for this K, exactly when
+    // seg_segments returns K
+    a.seg = a.ckpt_cu == nullptr && a.ws.lbuf != nullptr
+                ? seg_segments(a.dtype, a.H, a.dk, a.dv, a.chunk, a.n_seqs, a.total_tokens)
+                : 0;
     (void)hipGetLastError();  // report only errors raised by this call's launches
     const bool b16 = a.dtype == 1;
     if (a.conv_width == 0) return b16 ? launch_prefill_bf16(a, s) : launch_prefill_f32(a, s);

@@ -122,22 +122,50 @@ __device__ __forceinline__ ChunkLoc locate_chunk(int c, const int32_t* seq_first
     return r;
 }
 
-// Two-segment scan (PrefillArgs::seg): a first-segment workgroup (one tile) runs a chunk
-// faster than a second-segment one (two tiles), so the first segment takes SEG_A_64 / 64 of
-// a sequence's chunks (the fastest split measured on the 8192-token, 16-head call; 34 to 37
-// were within noise).
-constexpr int SEG_A_64 = 35;
-// Prep order for the two-segment scan: dispatch slot i of NG groups of 8 chunks -> the
-// group prepared there. The scan starts each segment at its first chunks, so those are
-// prepared last (the likeliest to be still cached when the scan reads them): the first
-// segment's groups (the first SEG_A_64 / 64, as the split) and the second's interleave in
-// descending order, ending with group 0 and the second segment's first group. Same-box
-// headline scan 61 -> 59.4 µs; one plain descending order gained nothing.
+// Prep order for the two-segment scan (PrefillArgs::seg = 2): dispatch slot i of NG groups
+// of 8 chunks -> the group prepared there. The scan starts each segment at its first
+// chunks, so those are prepared last (the likeliest to be still cached when the scan reads
+// them): the first segment's groups (the first seg_first_64(2) / 64, as the split) and the
+// second's interleave in descending order, ending with group 0 and the second segment's
+// first group. Same-box headline scan 61 -> 59.4 µs; one plain descending order gained
+// nothing.
 __device__ __forceinline__ int seg_prep_group(int i, int NG) {
-    const int sg = (NG * SEG_A_64 + 63) / 64, na = sg, nb = NG - sg, mn = min(na, nb);
+    const int sg = (NG * seg_first_64(2) + 63) / 64, na = sg, nb = NG - sg, mn = min(na, nb);
     const int r = NG - 1 - i;  // 0: dispatched last
     if (r < 2 * mn) return (r % 2 == 0) ? r / 2 : sg + r / 2;
     return na > nb ? r - mn : sg + (r - mn);
+}
+
+// The same for a call cut into k > 2 segments (the groups cut as a sequence of NG groups
+// would be): the slots dispatched last take, pass by pass, the m-th group of every segment
+// that long, segments in order (pass 0: each segment's first group). Slot r from the end
+// lies in the pass m with before(m) <= r < before(m + 1), before(m) = sum_s min(len_s, m)
+// the slots of the passes ahead of it, found by bisection.
+__device__ __forceinline__ int seg_prep_group_k(int i, int NG, int k) {
+    int b[SEG_MAX + 1];
+#pragma unroll
+    for (int s = 0; s <= SEG_MAX; s++) b[s] = seg_bound(0, NG, min(s, k), k);
+    auto before = [&](int m) {
+        int c = 0;
+#pragma unroll
+        for (int s = 0; s < SEG_MAX; s++) c += min(b[s + 1] - b[s], m);  // empty past k
+        return c;
+    };
+    const int r = NG - 1 - i;  // 0: dispatched last
+    int lo = 0, hi = NG;       // before(0) = 0 <= r < NG = before(NG)
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (before(mid) <= r) lo = mid;
+        else hi = mid;
+    }
+    int t = r - before(lo), grp = i;
+#pragma unroll
+    for (int s = 0; s < SEG_MAX; s++) {
+        const bool has = b[s + 1] - b[s] > lo;
+        if (has && t == 0) grp = b[s] + lo;
+        t -= has ? 1 : 0;
+    }
+    return grp;
 }
 
 // Fragment-major layout of an R x K MFMA A-operand matrix (R a multiple of 16, K of KB):
@@ -297,7 +325,11 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
     } else {
         const int xcd = blockIdx.x & 7, jj = blockIdx.x >> 3;
         int grp = jj / H;
-        if (a.seg) grp = seg_prep_group(grp, (int)((a.ws.max_chunks + 7) / 8));
+        const int NG = (int)((a.ws.max_chunks + 7) / 8);
+        if (a.seg == 2)
+            grp = seg_prep_group(grp, NG);
+        else if (a.seg > 2)
+            grp = seg_prep_group_k(grp, NG, seg_count((int)min(a.ws.max_chunks, (int64_t)SEG_MAX * SEG_PER_CHUNKS), a.seg));
         c = grp * 8 + xcd;
         h = jj - (jj / H) * H;
     }
@@ -1039,13 +1071,6 @@ __attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(Pr
     }
 }
 
-// First chunk of a sequence's second segment in the two-segment scan (c1: the sequence stays
-// in one piece), at SEG_A_64 / 64 of its chunks.
-__device__ __forceinline__ int seg_mid(int c0, int c1) {
-    const int n = c1 - c0;
-    return n < SEG_MIN_CHUNKS ? c1 : c0 + (n * SEG_A_64 + 63) / 64;
-}
-
 // =====================================================================================
 // scan kernel: the sequential state pass over chunks
 // =====================================================================================
@@ -1212,17 +1237,20 @@ __device__ __forceinline__ void scan_load_ops(ScanOps<T, DK, DV, C, PERKEY, EROL
 // pass without checkpoints carries none of the bookkeeping).
 // QRAW: the output waves multiply q itself by S and scale each row by the prep's factor
 // s e^{G_i} / |q_i| (scalar gate, q given, tiles wider than 16 columns; PrefillArgs::q_raw).
-// SEG (two-segment scan, PrefillArgs::seg): 0 = the whole sequence; 1 = its first segment,
-// chunks [c_first, seg_mid), from the initial state, ending with the state at the split in
-// the workspace (or, for a sequence too short to split, the final state in the pool as
-// usual); 2 = its second segment, chunks [seg_mid, c_end), with NVB = 2: the 16-column value
-// tile run from a zero state (outputs O0, fp32 in the workspace, and final state Delta)
-// beside the matching 16 columns of the identity run (state I, U = 0: outputs L and final
-// state P, the segment's transition). Every quantity of the pass is affine in the incoming
-// state, so with S_mid the state at the split the true outputs are O0 + L S_mid and the
-// final state is P S_mid + Delta, which the combine pass forms.
+// SEG (segmented scan, PrefillArgs::seg = K; a sequence of n chunks is cut into
+// k = seg_count(n, K) segments at seg_bound): 0 = the whole sequence; 1 = its first segment,
+// from the initial state, ending with the state at the first boundary in the workspace (or,
+// for a sequence left in one piece, the final state in the pool as usual); 2 = its later
+// segment sidx (1 <= sidx < k), with NVB = 2: the 16-column value tile run from a zero state
+// (outputs O0, fp32 in the workspace, and final state Delta) beside the matching 16 columns
+// of the identity run (state I, U = 0: outputs L and final state P, the segment's
+// transition). Every quantity of the pass is affine in the incoming state, so with S_j the
+// state at the start of segment j the true outputs are O0 + L S_j and the state at its end
+// is P S_j + Delta, which the chain and combine passes form.
+// (unit, vtile): the workgroup's (sequence, head) and value tile, as its kernel maps them.
 template <typename T, int DK, int DV, int C, bool PERKEY, int NVB, bool CKPT, bool QRAW, int SEG>
-__device__ __forceinline__ void prefill_scan_body(const PrefillArgs& a, const int id) {
+__device__ __forceinline__ void prefill_scan_body(const PrefillArgs& a, const int unit,
+                                                  const int vtile, const int sidx) {
     using F = PfCfg<T, DK, DV, C>;
     using MM = typename F::MM;
     using frag = typename MM::frag;
@@ -1233,20 +1261,14 @@ __device__ __forceinline__ void prefill_scan_body(const PrefillArgs& a, const in
     constexpr int BV = SCAN_BV * NVB;
     constexpr bool HYB = SEG == 2;  // value tile + identity tile
     static_assert(!HYB || NVB == 2, "the second segment pairs two tiles");
-    static_assert(SEG == 0 || (!CKPT && !QRAW), "two-segment scan: no checkpoints, Q_in");
+    static_assert(SEG == 0 || (!CKPT && !QRAW), "segmented scan: no checkpoints, Q_in");
     constexpr int TW = HYB ? SCAN_BV : BV;  // value columns of the workgroup
-    constexpr int NVT = DV / TW;
     __shared__ __align__(16) T st[BV][F::LDK];   // S^T slice (MFMA B operand)
     __shared__ __align__(16) T et[BV][F::LDC];   // E^T slice
     __shared__ __align__(16) T ot[NB][NVB][16][16];  // O tiles of the O waves, row-major
     constexpr bool UWS = NVB == 1 || HYB;  // U from the workspace (formed by the prep)
     __shared__ __align__(16) T vt[UWS ? 1 : BV][F::LDC];  // V^T slice of the next chunk
 
-    // XCD-aware unit mapping: all value tiles of a (sequence, head) on one XCD (id is the
-    // workgroup's index within its role; both roles' grids are multiples of 8)
-    const int xcd = id & 7, jj = id >> 3;
-    const int unit = (jj / NVT) * 8 + xcd;
-    const int vtile = jj % NVT;
     const int H = a.H;
     if (unit >= a.n_seqs * H) return;
     const int n = unit / H, h = unit - (unit / H) * H;
@@ -1268,11 +1290,11 @@ __device__ __forceinline__ void prefill_scan_body(const PrefillArgs& a, const in
     }
     // this workgroup's chunks [c_begin, c_end); token offsets count from c_first
     const int c_seq_end = (int)min((int64_t)c_last1, a.ws.max_chunks);
-    const int c_mid = SEG != 0 ? seg_mid(c_first, c_seq_end) : c_seq_end;
-    const int c_begin = SEG == 2 ? c_mid : c_first;
-    const int c_end = SEG == 1 ? c_mid : c_seq_end;
-    if (HYB && c_begin >= c_end) return;  // sequence not split (uniform across the workgroup)
-    const bool split = SEG == 1 && c_mid < c_seq_end;  // first segment of a split sequence
+    const int kseg = SEG != 0 ? seg_count(c_seq_end - c_first, a.seg) : 1;
+    if (HYB && sidx >= kseg) return;  // no such segment (uniform across the workgroup)
+    const int c_begin = SEG == 2 ? seg_bound(c_first, c_seq_end, sidx, kseg) : c_first;
+    const int c_end = SEG == 0 ? c_seq_end : seg_bound(c_first, c_seq_end, sidx + 1, kseg);
+    const bool split = SEG == 1 && kseg > 1;  // first segment of a split sequence
     const int t_begin = a.cu_seqlens[n], t_end = min(a.cu_seqlens[n + 1], a.total_tokens);
     const int slot = a.slots[n];
     const bool valid = slot >= 0 && slot < a.n_slots;
@@ -1611,8 +1633,9 @@ __device__ __forceinline__ void prefill_scan_body(const PrefillArgs& a, const in
     }
     if (!ewave) return;
     if constexpr (SEG == 2) {  // Delta (value tile) and P (identity tile), columns vcol0..+16
-        float* dl = a.ws.delta + (size_t)unit * DK * DV;
-        float* pt = a.ws.ptrans + (size_t)unit * DK * DV;
+        const size_t bu = (size_t)(sidx - 1) * a.n_seqs * H + unit;  // boundary sidx
+        float* dl = a.ws.delta + bu * DK * DV;
+        float* pt = a.ws.ptrans + bu * DK * DV;
 #pragma unroll
         for (int j = 0; j < RBW; j++) {
             const int rb = w + j * NB;
@@ -1625,7 +1648,7 @@ __device__ __forceinline__ void prefill_scan_body(const PrefillArgs& a, const in
                 }
             }
         }
-    } else if (split) {  // the state at the split: fp32, and bf16 transposed
+    } else if (split) {  // the state at the first boundary: fp32, and bf16 transposed
         store_state(a.ws.smid + (size_t)unit * DK * DV);
         T* smt = reinterpret_cast<T*>(a.ws.smidt) + (size_t)unit * DV * DK;
 #pragma unroll
@@ -1641,34 +1664,179 @@ __device__ __forceinline__ void prefill_scan_body(const PrefillArgs& a, const in
     }
 }
 
+// XCD-aware unit mapping: all value tiles of a (sequence, head) on one XCD, as workgroups
+// are dispatched to the 8 XCDs in turn (the grid is a multiple of 8 units).
 template <typename T, int DK, int DV, int C, bool PERKEY, int NVB, bool CKPT, bool QRAW>
 __global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_kernel(PrefillArgs a) {
-    prefill_scan_body<T, DK, DV, C, PERKEY, NVB, CKPT, QRAW, 0>(a, blockIdx.x);
+    constexpr int NVT = DV / (SCAN_BV * NVB);
+    const int xcd = (int)blockIdx.x & 7, jj = (int)blockIdx.x >> 3;
+    prefill_scan_body<T, DK, DV, C, PERKEY, NVB, CKPT, QRAW, 0>(a, (jj / NVT) * 8 + xcd,
+                                                                jj % NVT, 0);
 }
-// Both segments in one launch: workgroups [0, half) run first segments (one 16-column tile),
-// the rest second segments (value tile + identity tile), on the CUs the first leave idle.
+// All segments in one launch, on the CUs a one-segment scan leaves idle: virtual unit
+// vu = s units + unit is segment s of (sequence, head) unit, mapped to XCDs as above (the
+// segments of a unit read different chunks, so they need not share an XCD); s = 0 runs first
+// segments (one 16-column tile), s >= 1 later ones (value tile + identity tile).
 template <typename T, int D, int C, bool PERKEY>
-__global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_seg_kernel(PrefillArgs a,
-                                                                                  int half) {
-    if ((int)blockIdx.x < half)
-        prefill_scan_body<T, D, D, C, PERKEY, 1, false, false, 1>(a, blockIdx.x);
+__global__ __launch_bounds__(ScanShape<C>::THREADS) void prefill_scan_seg_kernel(PrefillArgs a) {
+    constexpr int NVT = D / SCAN_BV;
+    const int units = a.n_seqs * a.H;
+    const int xcd = (int)blockIdx.x & 7, jj = (int)blockIdx.x >> 3;
+    const int vu = (jj / NVT) * 8 + xcd, vtile = jj % NVT;
+    if (vu >= a.seg * units) return;
+    const int sidx = vu / units, unit = vu - sidx * units;
+    if (sidx == 0)
+        prefill_scan_body<T, D, D, C, PERKEY, 1, false, false, 1>(a, unit, vtile, 0);
     else
-        prefill_scan_body<T, D, D, C, PERKEY, 2, false, false, 2>(a, blockIdx.x - half);
+        prefill_scan_body<T, D, D, C, PERKEY, 2, false, false, 2>(a, unit, vtile, sidx);
 }
 
 // =====================================================================================
-// combine pass of the two-segment scan (bf16)
+// chain and combine passes of the segmented scan (bf16)
 // =====================================================================================
-// Workgroups [0, n_seqs H d_k / 16): 16 state rows of a (sequence, head) whose sequence was
-// split, S = P S_mid + Delta on fp32 MFMA, written to its pool slot (none for a slot outside
-// the pool). They come first so they run beside the rest. Then one workgroup per chunk of a
-// second segment (counted over the sequences, head-minor): O = O0 + L S_mid on bf16 MFMA
-// (O0 in fp32; L and S_mid rounded to bf16, as the scan rounds Q_in and S for Q_in S), one
-// wave per 16-token block, written to o.
+// Per sequence (lane n of a wave): its chunk range [c0, c1) (clamped as in the scan), its
+// segment count k, and the chunks of its later segments, [seg_bound(1), c1), counted (nbl)
+// and prefixed over the sequences (pex exclusive, pin inclusive).
+struct SegTable {
+    int c0, c1, k, nbl, pex, pin;
+};
+__device__ __forceinline__ SegTable seg_table(const PrefillArgs& a, int C) {
+    const WaveSeqTable t = wave_seq_table(a.cu_seqlens, a.n_seqs, C);
+    SegTable r;
+    r.c0 = t.excl;
+    r.c1 = (int)min((int64_t)t.incl, a.ws.max_chunks);
+    const bool live = lane_id() < a.n_seqs;
+    r.k = live ? seg_count(r.c1 - r.c0, a.seg) : 1;
+    r.nbl = live && r.k > 1 ? max(0, r.c1 - seg_bound(r.c0, r.c1, 1, r.k)) : 0;
+    r.pin = r.nbl;
+#pragma unroll
+    for (int off = 1; off < WAVE; off <<= 1) {
+        const int y = __shfl_up(r.pin, off, WAVE);
+        if (lane_id() >= off) r.pin += y;
+    }
+    r.pex = r.pin - r.nbl;
+    return r;
+}
+
 constexpr int CB_THREADS = 256;
-// second-segment chunks of a call, at most (the grid's chunk part is H times this)
-inline int64_t seg_b_chunks_bound(int64_t max_chunks) {
-    return (max_chunks * (64 - SEG_A_64) + 63) / 64 + 1;
+// Chain pass (K > 2): the state at the start of each later segment but the last,
+// S_{j+1} = P_j S_j + Delta_j for j = 1 .. k - 2, from S_1 (the first segment's end state), on
+// fp32 MFMA. One workgroup per (sequence, head, 16 state columns): each column slice of the
+// state evolves on its own, kept transposed in LDS across the steps. Each S_{j+1} is written
+// in bf16 transposed (the combine's output operand), and S_{k-1} also in fp32, from which
+// the combine forms the final state. The steps form a dependent chain, so each one's
+// latency counts: its B operands come from LDS as 16-byte reads issued together before the
+// products, and the next step's P and Delta (which do not depend on the chain) are loaded
+// before this step's products.
+template <int DK, int DV, int C>
+__global__ __launch_bounds__(CB_THREADS) void prefill_seg_chain_kernel(PrefillArgs a) {
+    using T = bf16;
+    using MF = Mma<float>;
+    constexpr int NT = DV / 16, NW = CB_THREADS / WAVE, RBW = DK / 16 / NW, NQ = DK / 16;
+    constexpr int LDS_T = DK + 4;  // row stride of the transposed slice (floats, 16-byte rows)
+    static_assert(DK % (16 * NW) == 0, "state row blocks spread evenly over the waves");
+    static_assert((DK * 16 / 4) % CB_THREADS == 0, "S_1 slice in whole 16-byte loads");
+    __shared__ __align__(16) float slt[16][LDS_T];  // slt[c][key] = S_j[key][16 tv + c]
+    const int H = a.H, nu = a.n_seqs * H;
+    const int unit = (int)blockIdx.x / NT, tv = (int)blockIdx.x % NT;
+    const SegTable t = seg_table(a, C);
+    if (unit >= nu) return;
+    const int n = unit / H;
+    const int k = __builtin_amdgcn_readlane(t.k, n);
+    if (k <= 2) return;
+    const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
+    const int r16 = lane & 15, g = lane >> 4;
+    // step j's operands for this wave's row blocks rb = w + r NW, as in the combine's state
+    // rows: pa[r][q][e] = P_j[16 rb + r16][16 q + 4 g + e], da[r][e] = Delta_j[16 rb + 4 g + e]
+    // [16 tv + r16], so step (q, e) contracts over keys 16 q + 4 g + e with S_j's same rows
+    f32x4 pa[RBW][NQ], pn[RBW][NQ];
+    f32x4 da[RBW], dn[RBW];
+    auto load_step = [&](int j, f32x4 (&p)[RBW][NQ], f32x4 (&d)[RBW]) {
+        const size_t bu = (size_t)(j - 1) * nu + unit;
+        const float* P = a.ws.ptrans + bu * DK * DV;
+        const float* Dl = a.ws.delta + bu * DK * DV;
+#pragma unroll
+        for (int r = 0; r < RBW; r++) {
+            const int rb = w + r * NW;
+#pragma unroll
+            for (int q = 0; q < NQ; q++)
+                p[r][q] = *reinterpret_cast<const f32x4*>(P + (size_t)(16 * rb + r16) * DK + 16 * q + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; e++) d[r][e] = Dl[(size_t)(16 * rb + 4 * g + e) * DV + 16 * tv + r16];
+        }
+    };
+    // step j with its operands (pc, dc), loading step j + 1's into (px, dx) first: issued
+    // unconditionally (the last step reloads its own), and kept ahead of the products, so
+    // their latency overlaps the step and the wait counts stay exact
+    auto step = [&](int j, f32x4 (&pc)[RBW][NQ], f32x4 (&dc)[RBW], f32x4 (&px)[RBW][NQ],
+                    f32x4 (&dx)[RBW]) {
+        load_step(min(j + 1, k - 2), px, dx);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 sb[NQ];  // sb[q][e] = S_j[16 q + 4 g + e][16 tv + r16]
+#pragma unroll
+        for (int q = 0; q < NQ; q++) sb[q] = *reinterpret_cast<const f32x4*>(&slt[r16][16 * q + 4 * g]);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 acc[RBW];
+#pragma unroll
+        for (int r = 0; r < RBW; r++) acc[r] = dc[r];
+#pragma unroll
+        for (int q = 0; q < NQ; q++)
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+#pragma unroll
+                for (int r = 0; r < RBW; r++) acc[r] = MF::mma(pc[r][q][e], sb[q][e], acc[r]);
+        __syncthreads();  // every wave has read S_j
+        const size_t bn = (size_t)j * nu + unit;
+        T* smt = reinterpret_cast<T*>(a.ws.smidt) + bn * DV * DK;
+        float* sm = a.ws.smid + bn * DK * DV;
+#pragma unroll
+        for (int r = 0; r < RBW; r++) {
+            const int rb = w + r * NW;
+            float sv[4] = {acc[r][0], acc[r][1], acc[r][2], acc[r][3]};
+            *reinterpret_cast<f32x4*>(&slt[r16][16 * rb + 4 * g]) = acc[r];
+            store4<T>(smt + (size_t)(16 * tv + r16) * DK + 16 * rb + 4 * g, sv);
+            if (j == k - 2)
+#pragma unroll
+                for (int e = 0; e < 4; e++) sm[(size_t)(16 * rb + 4 * g + e) * DV + 16 * tv + r16] = sv[e];
+        }
+        __syncthreads();  // S_{j+1} complete in LDS
+    };
+    load_step(1, pa, da);
+    {  // S_1's column slice, 16-byte loads (4 columns of one key row each), stored transposed
+        const float* s1 = a.ws.smid + (size_t)unit * DK * DV + 16 * tv;
+        f32x4 x[DK * 16 / 4 / CB_THREADS];
+#pragma unroll
+        for (int it = 0; it < DK * 16 / 4 / CB_THREADS; it++) {
+            const int p = (int)threadIdx.x + it * CB_THREADS;
+            x[it] = *reinterpret_cast<const f32x4*>(s1 + (size_t)(p / 4) * DV + 4 * (p % 4));
+        }
+#pragma unroll
+        for (int it = 0; it < DK * 16 / 4 / CB_THREADS; it++) {
+            const int p = (int)threadIdx.x + it * CB_THREADS;
+#pragma unroll
+            for (int e = 0; e < 4; e++) slt[4 * (p % 4) + e][p / 4] = x[it][e];
+        }
+    }
+    __syncthreads();
+    for (int j = 1; j <= k - 2; j += 2) {  // two steps per pass: the operand sets alternate
+        step(j, pa, da, pn, dn);
+        if (j + 1 > k - 2) break;
+        step(j + 1, pn, dn, pa, da);
+    }
+}
+
+// Combine pass. Workgroups [0, n_seqs H d_k / 16): 16 state rows of a (sequence, head)
+// whose sequence was split into k segments, S = P S_{k-1} + Delta with the last segment's
+// P and Delta, on fp32 MFMA, written to its pool slot (none for a slot outside the pool).
+// They come first so they run beside the rest. Then one workgroup per chunk of a later
+// segment j (counted over the sequences, head-minor): O = O0 + L S_j on bf16 MFMA (O0 in
+// fp32; L and S_j rounded to bf16, as the scan rounds Q_in and S for Q_in S), one wave per
+// 16-token block, written to o.
+// later-segment chunks of a call, at most (the grid's chunk part is H times this): a
+// sequence of n chunks cut into k <= kmax has n - ceil(n seg_first_64(k) / 64) of them, and
+// the share falls as k grows
+inline int64_t seg_b_chunks_bound(int64_t max_chunks, int kmax) {
+    return (max_chunks * (64 - seg_first_64(kmax)) + 63) / 64 + 1;
 }
 template <int DK, int DV, int C>
 __global__ __launch_bounds__(CB_THREADS) void prefill_seg_combine_kernel(PrefillArgs a) {
@@ -1676,41 +1844,32 @@ __global__ __launch_bounds__(CB_THREADS) void prefill_seg_combine_kernel(Prefill
     using MM = Mma<T>;
     using MF = Mma<float>;
     constexpr int KB = MM::KB, KPL = MM::KPL, NB = C / 16, NT = DV / 16;
-    constexpr int LDT = DK + 8;   // S_mid^T rows in LDS (bf16, 16-byte padding)
+    constexpr int LDT = DK + 8;   // S_j^T rows in LDS (bf16, 16-byte padding)
     constexpr int LDO = DV + 8;   // output rows in LDS
     static_assert(NB == CB_THREADS / WAVE, "one wave per 16-token block");
     static_assert(DK % KB == 0 && DK % 16 == 0, "no key padding");
-    static_assert(NB * 16 * LDO <= DV * LDT, "output rows reuse the S_mid^T space");
+    static_assert(NB * 16 * LDO <= DV * LDT, "output rows reuse the S_j^T space");
     __shared__ __align__(16) T lds[DV * LDT];
-    const int H = a.H;
+    const int H = a.H, nu = a.n_seqs * H;
     const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
     const int r16 = lane & 15, g = lane >> 4;
-    // lane n: chunk range [c0l, c1l) of sequence n (clamped as in the scan), its
-    // second-segment chunk count nbl and their exclusive prefix pex over the sequences
-    const WaveSeqTable t = wave_seq_table(a.cu_seqlens, a.n_seqs, C);
-    const int c0l = t.excl, c1l = (int)min((int64_t)t.incl, a.ws.max_chunks);
-    const int nbl = lane < a.n_seqs ? max(0, c1l - seg_mid(c0l, c1l)) : 0;
-    int pin = nbl;
-#pragma unroll
-    for (int off = 1; off < WAVE; off <<= 1) {
-        const int y = __shfl_up(pin, off, WAVE);
-        if (lane >= off) pin += y;
-    }
-    const int pex = pin - nbl;
-    const int n_state = a.n_seqs * H * (DK / 16);
+    const SegTable t = seg_table(a, C);
+    const int n_state = nu * (DK / 16);
 
     if ((int)blockIdx.x < n_state) {
         const int unit = (int)blockIdx.x / (DK / 16), rb = (int)blockIdx.x % (DK / 16);
         const int n = unit / H, h = unit - n * H;
-        if (__builtin_amdgcn_readlane(nbl, n) == 0) return;  // not split: stored by the scan
+        const int k = __builtin_amdgcn_readlane(t.k, n);
+        if (k < 2) return;  // not split: stored by the scan
         const int slot = a.slots[n];
         if (slot < 0 || slot >= a.n_slots) return;
-        const float* P = a.ws.ptrans + (size_t)unit * DK * DV;
-        const float* Sm = a.ws.smid + (size_t)unit * DK * DV;
-        const float* Dl = a.ws.delta + (size_t)unit * DK * DV;
+        const size_t bu = (size_t)(k - 2) * nu + unit;  // the last boundary
+        const float* P = a.ws.ptrans + bu * DK * DV;
+        const float* Sm = a.ws.smid + bu * DK * DV;
+        const float* Dl = a.ws.delta + bu * DK * DV;
         float* S = a.state_pool + ((size_t)slot * H + h) * DK * DV;
         // A operand: lane (r16, g) holds P[16 rb + r16][16 q + 4 g + e] in pa[q][e], and the
-        // B operand of step (q, e) the same key rows of S_mid, so each step contracts over
+        // B operand of step (q, e) the same key rows of S_{k-1}, so each step contracts over
         // keys 16 q + e + {0, 4, 8, 12}: all d_k keys once over the DK / 4 steps
         f32x4 pa[DK / 16];
 #pragma unroll
@@ -1736,16 +1895,19 @@ __global__ __launch_bounds__(CB_THREADS) void prefill_seg_combine_kernel(Prefill
         return;
     }
     const int id = (int)blockIdx.x - n_state;
-    const int h = id % H, k = id / H;
-    const uint64_t m = __ballot(lane < a.n_seqs && pex <= k && k < pin);
+    const int h = id % H, kc = id / H;
+    const uint64_t m = __ballot(lane < a.n_seqs && t.pex <= kc && kc < t.pin);
     if (m == 0) return;
     const int n = __builtin_ctzll(m);
-    const int c0 = __builtin_amdgcn_readlane(c0l, n), c1 = __builtin_amdgcn_readlane(c1l, n);
-    const int c = seg_mid(c0, c1) + (k - __builtin_amdgcn_readlane(pex, n));
+    const int c0 = __builtin_amdgcn_readlane(t.c0, n), c1 = __builtin_amdgcn_readlane(t.c1, n);
+    const int k = __builtin_amdgcn_readlane(t.k, n);
+    const int c = seg_bound(c0, c1, 1, k) + (kc - __builtin_amdgcn_readlane(t.pex, n));
+    int j = 1;  // the chunk's segment
+    while (j + 1 < k && seg_bound(c0, c1, j + 1, k) <= c) j++;
     const size_t u = (size_t)c * H + h;
     const float* o0 = reinterpret_cast<const float*>(a.ws.ut) + u * DV * C;
     const T* lb = reinterpret_cast<const T*>(a.ws.lbuf) + u * C * DK;
-    const T* smt = reinterpret_cast<const T*>(a.ws.smidt) + (size_t)(n * H + h) * DV * DK;
+    const T* smt = reinterpret_cast<const T*>(a.ws.smidt) + ((size_t)(j - 1) * nu + n * H + h) * DV * DK;
     const int mb = w;
     f32x4 acc[NT];
 #pragma unroll
@@ -1754,7 +1916,7 @@ __global__ __launch_bounds__(CB_THREADS) void prefill_seg_combine_kernel(Prefill
     typename MM::frag al[DK / KB];
 #pragma unroll
     for (int kb = 0; kb < DK / KB; kb++) al[kb] = MM::load(Frag<T>::ptr(lb, mb, kb, DK, lane));
-    // S_mid^T into LDS once for all four waves
+    // S_j^T into LDS once for all four waves
 #pragma unroll
     for (int it = 0; it < DV * DK / 8 / CB_THREADS; it++) {
         const int p = (int)threadIdx.x + it * CB_THREADS, row = p / (DK / 8), c8 = p % (DK / 8);
@@ -1767,7 +1929,7 @@ __global__ __launch_bounds__(CB_THREADS) void prefill_seg_combine_kernel(Prefill
 #pragma unroll
         for (int tv = 0; tv < NT; tv++)
             acc[tv] = MM::mma(al[kb], MM::load(&lds[(16 * tv + r16) * LDT + kb * KB + g * KPL]), acc[tv]);
-    __syncthreads();  // the S_mid^T space now holds each wave's output rows
+    __syncthreads();  // the S_j^T space now holds each wave's output rows
     T* ob = lds + mb * 16 * LDO;
 #pragma unroll
     for (int tv = 0; tv < NT; tv++)
@@ -1844,11 +2006,15 @@ template <typename T, int D, int C, bool PERKEY>
 hipError_t prefill_scan_cfg(const PrefillArgs& a, hipStream_t s) {
     const int units = a.n_seqs * a.H;
     if constexpr (std::is_same<T, bf16>::value && D == 128 && C == 64) {
-        if (a.seg) {  // see seg_scan
-            const unsigned half = (unsigned)(((units + 7) / 8) * 8 * (D / SCAN_BV));
-            hipLaunchKernelGGL((prefill_scan_seg_kernel<T, D, C, PERKEY>), dim3(2 * half),
-                               dim3(ScanShape<C>::THREADS), 0, s, a, (int)half);
-            const int64_t nb = seg_b_chunks_bound(a.ws.max_chunks) * a.H + (int64_t)units * (D / 16);
+        if (a.seg) {  // see seg_segments
+            const int kmax = a.seg;
+            const unsigned grid = (unsigned)(((kmax * units + 7) / 8) * 8 * (D / SCAN_BV));
+            hipLaunchKernelGGL((prefill_scan_seg_kernel<T, D, C, PERKEY>), dim3(grid),
+                               dim3(ScanShape<C>::THREADS), 0, s, a);
+            if (kmax > 2)
+                hipLaunchKernelGGL((prefill_seg_chain_kernel<D, D, C>), dim3((unsigned)(units * (D / 16))),
+                                   dim3(CB_THREADS), 0, s, a);
+            const int64_t nb = seg_b_chunks_bound(a.ws.max_chunks, kmax) * a.H + (int64_t)units * (D / 16);
             hipLaunchKernelGGL((prefill_seg_combine_kernel<D, D, C>), dim3((unsigned)nb),
                                dim3(CB_THREADS), 0, s, a);
             return hipGetLastError();

@@ -135,8 +135,8 @@ def test_prefill_workspace_too_small_and_sizing():
     per = (64 * 128 * 2 * 2 + 128 * 64 * 2 + 64 * 64 * 2
            + max(64 * 128 * 4, 64 * 64 * 2 + 64 * 4 + 64 * 128 * 2) + 128 * 4)
     # 16 (sequence, head) units leave half of the chip's CUs idle (the CU count is 256
-    # without a device), so the scan runs in two segments: + L (bf16) per unit and, per
-    # (sequence, head), the state at the split (fp32 and bf16) and the second segment's
+    # without a device), so the scan runs in (at most) two segments: + L (bf16) per unit and,
+    # per (sequence, head), the state at the split (fp32 and bf16) and the second segment's
     # transition and zero-state final state (fp32)
     seg = 16 * 128 * 128 * (4 + 2 + 4 + 4)
     assert need.value >= 128 * 16 * (per + 64 * 128 * 2) + seg
@@ -147,6 +147,13 @@ def test_prefill_workspace_too_small_and_sizing():
     more = ctypes.c_size_t(0)
     lib.gdn_prefill_workspace_bytes(ctypes.byref(dims), 8, 8192, 64, ctypes.byref(more))
     assert 135 * 16 * per <= more.value < 135 * 16 * per + 64 * 1024
+    # 4 heads: 256 / (4 x 8) = 8 segments fit, but a sequence of 128 chunks takes 128 / 20
+    # = 6, so 5 segment boundaries of the four states
+    four = ctypes.c_size_t(0)
+    dims4 = _dims(H=4, dk=128, dv=128)
+    lib.gdn_prefill_workspace_bytes(ctypes.byref(dims4), 1, 8192, 64, ctypes.byref(four))
+    base4 = 128 * 4 * (per + 64 * 128 * 2) + 5 * 4 * 128 * 128 * (4 + 2 + 4 + 4)
+    assert base4 <= four.value < base4 + 64 * 1024
 
 
 def _prefill_noalloc(dims, **kw):

@@ -44,9 +44,10 @@ def test_decode_step_graph_replays_match_eager():
         assert torch.equal(o, ref_o) and torch.equal(pool, ref_pool), r
 
 
-@pytest.mark.parametrize("lengths", [[300, 77, 128], [3000, 2600]])
+@pytest.mark.parametrize("lengths", [[300, 77, 128], [3000, 2600], [6000, 2600]])
 def test_prefill_graph_replays_match_eager(lengths):
-    """[3000, 2600] x 4 heads runs the two-segment scan and its combine pass."""
+    """x 4 heads: [3000, 2600] runs the segmented scan in two segments and its combine pass,
+    [6000, 2600] in four and two, with the chain pass between."""
     say(f"case graph: prefill {lengths}")
     x = inputs.random_prefill(73, lengths, H=4, dk=128, dv=128, with_init=True)
     q, k, v, g_, b, cu = to_dev(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens)

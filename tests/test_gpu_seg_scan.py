@@ -1,14 +1,16 @@
-"""Two-segment scan on the GPU vs the fp64 oracle, through the C ABI.
+"""Segmented scan on the GPU vs the fp64 oracle, through the C ABI.
 
 With bf16, d_k = d_v = 128, C = 64 and few (sequence, head) units (at most one sixteenth of
-the CU count), the scan runs each sequence of at least 40 chunks as two segments at once:
-the first from the initial state, the second from a zero state beside an identity run that
-yields the segment's transition, and a combine pass adds (identity-run outputs) x (state at
-the split) to the second segment's outputs and forms the final state ([LA-Infra] "Linear
-Attention Chunk-Wise": chunk states compose as S_C = Transition S_0 + Delta). These cases
-cover split and unsplit sequences in one call, ragged and empty sequences, initial states,
-slots outside the pool, both gates, very strong decay, the in-kernel L2 norm and the fused
-convolution. Bar: max|x - ref| / max|ref| <= 1e-2 (bf16 inputs).
+the CU count), the scan cuts each sequence of n >= 40 chunks into k segments run at once
+(k = 2 below 80 chunks, then min(K, n / 20); K = CUs / (8 units), at most 8): the first from the initial
+state, each later one from a zero state beside an identity run that yields the segment's
+transition. A chain pass carries the state across the boundaries (S_{j+1} = P_j S_j +
+Delta_j) and a combine pass adds (identity-run outputs) x (state at the segment's start) to
+each later segment's outputs and forms the final state ([LA-Infra] "Linear Attention
+Chunk-Wise": chunk states compose as S_C = Transition S_0 + Delta). These cases cover 2 to 8
+segments, split and unsplit sequences in one call, ragged and empty sequences, initial
+states, slots outside the pool, both gates, very strong decay, the in-kernel L2 norm and the
+fused convolution. Bar: max|x - ref| / max|ref| <= 1e-2 (bf16 inputs).
 """
 import pytest
 import torch
@@ -40,15 +42,18 @@ def _check(x, o, pool, heads=None):
 
 
 @pytest.mark.parametrize("lengths,H,perkey,init,l2", [
-    ([4096], 2, False, True, True),        # one sequence, 64 chunks: split 35 / 29
-    ([3000], 4, True, True, False),        # ragged last chunk, per-key gate
+    ([4096], 2, False, True, True),        # 64 chunks, K = 8: 2 segments
+    ([3000], 4, True, True, False),        # ragged last chunk, per-key gate: 2 segments
     ([2560], 1, False, False, True),       # exactly 40 chunks: the shortest split
-    ([9000, 0, 700, 2560], 2, False, True, True),  # split, empty, unsplit, split
-    ([2222, 4500], 4, True, False, True),  # unsplit (35 chunks), split
+    ([9000, 0, 700, 2560], 2, False, True, True),  # K = 4: 4 segments, empty, 1, 2
+    ([2222, 4500], 4, True, False, True),  # K = 4: unsplit (35 chunks), 2 segments
+    ([5200, 5200, 1000], 3, False, True, True),  # 9 units, K = 3: 3, 3, unsplit
+    ([8192], 1, False, True, True),        # 128 chunks: 6 segments
+    ([12000], 1, True, True, True),        # 188 chunks: 8 segments (K), per-key gate
 ])
-def test_two_segment_vs_oracle(lengths, H, perkey, init, l2):
+def test_segmented_vs_oracle(lengths, H, perkey, init, l2):
     T = sum(lengths)
-    say(f"case two-segment scan lengths={lengths} H={H} perkey={perkey} init={init} l2={l2}")
+    say(f"case segmented scan lengths={lengths} H={H} perkey={perkey} init={init} l2={l2}")
     assert seg_active(H, len(lengths), T, perkey)
     x = inputs.random_prefill(91, lengths, H=H, dk=128, dv=128, dtype=BF, perkey=perkey,
                               prenorm=not l2, with_init=init)
@@ -56,13 +61,14 @@ def test_two_segment_vs_oracle(lengths, H, perkey, init, l2):
     _check(x, o, pool)
 
 
-def test_two_segment_slots_outside_pool_and_untouched_slots():
-    """A sequence whose slot is -1 (no state read or written) and one whose slot is past the
-    pool, beside split ones: outputs still match, the other pool slots stay bit-identical."""
+def test_segmented_slots_outside_pool_and_untouched_slots():
+    """K = 5: a sequence of 4 segments, one of 2 whose slot is -1 (no state read or
+    written) and an unsplit one whose slot is past the pool: outputs still match, the other
+    pool slots stay bit-identical."""
     lengths = [5100, 2600, 1500]
     n, H = 3, 2
     assert seg_active(H, n, sum(lengths))
-    say("case two-segment scan with slots outside the pool")
+    say("case segmented scan with slots outside the pool")
     x = inputs.random_prefill(92, lengths, H=H, dk=128, dv=128, dtype=BF, with_init=True)
     pool0 = torch.randn(5, H, 128, 128, generator=torch.Generator().manual_seed(3))
     pool0[4] = x.init_states[0]
@@ -80,28 +86,28 @@ def test_two_segment_slots_outside_pool_and_untouched_slots():
 
 
 @pytest.mark.parametrize("perkey", [False, True])
-def test_two_segment_strong_decay(perkey):
-    """Gates at -6 on every step and a -100 token inside a block of the second segment: the
-    transition of that segment is then (near) zero and the combine must still be exact."""
-    lengths = [4000]
+def test_segmented_strong_decay(perkey):
+    """Gates at -6 on every step and a -100 token inside a block of the last of 4 segments:
+    the transitions are then (near) zero and the chain and combine must still be exact."""
+    lengths = [6000]
     H = 2
-    say(f"case two-segment scan with strong decay perkey={perkey}")
+    say(f"case segmented scan with strong decay perkey={perkey}")
     x = inputs.random_prefill(93, lengths, H=H, dk=128, dv=128, dtype=BF, perkey=perkey,
                               with_init=True)
     g = torch.full_like(x.g, -6.0)
-    g[3000] = -100.0
+    g[5000] = -100.0
     x.g = g
     o, pool = run_prefill(x)
     _check(x, o, pool)
 
 
-def test_two_segment_conv_fused():
-    """Conv-fused prefill of 2 sequences x 4 heads (both split), with a conv history and an
-    initial state for one of them."""
-    lengths = [4100, 2600]
+def test_segmented_conv_fused():
+    """Conv-fused prefill of 2 sequences x 4 heads (4 and 2 segments), with a conv history
+    and an initial state for one of them."""
+    lengths = [6100, 2600]
     n, H, d, W = 2, 4, 128, 4
     assert seg_active(H, n, sum(lengths))
-    say("case two-segment scan, conv-fused prefill")
+    say("case segmented scan, conv-fused prefill")
     x = inputs.conv_prefill(94, lengths, H, d, width=W, dtype=BF, perkey=False)
     CH = 3 * H * d
     cs0 = torch.zeros(n, CH, W - 1, dtype=BF)
@@ -119,10 +125,10 @@ def test_two_segment_conv_fused():
     assert e_o <= BAR[BF] and e_s <= BAR[BF]
 
 
-def test_two_segment_against_one_segment():
-    """The same call with a checkpoint list (which keeps the scan in one segment) and
-    without: both within the bar of the oracle and of each other, and the two-segment call
-    is deterministic."""
+def test_segmented_against_one_segment():
+    """The same call (2 segments) with a checkpoint list (which keeps the scan in one
+    segment) and without: both within the bar of the oracle and of each other, and the
+    segmented call is deterministic."""
     lengths = [3500]
     H = 2
     x = inputs.random_prefill(95, lengths, H=H, dk=128, dv=128, dtype=BF, with_init=True)

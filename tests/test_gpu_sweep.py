@@ -3,7 +3,7 @@
 Each case draws its own combination of element type, head dim, chunk size, gate kind, L2 norm,
 head count, ragged sequence lengths (empty and 1-token sequences included), initial states
 and slot map (a second set with enough sequences for the scan's wide value tiles, a third
-with few long sequences for its two-segment form), and runs
+with few long sequences for its segmented form), and runs
 one of three entry points: the plain chunked prefill, the prefill with
 checkpoint exports, or the conv-fused prefill with conv histories. Outputs, final states,
 exported states and conv windows are compared with the oracle (the conv window, a copy, bit
@@ -30,8 +30,8 @@ def draw(seed, wide=False, seg=False):
     """wide: enough (sequence, head) units (4 heads, 16-104 sequences) that the scan runs
     32- to 128-column value tiles, where it forms U itself and, for the scalar gate with q
     given, reads q itself. seg: bf16, d = 128, C = 64, at most 16 units and long sequences
-    (at least 40 chunks on average), where the scan runs each sequence of 40 or more chunks
-    in two segments (a checkpoint list keeps it in one)."""
+    (at least 40 chunks on average), where the scan cuts each sequence of 40 or more chunks
+    into 2 to 8 segments (a checkpoint list keeps it in one)."""
     r = np.random.default_rng(1000 + seed)
     dtype = [torch.float32, torch.bfloat16][r.integers(2)]
     d = int(r.choice([32, 64, 128] if wide else [16, 32, 64, 128]))
@@ -79,7 +79,7 @@ def test_sweep_wide_tiles_vs_oracle(seed):
 
 
 @pytest.mark.parametrize("seed", range(N_SEG))
-def test_sweep_two_segment_vs_oracle(seed):
+def test_sweep_segmented_vs_oracle(seed):
     c = draw(800 + seed, seg=True)
     n = len(c["lengths"])
     ncu = torch.cuda.get_device_properties(0).multi_processor_count

@@ -10,12 +10,12 @@ workgroups are dealt round-robin over the 8 XCDs); the scan runs one chain per
   - with cu_seqlens that break that contract (decreasing, negative, past T, describing more
     chunks than the workspace bound), no workgroup reads or writes a workspace unit at or past
     the bound, and no token row outside [0, T) is read or written.
-The same holds for the two-segment scan (first segment [c0, mid), second [mid, c_end) with
-mid = c0 + ceil(35 n / 64) for n >= 40 chunks) and its combine pass, whose chunk workgroups
-are numbered over the second segments' chunks of all sequences: with valid cu_seqlens every
-second-segment chunk of every (sequence, head) is combined by exactly one workgroup within
-the grid bound, and the first segments and the combine together write every output row
-once.
+The same holds for the segmented scan (a sequence of n >= 40 chunks cut into
+k = min(K, n / 20) segments, at least 2, at seg_bound) and its chain and combine passes,
+whose chunk workgroups are numbered over the later segments' chunks of all sequences: with
+valid cu_seqlens every later-segment chunk of every (sequence, head) is combined by exactly
+one workgroup within the grid bound, the first segments and the combine together write every
+output row once, and every boundary state is written (once) before it is read.
 """
 import random
 
@@ -54,7 +54,7 @@ def locate_chunk(c, cu, n, C, T):
 
 
 def seg_prep_group(i, NG, a64=35):
-    """The two-segment scan's prep order: dispatch slot i -> chunk group."""
+    """The two-segment scan's prep order (K = 2): dispatch slot i -> chunk group."""
     sg = (NG * a64 + 63) // 64
     na, nb = sg, NG - sg
     mn = min(na, nb)
@@ -194,25 +194,76 @@ def test_random_broken_cu_seqlens_stay_in_bounds():
             assert all(0 <= u < mc * H for u in units) and all(0 <= r < T for r in rows)
 
 
-# ------------------------------------------------------------------ two-segment scan
-SEG_MIN_CHUNKS, SEG_A_64 = 40, 35
+# ------------------------------------------------------------------ segmented scan
+SEG_MIN_CHUNKS, SEG_MULTI_CHUNKS, SEG_PER_CHUNKS, SEG_MAX = 40, 80, 20, 8
 
 
-def seg_mid(c0, c1):
-    n = c1 - c0
-    return c1 if n < SEG_MIN_CHUNKS else c0 + (n * SEG_A_64 + 63) // 64
+def seg_segments(H, n, T, cus=256, C=64):
+    """K, the most segments a sequence is cut into (bf16, d = 128, C = 64), or 0."""
+    units = n * H
+    if not (units > 0 and n <= 64 and T >= n * SEG_MIN_CHUNKS * C):
+        return 0
+    k = cus // (units * 8)
+    if k < 2:
+        return 0
+    return seg_count(min(-(-T // C), SEG_MAX * SEG_PER_CHUNKS), min(k, SEG_MAX))
 
 
-def seg_scan_touch(cu, n, T, H, C):
-    """Both segments' workgroups: (sequence, head, units read, units written, rows written).
-    A second-segment workgroup writes its chunks' zero-state outputs over their U and their
-    L, both in the unit's own workspace slots, and no token rows."""
+def seg_count(nch, kmax):
+    if nch < SEG_MIN_CHUNKS or kmax < 2:
+        return 1
+    if nch < SEG_MULTI_CHUNKS:
+        return 2
+    return min(kmax, nch // SEG_PER_CHUNKS)
+
+
+def seg_first_64(k):
+    d = 29 * k + 6
+    return (2240 + d // 2) // d
+
+
+def cdiv_int(a, b):
+    """C integer division (truncates toward zero), as the device code divides."""
+    q = abs(a) // abs(b)
+    return q if (a >= 0) == (b >= 0) else -q
+
+
+def seg_bound(c0, c1, j, k):
+    if j <= 0:
+        return c0
+    if j >= k:
+        return c1
+    b1 = c0 + cdiv_int((c1 - c0) * seg_first_64(k) + 63, 64)
+    return b1 + cdiv_int((j - 1) * (c1 - b1), k - 1)
+
+
+def test_seg_split_rules():
+    assert [seg_first_64(k) for k in range(1, 9)] == [64, 35, 24, 18, 15, 12, 11, 9]
+    for kmax in range(2, SEG_MAX + 1):
+        for nch in range(0, 3000):
+            k = seg_count(nch, kmax)
+            assert (k == 1) == (nch < SEG_MIN_CHUNKS) and k <= kmax
+            assert k <= 2 or nch >= SEG_MULTI_CHUNKS
+            b = [seg_bound(5, 5 + nch, j, k) for j in range(k + 1)]
+            assert b[0] == 5 and b[-1] == 5 + nch
+            assert all(b[j] < b[j + 1] for j in range(k)) or nch == 0  # no empty segment
+            if k == 2:  # the two-segment split at ceil(35 n / 64)
+                assert b[1] == 5 + (nch * 35 + 63) // 64
+            later = nch - (b[1] - b[0]) if k > 1 else 0
+            assert later <= (nch * (64 - seg_first_64(kmax)) + 63) // 64
+
+
+def seg_scan_touch(cu, n, T, H, C, kmax=2):
+    """Every segment's workgroups: (sequence, head, units read, units written, rows written,
+    boundary slots written). A later segment's workgroup writes its chunks' zero-state
+    outputs over their U and their L, both in the unit's own workspace slots, no token rows,
+    and its transition and Delta at boundary slot (segment - 1)."""
     mc = max_chunks(T, n, C)
     excl, incl = seq_table(cu, n, C)
     out = []
     for s in range(n):
         c0, c_end = excl[s], min(incl[s], mc)
-        mid = seg_mid(c0, c_end)
+        k = seg_count(c_end - c0, kmax)
         t_begin, t_end = cu[s], min(cu[s + 1], T)
 
         def rows_of(cc):
@@ -221,46 +272,109 @@ def seg_scan_touch(cu, n, T, H, C):
             return [tok0 + i for i in range(C) if i < ln and tok0 + i >= 0]
 
         for h in range(H):
-            for lo, hi, second in ((c0, mid, False), (mid, c_end, True)):
-                if second and lo >= hi:
-                    continue
+            for j in range(k):
+                lo, hi = seg_bound(c0, c_end, j, k), seg_bound(c0, c_end, j + 1, k)
                 clast = hi - 1
                 rd, wr, rows = [], [], []
                 for c in range(lo, hi):
                     rd += [cc * H + h for cc in {c, min(c + 1, clast)}]
-                    if second:
+                    if j > 0:
                         wr.append(c * H + h)
                     else:
                         rows += rows_of(c)
-                out.append((s, h, rd, wr, rows))
+                # P and Delta of segment j, or (first segment of a split sequence) S_1
+                slots = ([("P", (j - 1) * n * H + s * H + h)] if j > 0 else
+                         [("S", s * H + h)] if k > 1 else [])
+                out.append((s, h, rd, wr, rows, slots))
     return out
 
 
-def combine_touch(cu, n, T, H, C):
-    """Chunk workgroups of the combine: (sequence, head, chunk, unit, rows written)."""
+def combine_touch(cu, n, T, H, C, kmax=2):
+    """Chunk workgroups of the combine: (sequence, head, chunk, unit, rows written, the
+    boundary slot of S_j read)."""
     mc = max_chunks(T, n, C)
     excl, incl = seq_table(cu, n, C)
     c1l = [min(x, mc) for x in incl]
-    nbl = [max(0, c1l[s] - seg_mid(excl[s], c1l[s])) for s in range(n)]
+    ks = [seg_count(c1l[s] - excl[s], kmax) for s in range(n)]
+    nbl = [max(0, c1l[s] - seg_bound(excl[s], c1l[s], 1, ks[s])) if ks[s] > 1 else 0
+           for s in range(n)]
     pin, run = [], 0
     for x in nbl:
         run += x
         pin.append(run)
     pex = [pin[s] - nbl[s] for s in range(n)]
-    bound = (mc * (64 - SEG_A_64) + 63) // 64 + 1
+    bound = (mc * (64 - seg_first_64(kmax)) + 63) // 64 + 1
     out = []
     for b in range(bound * H):
-        h, k = b % H, b // H
-        hits = [s for s in range(n) if pex[s] <= k < pin[s]]
+        h, kc = b % H, b // H
+        hits = [s for s in range(n) if pex[s] <= kc < pin[s]]
         if not hits:
             continue
         s = hits[0]
-        c = seg_mid(excl[s], c1l[s]) + (k - pex[s])
+        k = ks[s]
+        c = seg_bound(excl[s], c1l[s], 1, k) + (kc - pex[s])
+        j = 1
+        while j + 1 < k and seg_bound(excl[s], c1l[s], j + 1, k) <= c:
+            j += 1
         tok0 = cu[s] + (c - excl[s]) * C
         ln = min(C, min(cu[s + 1], T) - tok0)
         rows = [tok0 + i for i in range(C) if i < ln and tok0 + i >= 0]
-        out.append((s, h, c, c * H + h, rows))
+        out.append((s, h, c, c * H + h, rows, ("S", (j - 1) * n * H + s * H + h)))
     return out
+
+
+def chain_slots(cu, n, T, H, C, kmax):
+    """Boundary slots ("P": transition and Delta, "S": S_j) that the chain pass reads
+    (P_j, S_j for j < k - 1) and writes (S_{j+1}) and that the combine's state rows read
+    (j = k - 1), per (sequence, head)."""
+    mc = max_chunks(T, n, C)
+    excl, incl = seq_table(cu, n, C)
+    out = []
+    for s in range(n):
+        k = seg_count(min(incl[s], mc) - excl[s], kmax)
+        for h in range(H):
+            u = s * H + h
+            rd = [(b, (j - 1) * n * H + u) for j in range(1, k) for b in "PS"]
+            wr = [("S", j * n * H + u) for j in range(1, k - 1)]
+            out.append((rd, wr))
+    return out
+
+
+def seg_grid_cover(n, H, kmax):
+    """The segmented scan kernel's workgroup -> (segment, unit, value tile) map."""
+    units, NVT = n * H, 8
+    grid = (kmax * units + 7) // 8 * 8 * NVT
+    seen = []
+    for b in range(grid):
+        xcd, jj = b & 7, b >> 3
+        vu, vt = (jj // NVT) * 8 + xcd, jj % NVT
+        if vu >= kmax * units:
+            continue
+        seen.append((vu // units, vu % units, vt))
+    return seen
+
+
+def test_seg_grid_covers_every_segment_tile_once():
+    for n in (1, 2, 3, 5, 8):
+        for H in (1, 2, 3, 4, 8, 16):
+            kmax = seg_segments(H, n, 10 ** 7)
+            if kmax == 0:
+                continue
+            seen = seg_grid_cover(n, H, kmax)
+            assert sorted(seen) == [(s, u, v) for s in range(kmax) for u in range(n * H)
+                                    for v in range(8)]
+    # the 16-head call: two segments, on all 256 CUs
+    assert seg_segments(16, 1, 8192) == 2 and len(seg_grid_cover(1, 16, 2)) == 256
+    assert seg_segments(8, 1, 8192) == 4 and seg_segments(4, 1, 8192) == 6
+    assert seg_segments(4, 1, 12000) == 8 and seg_segments(4, 1, 5057) == 4
+    assert seg_segments(4, 1, 5056) == 2  # 79 chunks: no sequence takes more than 2
+    assert seg_segments(3, 3, 20000) == 3  # 9 units: K = 3
+    assert seg_segments(17, 1, 8192) == 0 and seg_segments(16, 1, 40 * 64 - 1) == 0
+    # K only bounds the segment count: every sequence of a call gets what the CUs allow
+    for T in range(2560, 20000, 97):
+        kcu = 256 // (2 * 8)
+        for nch in range(0, -(-T // 64) + 1):
+            assert seg_count(nch, seg_segments(2, 1, T)) == seg_count(nch, min(kcu, SEG_MAX))
 
 
 def _long_cu(rng, n):
@@ -272,59 +386,124 @@ def _long_cu(rng, n):
 
 
 @pytest.mark.parametrize("seed", range(8))
-def test_two_segment_exact_cover(seed):
+def test_segmented_exact_cover(seed):
     rng = random.Random(100 + seed)
     n, H, C = rng.randrange(1, 17), rng.choice([1, 2, 4]), 64
+    kmax = rng.choice([2, 3, 4, 8])
     cu = _long_cu(rng, n)
     T = cu[-1]
     excl, incl = seq_table(cu, n, C)
+    nslot = (kmax - 1) * n * H
     written = {}
-    for s, h, rd, wr, rows in seg_scan_touch(cu, n, T, H, C):
+    bslots = []
+    for s, h, rd, wr, rows, slots in seg_scan_touch(cu, n, T, H, C, kmax):
         assert set(rd) <= {c * H + h for c in range(excl[s], incl[s])}
+        assert all(0 <= x < nslot for _, x in slots)
+        bslots += slots
         for r in rows:
             written[(r, h)] = written.get((r, h), 0) + 1
-    comb = combine_touch(cu, n, T, H, C)
+    chain = chain_slots(cu, n, T, H, C, kmax)
+    chain_written = [x for _, wr in chain for x in wr]
+    writes = bslots + chain_written
+    assert len(writes) == len(set(writes))  # each boundary slot has one writer
+    comb = combine_touch(cu, n, T, H, C, kmax)
     seen = set()
-    for s, h, c, u, rows in comb:
-        assert seg_mid(excl[s], incl[s]) <= c < incl[s]
+    for s, h, c, u, rows, sl in comb:
+        k = seg_count(incl[s] - excl[s], kmax)
+        assert seg_bound(excl[s], incl[s], 1, k) <= c < incl[s]
+        assert sl in writes  # S_j of the chunk's segment: the first segment's or the chain's
         assert (s, h, c) not in seen
         seen.add((s, h, c))
         for r in rows:
             written[(r, h)] = written.get((r, h), 0) + 1
-    expect = {(s, h, c) for s in range(n) for h in range(H)
-              for c in range(seg_mid(excl[s], incl[s]), incl[s])}
+    expect = set()
+    for s in range(n):
+        k = seg_count(incl[s] - excl[s], kmax)
+        if k > 1:
+            expect |= {(s, h, c) for h in range(H)
+                       for c in range(seg_bound(excl[s], incl[s], 1, k), incl[s])}
     assert seen == expect
     assert written == {(r, h): 1 for r in range(T) for h in range(H)}
+    done = set(bslots)  # the scan's writes, then the chain's steps in order
+    for rd, wr in chain:
+        assert all(0 <= x < nslot for _, x in rd + wr)
+        for j, x in enumerate(wr):  # step j + 1 reads P_{j+1} and S_{j+1}, writes S_{j+2}
+            assert ("P", rd[2 * j][1]) in done and ("S", rd[2 * j + 1][1]) in done
+            done.add(x)
+        assert set(rd) <= done  # the combine's state rows: the last P and S_{k-1}
 
 
 @pytest.mark.parametrize("cu", BROKEN)
-def test_two_segment_broken_cu_seqlens_stay_in_bounds(cu):
+@pytest.mark.parametrize("kmax", [2, 8])
+def test_segmented_broken_cu_seqlens_stay_in_bounds(cu, kmax):
     n, H, C = len(cu) - 1, 3, 64
     for T in (400, 1000, 5000):
         mc = max_chunks(T, n, C)
-        for _, _, rd, wr, rows in seg_scan_touch(cu, n, T, H, C):
+        nslot = (kmax - 1) * n * H
+        for _, _, rd, wr, rows, slots in seg_scan_touch(cu, n, T, H, C, kmax):
             assert all(0 <= u < mc * H for u in rd + wr)
-            assert all(0 <= r < T for r in rows)
-        for _, _, _, u, rows in combine_touch(cu, n, T, H, C):
-            assert 0 <= u < mc * H and all(0 <= r < T for r in rows)
+            assert all(0 <= r < T for r in rows) and all(0 <= x < nslot for _, x in slots)
+        for _, _, _, u, rows, sl in combine_touch(cu, n, T, H, C, kmax):
+            assert 0 <= u < mc * H and all(0 <= r < T for r in rows) and 0 <= sl[1] < nslot
+        for rd, wr in chain_slots(cu, n, T, H, C, kmax):
+            assert all(0 <= x < nslot for _, x in rd + wr)
 
 
-def test_two_segment_random_broken_cu_seqlens_stay_in_bounds():
+def test_segmented_random_broken_cu_seqlens_stay_in_bounds():
     rng = random.Random(11)
     for _ in range(200):
         n, H, C = rng.randrange(1, 9), rng.choice([1, 2, 5]), 64
+        kmax = rng.choice([2, 3, 5, 8])
         T = rng.randrange(0, 6000)
         cu = [rng.randrange(-500, 7000) for _ in range(n + 1)]
         mc = max_chunks(T, n, C)
-        for _, _, rd, wr, rows in seg_scan_touch(cu, n, T, H, C):
+        nslot = (kmax - 1) * n * H
+        for _, _, rd, wr, rows, slots in seg_scan_touch(cu, n, T, H, C, kmax):
             assert all(0 <= u < mc * H for u in rd + wr) and all(0 <= r < T for r in rows)
-        for _, _, _, u, rows in combine_touch(cu, n, T, H, C):
-            assert 0 <= u < mc * H and all(0 <= r < T for r in rows)
+            assert all(0 <= x < nslot for _, x in slots)
+        for _, _, _, u, rows, sl in combine_touch(cu, n, T, H, C, kmax):
+            assert 0 <= u < mc * H and all(0 <= r < T for r in rows) and 0 <= sl[1] < nslot
+        for rd, wr in chain_slots(cu, n, T, H, C, kmax):
+            assert all(0 <= x < nslot for _, x in rd + wr)
+
+
+def seg_prep_group_k(i, NG, k):
+    """The prep order of a call cut into k > 2 segments: slot i -> chunk group (the device's
+    bisection over passes, written out)."""
+    b = [seg_bound(0, NG, min(s, k), k) for s in range(SEG_MAX + 1)]
+
+    def before(m):
+        return sum(min(b[s + 1] - b[s], m) for s in range(SEG_MAX))
+
+    r = NG - 1 - i
+    lo, hi = 0, NG
+    while hi - lo > 1:
+        mid = (lo + hi) >> 1
+        if before(mid) <= r:
+            lo = mid
+        else:
+            hi = mid
+    t, grp = r - before(lo), i
+    for s in range(SEG_MAX):
+        has = b[s + 1] - b[s] > lo
+        if has and t == 0:
+            grp = b[s] + lo
+        t -= 1 if has else 0
+    return grp
 
 
 def test_seg_prep_order_is_a_permutation():
     for NG in range(1, 200):
         assert sorted(seg_prep_group(i, NG) for i in range(NG)) == list(range(NG))
+        for k in range(1, SEG_MAX + 1):
+            order = [seg_prep_group_k(i, NG, k) for i in range(NG)]
+            assert sorted(order) == list(range(NG))
+            if k == 2:  # the same order as the two-segment form
+                assert order == [seg_prep_group(i, NG) for i in range(NG)]
+            # the last slots go to each segment's first group, first segment first
+            firsts = [g for g in (seg_bound(0, NG, s, k) for s in range(k)) if g < NG]
+            firsts = sorted(set(firsts))
+            assert order[::-1][:len(firsts)] == firsts
 
 
 @pytest.mark.parametrize("seed", range(6))

@@ -71,17 +71,17 @@ def test_noalloc_prefill_wide_then_narrow_tiles(perkey):
 
 
 @pytest.mark.parametrize("perkey", [False, True])
-def test_noalloc_prefill_two_segment_scan(perkey):
-    """Few (sequence, head) units with long sequences: the scan runs in two segments and a
-    combine pass, with their extra workspace sections in the scratch. A 4096-token, 2-head
-    call, then a 2700-token, 1-head one over the same scratch: each bit-identical to the
-    workspace prefill and within the oracle's bar."""
-    first = inputs.random_prefill(86, [4096], H=2, dk=128, dv=128, perkey=perkey,
+def test_noalloc_prefill_segmented_scan(perkey):
+    """Few (sequence, head) units with long sequences: the scan runs in segments with chain
+    and combine passes, their extra workspace sections in the scratch. A 6000-token, 2-head
+    call (4 segments), then a 2700-token, 1-head one (2) over the same scratch: each
+    bit-identical to the workspace prefill and within the oracle's bar."""
+    first = inputs.random_prefill(86, [6000], H=2, dk=128, dv=128, perkey=perkey,
                                   with_init=True)
     second = inputs.random_prefill(87, [2700], H=1, dk=128, dv=128, perkey=perkey,
                                    with_init=True)
     for name, x in (("first, larger", first), ("second, smaller", second)):
-        say(f"case noalloc prefill, two-segment scan, perkey={perkey}: {name} call")
+        say(f"case noalloc prefill, segmented scan, perkey={perkey}: {name} call")
         (o_ws, p_ws), (o_na, p_na) = _both(x)
         assert torch.equal(o_na, o_ws) and torch.equal(p_na, p_ws)
         o_ref, s_ref = oracle_prefill(x)
