@@ -1738,7 +1738,10 @@ __global__ __launch_bounds__(CB_THREADS) void prefill_seg_chain_kernel(PrefillAr
     static_assert((DK * 16 / 4) % CB_THREADS == 0, "S_1 slice in whole 16-byte loads");
     __shared__ __align__(16) float slt[16][LDS_T];  // slt[c][key] = S_j[key][16 tv + c]
     const int H = a.H, nu = a.n_seqs * H;
-    const int unit = (int)blockIdx.x / NT, tv = (int)blockIdx.x % NT;
+    // the NT slices of a (sequence, head) on one XCD, as in the scan: they all read the same
+    // P_j, which one L2 then serves (the grid is a multiple of 8 units)
+    const int xcd = (int)blockIdx.x & 7, jj = (int)blockIdx.x >> 3;
+    const int unit = (jj / NT) * 8 + xcd, tv = jj % NT;
     const SegTable t = seg_table(a, C);
     if (unit >= nu) return;
     const int n = unit / H;
@@ -2012,7 +2015,7 @@ hipError_t prefill_scan_cfg(const PrefillArgs& a, hipStream_t s) {
             hipLaunchKernelGGL((prefill_scan_seg_kernel<T, D, C, PERKEY>), dim3(grid),
                                dim3(ScanShape<C>::THREADS), 0, s, a);
             if (kmax > 2)
-                hipLaunchKernelGGL((prefill_seg_chain_kernel<D, D, C>), dim3((unsigned)(units * (D / 16))),
+                hipLaunchKernelGGL((prefill_seg_chain_kernel<D, D, C>), dim3((unsigned)(((units + 7) / 8) * 8 * (D / 16))),
                                    dim3(CB_THREADS), 0, s, a);
             const int64_t nb = seg_b_chunks_bound(a.ws.max_chunks, kmax) * a.H + (int64_t)units * (D / 16);
             hipLaunchKernelGGL((prefill_seg_combine_kernel<D, D, C>), dim3((unsigned)nb),

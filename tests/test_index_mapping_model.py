@@ -363,6 +363,17 @@ def test_seg_grid_covers_every_segment_tile_once():
             seen = seg_grid_cover(n, H, kmax)
             assert sorted(seen) == [(s, u, v) for s in range(kmax) for u in range(n * H)
                                     for v in range(8)]
+            # the chain pass: every (unit, 16-column slice) once, a unit's slices on one XCD
+            grid = (n * H + 7) // 8 * 8 * 8
+            cover = {}
+            for b in range(grid):
+                xcd, jj = b & 7, b >> 3
+                u, tv = (jj // 8) * 8 + xcd, jj % 8
+                if u < n * H:
+                    assert (u, tv) not in cover
+                    cover[(u, tv)] = xcd
+            assert sorted(cover) == [(u, tv) for u in range(n * H) for tv in range(8)]
+            assert all(len({cover[(u, tv)] for tv in range(8)}) == 1 for u in range(n * H))
     # the 16-head call: two segments, on all 256 CUs
     assert seg_segments(16, 1, 8192) == 2 and len(seg_grid_cover(1, 16, 2)) == 256
     assert seg_segments(8, 1, 8192) == 4 and seg_segments(4, 1, 8192) == 6

@@ -48,7 +48,7 @@ def _random_case(seed, T, H, dk, dv, perkey=False, lengths=None, init=False):
 
 # ----------------------------------------------------------------- exact rational pins
 def _frac_matrix_update_scalar(S, alpha, beta, k, v):
-    """spec matrix form in d_k x d_v orientation:
+    """The gated delta rule's matrix form in d_k x d_v orientation:
     S_t = alpha (I - beta k k^T) S_{t-1} + beta k v^T."""
     dk, dv = len(S), len(S[0])
     kS = [sum(k[i] * S[i][j] for i in range(dk)) for j in range(dv)]   # k^T S
@@ -79,7 +79,7 @@ RAT_BETA = [Fr(1), Fr(1, 2), Fr(3, 4), Fr(0), Fr(1, 3), Fr(2, 5)]
 
 @pytest.mark.parametrize("scale", [Fr(1), Fr(1, 2)])
 def test_rational_exact_scalar_gate(scale):
-    """[LA-Infra] "GDN：增加遗忘门" + spec formula, exact rationals vs fp64 oracle."""
+    """[LA-Infra] "GDN：增加遗忘门" matrix form, exact rationals vs fp64 oracle."""
     T, dk, dv = 6, 3, 2
     S = [[Fr(i - j, 3) for j in range(dv)] for i in range(dk)]          # nonzero S0
     S0 = np.array([[float(x) for x in row] for row in S])
@@ -146,6 +146,32 @@ def test_affine_transition_product(perkey):
     o, st = oracle.recurrence(q, k, v, g, beta, cu, init_states=S0)
     assert np.max(np.abs(o[:, 0] - np.array(outs))) < 1e-12
     assert np.max(np.abs(st[0, 0] - (Tr @ S0[0, 0] + Dl))) < 1e-12
+
+
+# ------------------------------------------------------------ segment composition
+@pytest.mark.parametrize("perkey", [False, True])
+@pytest.mark.parametrize("bounds", [[0, 23, 50], [0, 9, 20, 31, 50], [0, 7, 13, 20, 27, 33, 40, 46, 50]])
+def test_segment_composition(perkey, bounds):
+    """[LA-Infra] "Linear Attention Chunk-Wise": every output and the final state are affine in
+    the incoming state, so a sequence cut into segments is rebuilt from per-segment runs of
+    the recurrence alone: a run from a zero state with the real v (outputs O0_j, final state
+    Delta_j) and a run from the identity with v = 0 (outputs L_j, final state, the
+    transition, P_j), then S_(j+1) = P_j S_j + Delta_j and O = O0_j + L_j S_j. This is the
+    composition the segmented scan evaluates; 2, 4 and 8 segments against one pass."""
+    T, dk, dv = bounds[-1], 6, 5
+    q, k, v, g, beta, cu, S0 = _random_case(9, T, 1, dk, dv, perkey=perkey, init=True)
+    o_ref, s_ref = oracle.recurrence(q, k, v, g, beta, cu, scale=0.7, init_states=S0)
+    S = S0[0, 0]
+    o = np.zeros_like(o_ref)
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        part = np.array([0, b - a], dtype=np.int32)
+        o0, dl = oracle.recurrence(q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b], part, scale=0.7)
+        lo, p = oracle.recurrence(q[a:b], k[a:b], np.zeros((b - a, 1, dk)), g[a:b], beta[a:b],
+                                  part, scale=0.7, init_states=np.eye(dk)[None, None])
+        o[a:b, 0] = o0[:, 0] + lo[:, 0] @ S
+        S = p[0, 0] @ S + dl[0, 0]
+    assert np.max(np.abs(o - o_ref)) < 1e-12
+    assert np.max(np.abs(S - s_ref[0, 0])) < 1e-12
 
 
 # ------------------------------------------------------------------- chunk-wise form
