@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 
 N_CASES = 48
 N_WIDE = 16
-N_SEG = 12
+N_SEG = 20
 
 
 def draw(seed, wide=False, seg=False):
@@ -45,8 +45,8 @@ def draw(seed, wide=False, seg=False):
         dtype, d, chunk = torch.bfloat16, 128, 64
         H = int(r.choice([1, 2, 4]))
         n = int(r.integers(1, min(6, 16 // H) + 1))
-        lengths = [int(x) for x in r.choice([0, 1, 65, 700, 2559, 2560, 2600, 3500, 5000, 8000],
-                                            size=n)]
+        lengths = [int(x) for x in r.choice([0, 1, 65, 700, 2559, 2560, 2600, 3500, 5000, 5200,
+                                             8000, 12000], size=n)]
         if sum(lengths) < 2560 * n:
             lengths[int(r.integers(n))] += 2560 * n - sum(lengths) + int(r.integers(0, 700))
     if sum(lengths) == 0:
