@@ -155,3 +155,14 @@ def test_segmented_against_one_segment():
     e = oracle.rel_err(o, o1)
     say(f"   two vs one segment: rel diff o={e:.2e}")
     assert e <= 1e-2
+
+
+def test_segmented_full_size_few_heads():
+    """The call bench.py times as `prefill_few_heads` (same seeded inputs: one sequence of
+    32768 tokens, H = 2, bf16, d = 128, chunk 64; 8 segments, 6 chain steps), every output
+    and both heads' final states against the oracle."""
+    say("case segmented scan at the few-heads bench size (32768 tokens, H=2)")
+    x = inputs.random_prefill(7, [32768], H=2, dk=128, dv=128, dtype=BF)
+    assert seg_active(2, 1, 32768)
+    o, pool = run_prefill(x)
+    _check(x, o, pool)
