@@ -2008,7 +2008,7 @@ hipError_t prefill_prep_cfg(const PrefillArgs& a, hipStream_t s) {
 template <typename T, int D, int C, bool PERKEY>
 hipError_t prefill_scan_cfg(const PrefillArgs& a, hipStream_t s) {
     const int units = a.n_seqs * a.H;
-    if constexpr (std::is_same<T, bf16>::value && D == 128 && C == 64) {
+    if constexpr (std::is_same<T, bf16>::value && (D == 128 || D == 64) && C == 64) {
         if (a.seg) {  // see seg_segments
             const int kmax = a.seg;
             const unsigned grid = (unsigned)(((kmax * units + 7) / 8) * 8 * (D / SCAN_BV));

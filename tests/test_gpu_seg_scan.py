@@ -25,13 +25,13 @@ pytestmark = pytest.mark.gpu
 BF = torch.bfloat16
 
 
-def seg_active(H, n_seqs, T, perkey=False):
-    """True when the library sizes the workspace for the two-segment scan for this call."""
+def seg_active(H, n_seqs, T, perkey=False, d=128):
+    """True when the library sizes the workspace for the segmented scan for this call."""
     plain = ((T + n_seqs * 63) // 64) * H * (
-        64 * 128 * 2 * 2 + 128 * 64 * 2 + 64 * 64 * 2
-        + max(64 * 128 * 4, 64 * 64 * 2 + 64 * 4 + 64 * 128 * 2) + 128 * 4)
-    need = gdn.gdn_prefill_workspace_bytes(H, 128, 128, BF, perkey, n_seqs, T, 64)
-    return need > plain + n_seqs * H * 128 * 128 * 14
+        64 * d * 2 * 2 + d * 64 * 2 + 64 * 64 * 2
+        + max(64 * d * 4, 64 * 64 * 2 + 64 * 4 + 64 * d * 2) + d * 4)
+    need = gdn.gdn_prefill_workspace_bytes(H, d, d, BF, perkey, n_seqs, T, 64)
+    return need > plain + n_seqs * H * d * d * 14
 
 
 def _check(x, o, pool, heads=None):
@@ -57,6 +57,22 @@ def test_segmented_vs_oracle(lengths, H, perkey, init, l2):
     assert seg_active(H, len(lengths), T, perkey)
     x = inputs.random_prefill(91, lengths, H=H, dk=128, dv=128, dtype=BF, perkey=perkey,
                               prenorm=not l2, with_init=init)
+    o, pool = run_prefill(x)
+    _check(x, o, pool)
+
+
+@pytest.mark.parametrize("lengths,H,perkey", [
+    ([8192], 2, False),          # K = 8: 6 segments
+    ([3000, 6000], 4, True),     # K = 8: 2 and 4 segments, per-key gate
+    ([5000, 5000], 16, False),   # 32 units, K = 2: the two-segment form and its prep order
+])
+def test_segmented_d64_vs_oracle(lengths, H, perkey):
+    """d_k = d_v = 64: 4 value tiles per head, so the segments fit for twice the units."""
+    T = sum(lengths)
+    say(f"case segmented scan d=64 lengths={lengths} H={H} perkey={perkey}")
+    assert seg_active(H, len(lengths), T, perkey, d=64)
+    x = inputs.random_prefill(96, lengths, H=H, dk=64, dv=64, dtype=BF, perkey=perkey,
+                              with_init=True)
     o, pool = run_prefill(x)
     _check(x, o, pool)
 

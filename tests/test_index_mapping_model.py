@@ -198,12 +198,12 @@ def test_random_broken_cu_seqlens_stay_in_bounds():
 SEG_MIN_CHUNKS, SEG_MULTI_CHUNKS, SEG_PER_CHUNKS, SEG_MAX = 40, 80, 20, 8
 
 
-def seg_segments(H, n, T, cus=256, C=64):
-    """K, the most segments a sequence is cut into (bf16, d = 128, C = 64), or 0."""
+def seg_segments(H, n, T, cus=256, C=64, d=128):
+    """K, the most segments a sequence is cut into (bf16, d = 64 or 128, C = 64), or 0."""
     units = n * H
-    if not (units > 0 and n <= 64 and T >= n * SEG_MIN_CHUNKS * C):
+    if not (units > 0 and n <= 64 and T >= n * SEG_MIN_CHUNKS * C and d in (64, 128)):
         return 0
-    k = cus // (units * 8)
+    k = cus // (units * (d // 16))
     if k < 2:
         return 0
     return seg_count(min(-(-T // C), SEG_MAX * SEG_PER_CHUNKS), min(k, SEG_MAX))
@@ -340,9 +340,10 @@ def chain_slots(cu, n, T, H, C, kmax):
     return out
 
 
-def seg_grid_cover(n, H, kmax):
-    """The segmented scan kernel's workgroup -> (segment, unit, value tile) map."""
-    units, NVT = n * H, 8
+def seg_grid_cover(n, H, kmax, NVT=8):
+    """The segmented scan kernel's workgroup -> (segment, unit, value tile) map (NVT value
+    tiles of 16 columns per head: d / 16)."""
+    units = n * H
     grid = (kmax * units + 7) // 8 * 8 * NVT
     seen = []
     for b in range(grid):
@@ -355,31 +356,38 @@ def seg_grid_cover(n, H, kmax):
 
 
 def test_seg_grid_covers_every_segment_tile_once():
-    for n in (1, 2, 3, 5, 8):
-        for H in (1, 2, 3, 4, 8, 16):
-            kmax = seg_segments(H, n, 10 ** 7)
-            if kmax == 0:
-                continue
-            seen = seg_grid_cover(n, H, kmax)
-            assert sorted(seen) == [(s, u, v) for s in range(kmax) for u in range(n * H)
-                                    for v in range(8)]
-            # the chain pass: every (unit, 16-column slice) once, a unit's slices on one XCD
-            grid = (n * H + 7) // 8 * 8 * 8
-            cover = {}
-            for b in range(grid):
-                xcd, jj = b & 7, b >> 3
-                u, tv = (jj // 8) * 8 + xcd, jj % 8
-                if u < n * H:
-                    assert (u, tv) not in cover
-                    cover[(u, tv)] = xcd
-            assert sorted(cover) == [(u, tv) for u in range(n * H) for tv in range(8)]
-            assert all(len({cover[(u, tv)] for tv in range(8)}) == 1 for u in range(n * H))
+    for d in (64, 128):
+        NT = d // 16
+        for n in (1, 2, 3, 5, 8):
+            for H in (1, 2, 3, 4, 8, 16):
+                kmax = seg_segments(H, n, 10 ** 7, d=d)
+                if kmax == 0:
+                    continue
+                seen = seg_grid_cover(n, H, kmax, NT)
+                assert sorted(seen) == [(s, u, v) for s in range(kmax) for u in range(n * H)
+                                        for v in range(NT)]
+                # the chain pass: every (unit, 16-column slice) once, a unit's slices on one
+                # XCD
+                grid = (n * H + 7) // 8 * 8 * NT
+                cover = {}
+                for b in range(grid):
+                    xcd, jj = b & 7, b >> 3
+                    u, tv = (jj // NT) * 8 + xcd, jj % NT
+                    if u < n * H:
+                        assert (u, tv) not in cover
+                        cover[(u, tv)] = xcd
+                assert sorted(cover) == [(u, tv) for u in range(n * H) for tv in range(NT)]
+                assert all(len({cover[(u, tv)] for tv in range(NT)}) == 1 for u in range(n * H))
     # the 16-head call: two segments, on all 256 CUs
     assert seg_segments(16, 1, 8192) == 2 and len(seg_grid_cover(1, 16, 2)) == 256
     assert seg_segments(8, 1, 8192) == 4 and seg_segments(4, 1, 8192) == 6
     assert seg_segments(4, 1, 12000) == 8 and seg_segments(4, 1, 5057) == 4
     assert seg_segments(4, 1, 5056) == 2  # 79 chunks: no sequence takes more than 2
     assert seg_segments(3, 3, 20000) == 3  # 9 units: K = 3
+    # d = 64: 4 value tiles per head, so twice the units fit
+    assert seg_segments(16, 2, 20000, d=64) == 2 and seg_segments(32, 1, 8192, d=64) == 2
+    assert seg_segments(16, 1, 8192, d=64) == 4 and seg_segments(33, 1, 8192, d=64) == 0
+    assert seg_segments(4, 1, 8192, d=32) == 0
     assert seg_segments(17, 1, 8192) == 0 and seg_segments(16, 1, 40 * 64 - 1) == 0
     # K only bounds the segment count: every sequence of a call gets what the CUs allow
     for T in range(2560, 20000, 97):
