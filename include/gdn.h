@@ -180,8 +180,12 @@ int gdn_prefill_chunked(const gdn_dims_t* dims, const void* q, const void* k, co
  *               `slots` of this call (the writes of one launch are not ordered).
  *   n_ckpt      number of entries (>= 0). With n_ckpt == 0 the three arrays may be NULL and
  *               the call equals gdn_prefill_chunked.
- * The exported state is bit-identical to the final state of a gdn_prefill_chunked call over
- * the same p tokens with the same chunk size. */
+ * With checkpoints the scan runs every sequence in one segment. The exported state is then
+ * bit-identical to the final state of a gdn_prefill_chunked call over the same p tokens with
+ * the same chunk size, and the outputs and final states to those of gdn_prefill_chunked,
+ * wherever that call also runs in one segment; where it cuts a sequence into segments (few
+ * (sequence, head) units and long sequences, see gdn_prefill_chunked) the two agree to
+ * rounding, not bit for bit. */
 int gdn_prefill_chunked_ckpt(const gdn_dims_t* dims, const void* q, const void* k,
                              const void* v, const float* g, const float* beta,
                              const int32_t* cu_seqlens, int32_t n_seqs, int32_t total_tokens,
