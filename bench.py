@@ -204,15 +204,14 @@ def bench_prefill_ckpt(steps, warmup, plain_ms):
     return out
 
 
-def bench_prefill_few_heads(steps, warmup, T=32768, H=2):
-    """One long sequence with few heads (32768 tokens x 2 heads: one GPU's share of a 16-head
-    layer split over 8 GPUs by heads), bf16, d=128, chunk 64. Its 16 value-tile units would
-    leave most CUs idle, so the scan cuts the sequence into segments run at once (8 here) and
-    composes them; a call with a single checkpoint (at the last chunk boundary) keeps the scan
-    in one segment and is timed beside it."""
-    x = inputs.random_prefill(7, [T], H=H, dk=128, dv=128, dtype=torch.bfloat16)
+def bench_prefill_few_heads(steps, warmup, T=32768, H=2, d=128):
+    """One long sequence with few heads (by default 32768 tokens x 2 heads: one GPU's share of
+    a 16-head layer split over 8 GPUs by heads), bf16, chunk 64. Its few value-tile units
+    would leave most CUs idle, so the scan cuts the sequence into segments run at once (8
+    here) and composes them; a call with a single checkpoint (at the last chunk boundary)
+    keeps the scan in one segment and is timed beside it."""
+    x = inputs.random_prefill(7, [T], H=H, dk=d, dv=d, dtype=torch.bfloat16)
     q, k, v, g, b, cu = (t.to(DEV) for t in (x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens))
-    d = 128
     pool = torch.zeros((2, H, d, d), device=DEV)
     slots = torch.zeros(1, dtype=torch.int32, device=DEV)
     ck_cu = torch.tensor([0, 1], dtype=torch.int32, device=DEV)
@@ -234,7 +233,7 @@ def bench_prefill_few_heads(steps, warmup, T=32768, H=2):
     ms1, _, _ = ev_time_reps(one, steps, max(10, warmup // 5))
     return dict(ms=ms, tokens_per_s=T / (ms * 1e-3), ms_one_segment=ms1,
                 speedup_vs_one_segment=ms1 / ms,
-                workload=f"GDN chunked prefill, one sequence of {T} tokens, H={H}, d=128, "
+                workload=f"GDN chunked prefill, one sequence of {T} tokens, H={H}, d={d}, "
                          "chunk 64, bf16")
 
 
@@ -586,6 +585,8 @@ def main():
         line["prefill_batch"] = bench_prefill_batch(args.steps, args.warmup)
         log("prefill, few heads ...")
         line["prefill_few_heads"] = bench_prefill_few_heads(args.steps, args.warmup)
+        line["prefill_few_heads_d64"] = bench_prefill_few_heads(args.steps, args.warmup, H=4,
+                                                                d=64)
         log("decode ...")
         line["decode"] = bench_decode(args.steps, args.warmup)
         log("fused decode ...")

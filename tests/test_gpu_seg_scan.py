@@ -182,3 +182,14 @@ def test_segmented_full_size_few_heads():
     assert seg_active(2, 1, 32768)
     o, pool = run_prefill(x)
     _check(x, o, pool)
+
+
+def test_segmented_full_size_few_heads_d64():
+    """The call bench.py times as `prefill_few_heads_d64` (same seeded inputs: one sequence
+    of 32768 tokens, H = 4, d_k = d_v = 64; 8 segments), every output and every head's final
+    state against the oracle."""
+    say("case segmented scan at the d=64 few-heads bench size (32768 tokens, H=4)")
+    x = inputs.random_prefill(7, [32768], H=4, dk=64, dv=64, dtype=BF)
+    assert seg_active(4, 1, 32768, d=64)
+    o, pool = run_prefill(x)
+    _check(x, o, pool)
