@@ -154,6 +154,24 @@ def test_prefill_workspace_too_small_and_sizing():
     lib.gdn_prefill_workspace_bytes(ctypes.byref(dims4), 1, 8192, 64, ctypes.byref(four))
     base4 = 128 * 4 * (per + 64 * 128 * 2) + 5 * 4 * 128 * 128 * (4 + 2 + 4 + 4)
     assert base4 <= four.value < base4 + 64 * 1024
+    # d = 64, 16 heads: 4 value tiles per head, 256 / (16 x 4) = 4 segments fit and a
+    # 128-chunk sequence takes them all, so 3 boundaries; + L (bf16, 64 x 64) per unit
+    # (U's section holds the larger of U and the scan's own U operands with the raw-q row
+    # factors; at d = 64 the latter)
+    per64 = (64 * 64 * 2 * 2 + 64 * 64 * 2 + 64 * 64 * 2
+             + max(64 * 64 * 4, 64 * 64 * 2 + 64 * 4 + 64 * 64 * 2 + 64 * 4) + 64 * 4)
+    d64 = ctypes.c_size_t(0)
+    lib.gdn_prefill_workspace_bytes(ctypes.byref(_dims(H=16, dk=64, dv=64)), 1, 8192, 64,
+                                    ctypes.byref(d64))
+    base64 = 128 * 16 * (per64 + 64 * 64 * 2) + 3 * 16 * 64 * 64 * (4 + 2 + 4 + 4)
+    assert base64 <= d64.value < base64 + 64 * 1024
+    # d = 32 never runs segments: the plain layout only
+    d32 = ctypes.c_size_t(0)
+    lib.gdn_prefill_workspace_bytes(ctypes.byref(_dims(H=1, dk=32, dv=32)), 1, 8192, 64,
+                                    ctypes.byref(d32))
+    per32 = (64 * 32 * 2 * 2 + 32 * 64 * 2 + 64 * 64 * 2
+             + max(64 * 32 * 4, 64 * 64 * 2 + 64 * 4 + 64 * 32 * 2 + 64 * 4) + 32 * 4)
+    assert 128 * per32 <= d32.value < 128 * per32 + 64 * 1024
 
 
 def _prefill_noalloc(dims, **kw):
