@@ -117,13 +117,14 @@ def test_segmented_strong_decay(perkey):
     _check(x, o, pool)
 
 
-def test_segmented_conv_fused():
+@pytest.mark.parametrize("d", [128, 64])
+def test_segmented_conv_fused(d):
     """Conv-fused prefill of 2 sequences x 4 heads (4 and 2 segments), with a conv history
     and an initial state for one of them."""
     lengths = [6100, 2600]
-    n, H, d, W = 2, 4, 128, 4
-    assert seg_active(H, n, sum(lengths))
-    say("case segmented scan, conv-fused prefill")
+    n, H, W = 2, 4, 4
+    assert seg_active(H, n, sum(lengths), d=d)
+    say(f"case segmented scan, conv-fused prefill d={d}")
     x = inputs.conv_prefill(94, lengths, H, d, width=W, dtype=BF, perkey=False)
     CH = 3 * H * d
     cs0 = torch.zeros(n, CH, W - 1, dtype=BF)
