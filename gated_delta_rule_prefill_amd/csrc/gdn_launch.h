@@ -133,7 +133,7 @@ inline int scan_tiles(int dtype, int64_t units, int dv) {
     return nvb < cap ? nvb : cap;
 }
 
-// Segmented scan: bf16, d_k = d_v = 64 or 128, C = 64, no checkpoints, and few enough (sequence,
+// Segmented scan: bf16 or fp32, d_k = d_v = 64 or 128, C = 64, no checkpoints, and few enough (sequence,
 // head) units that at least two segments' workgroups (one 16-column tile for a first
 // segment, a 16-column value tile beside an identity tile for each later one) fit on the
 // chip at once; sequences long enough on average to split (SEG_MIN_CHUNKS, the length below
@@ -161,8 +161,8 @@ __host__ __device__ inline int seg_count(int n, int kmax) {
 inline int seg_segments(int dtype, int H, int dk, int dv, int chunk, int n_seqs,
                         int64_t total_tokens) {
     const int64_t units = (int64_t)n_seqs * H;
-    if (!(dtype == 1 && dk == dv && (dk == 64 || dk == 128) && chunk == 64 && units > 0 &&
-          n_seqs <= 64 && total_tokens >= (int64_t)n_seqs * SEG_MIN_CHUNKS * chunk))
+    if (!((dtype == 0 || dtype == 1) && dk == dv && (dk == 64 || dk == 128) && chunk == 64 &&
+          units > 0 && n_seqs <= 64 && total_tokens >= (int64_t)n_seqs * SEG_MIN_CHUNKS * chunk))
         return 0;
     const int64_t k = device_cu_count() / (units * (dv / 16));
     if (k < 2) return 0;

@@ -73,13 +73,13 @@ size_t prefill_ws_layout(int dtype, int H, int dk, int dv, int chunk, int n_seqs
     off = align256(off + std::max(units * dv * chunk * 4, s_r + s_b + s_v + s_q));
     const size_t o_d = off;   off = align256(off + units * dk * 4);
     // segmented scan: L per unit, and four d_k x d_v states per (segment boundary, sequence,
-    // head)
+    // head): three in fp32, one (transposed) in the element type
     const int kseg = seg_segments(dtype, H, dk, dv, chunk, n_seqs, total_tokens);
     const bool seg = kseg != 0;
     const size_t sh = (size_t)(seg ? kseg - 1 : 0) * n_seqs * H * dk * dv;
     const size_t o_l = off;   if (seg) off = align256(off + units * chunk * dkp * e);
     const size_t o_sm = off;  if (seg) off = align256(off + sh * 4);
-    const size_t o_st = off;  if (seg) off = align256(off + sh * 2);
+    const size_t o_st = off;  if (seg) off = align256(off + sh * e);
     const size_t o_p = off;   if (seg) off = align256(off + sh * 4);
     const size_t o_dl = off;  if (seg) off = align256(off + sh * 4);
     const size_t o_x = off;   off = align256(off + 256 * 4);

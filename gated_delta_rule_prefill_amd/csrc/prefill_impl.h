@@ -293,9 +293,19 @@ template <> struct Ident<float> {
 // lanes 13..15 also load the three rows before the block (from the previous block, the
 // previous chunk, or the sequence's conv history). The weights of the head's channels sit
 // in LDS for the duration of P0.
+// Occupancy floor: 3 waves per SIMD (2 with per-key gates), which fits the bf16 prep's
+// registers. fp32 operands take twice the registers for the same elements: at d = 64 that
+// floor made the compiler spill to scratch (2 thousand spill instructions), so fp32 at
+// d = 64 asks for one wave per SIMD and the whole register file (no spills; prep 854 ->
+// 205 µs at 8192 tokens x 16 heads). At d = 128 the fp32 working set exceeds even that
+// (it spills either way, and more slowly with one wave), so it keeps the floor.
+template <typename T, int DK>
+constexpr int prep_waves_per_eu(bool perkey) {
+    return sizeof(T) == 4 && DK == 64 ? 1 : (perkey ? 2 : 3);
+}
 template <typename T, int DK, int DV, int C, bool PERKEY, bool CONV>
 __global__ __launch_bounds__(PF_THREADS)
-__attribute__((amdgpu_waves_per_eu(PERKEY ? 2 : 3))) void prefill_prep_kernel(PrefillArgs a) {
+__attribute__((amdgpu_waves_per_eu(prep_waves_per_eu<T, DK>(PERKEY)))) void prefill_prep_kernel(PrefillArgs a) {
     using F = PfCfg<T, DK, DV, C>;
     using MM = typename F::MM;
     using frag = typename MM::frag;
@@ -1728,9 +1738,8 @@ constexpr int CB_THREADS = 256;
 // latency counts: its B operands come from LDS as 16-byte reads issued together before the
 // products, and the next step's P and Delta (which do not depend on the chain) are loaded
 // before this step's products.
-template <int DK, int DV, int C>
+template <typename T, int DK, int DV, int C>
 __global__ __launch_bounds__(CB_THREADS) void prefill_seg_chain_kernel(PrefillArgs a) {
-    using T = bf16;
     using MF = Mma<float>;
     constexpr int NT = DV / 16, NW = CB_THREADS / WAVE, RBW = DK / 16 / NW, NQ = DK / 16;
     constexpr int LDS_T = DK + 4;  // row stride of the transposed slice (floats, 16-byte rows)
@@ -1841,14 +1850,14 @@ __global__ __launch_bounds__(CB_THREADS) void prefill_seg_chain_kernel(PrefillAr
 inline int64_t seg_b_chunks_bound(int64_t max_chunks, int kmax) {
     return (max_chunks * (64 - seg_first_64(kmax)) + 63) / 64 + 1;
 }
-template <int DK, int DV, int C>
+template <typename T, int DK, int DV, int C>
 __global__ __launch_bounds__(CB_THREADS) void prefill_seg_combine_kernel(PrefillArgs a) {
-    using T = bf16;
     using MM = Mma<T>;
     using MF = Mma<float>;
     constexpr int KB = MM::KB, KPL = MM::KPL, NB = C / 16, NT = DV / 16;
-    constexpr int LDT = DK + 8;   // S_j^T rows in LDS (bf16, 16-byte padding)
-    constexpr int LDO = DV + 8;   // output rows in LDS
+    constexpr int V16 = 16 / (int)sizeof(T);  // elements per 16 bytes
+    constexpr int LDT = DK + V16;  // S_j^T rows in LDS (16-byte padding)
+    constexpr int LDO = DV + V16;  // output rows in LDS
     static_assert(NB == CB_THREADS / WAVE, "one wave per 16-token block");
     static_assert(DK % KB == 0 && DK % 16 == 0, "no key padding");
     static_assert(NB * 16 * LDO <= DV * LDT, "output rows reuse the S_j^T space");
@@ -1919,12 +1928,13 @@ __global__ __launch_bounds__(CB_THREADS) void prefill_seg_combine_kernel(Prefill
     typename MM::frag al[DK / KB];
 #pragma unroll
     for (int kb = 0; kb < DK / KB; kb++) al[kb] = MM::load(Frag<T>::ptr(lb, mb, kb, DK, lane));
-    // S_j^T into LDS once for all four waves
+    // S_j^T into LDS once for all four waves, 16 bytes per copy
+    static_assert((DV * DK / V16) % CB_THREADS == 0, "S_j^T in whole 16-byte pieces");
 #pragma unroll
-    for (int it = 0; it < DV * DK / 8 / CB_THREADS; it++) {
-        const int p = (int)threadIdx.x + it * CB_THREADS, row = p / (DK / 8), c8 = p % (DK / 8);
-        *reinterpret_cast<MM::frag*>(&lds[row * LDT + c8 * 8]) =
-            *reinterpret_cast<const MM::frag*>(smt + (size_t)row * DK + c8 * 8);
+    for (int it = 0; it < DV * DK / V16 / CB_THREADS; it++) {
+        const int p = (int)threadIdx.x + it * CB_THREADS, row = p / (DK / V16), cv = p % (DK / V16);
+        *reinterpret_cast<f32x4*>(&lds[row * LDT + cv * V16]) =
+            *reinterpret_cast<const f32x4*>(smt + (size_t)row * DK + cv * V16);
     }
     __syncthreads();
 #pragma unroll
@@ -2008,17 +2018,17 @@ hipError_t prefill_prep_cfg(const PrefillArgs& a, hipStream_t s) {
 template <typename T, int D, int C, bool PERKEY>
 hipError_t prefill_scan_cfg(const PrefillArgs& a, hipStream_t s) {
     const int units = a.n_seqs * a.H;
-    if constexpr (std::is_same<T, bf16>::value && (D == 128 || D == 64) && C == 64) {
+    if constexpr ((D == 128 || D == 64) && C == 64) {
         if (a.seg) {  // see seg_segments
             const int kmax = a.seg;
             const unsigned grid = (unsigned)(((kmax * units + 7) / 8) * 8 * (D / SCAN_BV));
             hipLaunchKernelGGL((prefill_scan_seg_kernel<T, D, C, PERKEY>), dim3(grid),
                                dim3(ScanShape<C>::THREADS), 0, s, a);
             if (kmax > 2)
-                hipLaunchKernelGGL((prefill_seg_chain_kernel<D, D, C>), dim3((unsigned)(((units + 7) / 8) * 8 * (D / 16))),
+                hipLaunchKernelGGL((prefill_seg_chain_kernel<T, D, D, C>), dim3((unsigned)(((units + 7) / 8) * 8 * (D / 16))),
                                    dim3(CB_THREADS), 0, s, a);
             const int64_t nb = seg_b_chunks_bound(a.ws.max_chunks, kmax) * a.H + (int64_t)units * (D / 16);
-            hipLaunchKernelGGL((prefill_seg_combine_kernel<D, D, C>), dim3((unsigned)nb),
+            hipLaunchKernelGGL((prefill_seg_combine_kernel<T, D, D, C>), dim3((unsigned)nb),
                                dim3(CB_THREADS), 0, s, a);
             return hipGetLastError();
         }

@@ -123,7 +123,7 @@ int gdn_prefill_workspace_bytes(const gdn_dims_t* dims, int32_t n_seqs, int32_t 
  * every sequence boundary; the last chunk of a sequence may be short. Splitting a sequence
  * over several calls and handing the state over through the pool gives the one-shot result
  * up to rounding ([Handbook] "同一个计算的两种写法", "在真实模型上核对"). When the call has few (sequence,
- * head) units (bf16, d_k = d_v = 64 or 128, chunk 64, 2 x units x d_v / 16 <= the device's
+ * head) units (bf16 or fp32, d_k = d_v = 64 or 128, chunk 64, 2 x units x d_v / 16 <= the device's
  * CU count, at least 40 chunks per sequence on average), each sequence of n >= 40 chunks is
  * scanned as segments at once (two below 80 chunks, then min(K, n / 20), K = CU count /
  * (units x d_v / 16) capped at 8), composed through their transitions,

@@ -165,6 +165,15 @@ def test_prefill_workspace_too_small_and_sizing():
                                     ctypes.byref(d64))
     base64 = 128 * 16 * (per64 + 64 * 64 * 2) + 3 * 16 * 64 * 64 * (4 + 2 + 4 + 4)
     assert base64 <= d64.value < base64 + 64 * 1024
+    # fp32, d = 128, 16 heads: two segments; every section in 4-byte elements (the transposed
+    # state at a boundary too)
+    perf = 3 * 64 * 128 * 4 + 64 * 64 * 4 + max(64 * 128 * 4, 64 * 64 * 4 + 64 * 4 + 64 * 128 * 4
+                                                  + 64 * 4) + 128 * 4
+    f32 = ctypes.c_size_t(0)
+    lib.gdn_prefill_workspace_bytes(ctypes.byref(_dims(H=16, dtype=0)), 1, 8192, 64,
+                                    ctypes.byref(f32))
+    basef = 128 * 16 * (perf + 64 * 128 * 4) + 16 * 128 * 128 * (4 + 4 + 4 + 4)
+    assert basef <= f32.value < basef + 64 * 1024
     # d = 32 never runs segments: the plain layout only
     d32 = ctypes.c_size_t(0)
     lib.gdn_prefill_workspace_bytes(ctypes.byref(_dims(H=1, dk=32, dv=32)), 1, 8192, 64,

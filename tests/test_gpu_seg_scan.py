@@ -1,16 +1,17 @@
 """Segmented scan on the GPU vs the fp64 oracle, through the C ABI.
 
-With bf16, d_k = d_v = 128, C = 64 and few (sequence, head) units (at most one sixteenth of
+With d_k = d_v = 64 or 128, C = 64 and few (sequence, head) units (value tiles at most half
 the CU count), the scan cuts each sequence of n >= 40 chunks into k segments run at once
-(k = 2 below 80 chunks, then min(K, n / 20); K = CUs / (8 units), at most 8): the first from the initial
-state, each later one from a zero state beside an identity run that yields the segment's
+(k = 2 below 80 chunks, then min(K, n / 20); K = CUs / (units x d / 16), at most 8): the
+first from the initial state, each later one from a zero state beside an identity run that yields the segment's
 transition. A chain pass carries the state across the boundaries (S_{j+1} = P_j S_j +
 Delta_j) and a combine pass adds (identity-run outputs) x (state at the segment's start) to
 each later segment's outputs and forms the final state ([LA-Infra] "Linear Attention
 Chunk-Wise": chunk states compose as S_C = Transition S_0 + Delta). These cases cover 2 to 8
 segments, split and unsplit sequences in one call, ragged and empty sequences, initial
 states, slots outside the pool, both gates, very strong decay, the in-kernel L2 norm and the
-fused convolution. Bar: max|x - ref| / max|ref| <= 1e-2 (bf16 inputs).
+fused convolution, and fp32 inputs. Bars: max|x - ref| / max|ref| <= 1e-2 (bf16 inputs), 1e-4
+(fp32 inputs).
 """
 import pytest
 import torch
@@ -25,12 +26,13 @@ pytestmark = pytest.mark.gpu
 BF = torch.bfloat16
 
 
-def seg_active(H, n_seqs, T, perkey=False, d=128):
+def seg_active(H, n_seqs, T, perkey=False, d=128, dtype=BF):
     """True when the library sizes the workspace for the segmented scan for this call."""
+    e = 2 if dtype == BF else 4
     plain = ((T + n_seqs * 63) // 64) * H * (
-        64 * d * 2 * 2 + d * 64 * 2 + 64 * 64 * 2
-        + max(64 * d * 4, 64 * 64 * 2 + 64 * 4 + 64 * d * 2) + d * 4)
-    need = gdn.gdn_prefill_workspace_bytes(H, d, d, BF, perkey, n_seqs, T, 64)
+        64 * d * e * 2 + d * 64 * e + 64 * 64 * e
+        + max(64 * d * 4, 64 * 64 * e + 64 * 4 + 64 * d * e + 64 * 4) + d * 4)
+    need = gdn.gdn_prefill_workspace_bytes(H, d, d, dtype, perkey, n_seqs, T, 64)
     return need > plain + n_seqs * H * d * d * 14
 
 
@@ -75,6 +77,27 @@ def test_segmented_d64_vs_oracle(lengths, H, perkey):
                               with_init=True)
     o, pool = run_prefill(x)
     _check(x, o, pool)
+
+
+@pytest.mark.parametrize("lengths,H,d,perkey", [
+    ([8192], 2, 128, False),      # K = 8: 6 segments
+    ([3000, 6000], 4, 64, True),  # K = 8: 2 and 4 segments, per-key gate
+    ([5000], 16, 128, True),      # K = 2
+])
+def test_segmented_fp32_vs_oracle(lengths, H, d, perkey):
+    """fp32 inputs: the same segmented scan on fp32 MFMA throughout (the combine's L S_j
+    product and the chain too), at the fp32 bar."""
+    F32 = torch.float32
+    T = sum(lengths)
+    say(f"case segmented scan fp32 d={d} lengths={lengths} H={H} perkey={perkey}")
+    assert seg_active(H, len(lengths), T, perkey, d=d, dtype=F32)
+    x = inputs.random_prefill(97, lengths, H=H, dk=d, dv=d, dtype=F32, perkey=perkey,
+                              with_init=True)
+    o, pool = run_prefill(x)
+    o_ref, s_ref = oracle_prefill(x)
+    e_o, e_s = oracle.rel_err(o, o_ref), oracle.rel_err(pool, s_ref)
+    say(f"   rel err o={e_o:.2e} S={e_s:.2e}")
+    assert e_o <= BAR[F32] and e_s <= BAR[F32]
 
 
 def test_segmented_slots_outside_pool_and_untouched_slots():
